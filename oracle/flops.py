@@ -1,0 +1,37 @@
+"""Algorithmic FLOP counts (test infrastructure; see ``oracle``).
+
+[HJ] counts a GEMM of shapes ``(m, k) x (k, n)`` as ``2 m k n`` FLOPs and
+neglects the activation, dropout and the all-reduce's additions (MLP,
+single-card forward and backward; TP forward).  Its totals for a GeLU MLP
+with ``d_ff = 4 d``: forward ``16 B S d^2``, backward twice that, and ``1/n``
+of each per rank under ``n``-way TP.  For attention (MHA, no causal saving):
+forward ``8 B S d^2 + 4 B S^2 d``, backward twice that.
+"""
+
+
+def gemm(m: int, k: int, n: int) -> int:
+    return 2 * m * k * n
+
+
+def mlp_shard(tokens: int, h: int, f: int, act: str) -> dict:
+    """Per-rank FLOPs of the MLP shard with intermediate width ``f``.
+
+    Forward: one (GeLU) or two (SwiGLU: gate and up) ``[T,h]x[h,f]`` GEMMs and
+    the ``[T,f]x[f,h]`` GEMM.  Backward: two GEMMs per forward GEMM (the input
+    and the weight gradient), so twice the forward.
+    """
+    n_first = 1 if act == "gelu" else 2
+    fwd = n_first * gemm(tokens, h, f) + gemm(tokens, f, h)
+    bwd = 2 * fwd
+    return dict(fwd=fwd, bwd=bwd, total=fwd + bwd)
+
+
+def attention_shard_fwd(b: int, s: int, h: int, q: int, kv: int, d: int, causal: bool = True) -> dict:
+    """Per-rank forward FLOPs: QKV GEMM, core (QK^T and PV over the key/query
+    pairs actually computed) and the output projection."""
+    T = b * s
+    pairs = s * (s + 1) // 2 if causal else s * s
+    qkv = gemm(T, h, (q + 2 * kv) * d)
+    core = 2 * (2 * d) * b * q * pairs
+    out = gemm(T, q * d, h)
+    return dict(qkv=qkv, core=core, out=out, total=qkv + core + out)

@@ -1,0 +1,468 @@
+"""Pins of the CPU oracle to facts outside itself (CPU only).
+
+Each test checks the oracle against something the pages or mathematics fix:
+tabulated values, closed forms, invariants the pages state, brute force on
+tiny inputs written with Python loops and ``math``, finite differences of the
+forward pass, and a simulated ring all-reduce.  The tests are chosen so that
+a plausible slip in the oracle (a dropped term, a sign, a wrong index, a
+transposed operand, the bias counted per rank) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import activations as A
+from oracle import attention as att
+from oracle import comm, dropout, flops, mlp
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- activations
+
+def test_gelu_matches_tabulated_normal_cdf():
+    pts = json.load(open(os.path.join(GOLDEN, "normal_cdf.json")))["points"]
+    for p in pts:
+        x = p["x"]
+        assert abs(A.normal_cdf(x) - p["Phi"]) < 1e-14
+        assert abs(A.gelu(x) - x * p["Phi"]) < 1e-14
+
+
+def test_activation_closed_forms():
+    x = np.linspace(-6, 6, 101)
+    assert A.gelu(0.0) == 0.0 and A.silu(0.0) == 0.0
+    # GeLU(-x) = GeLU(x) - x and SiLU(-x) = SiLU(x) - x (Phi(-x) = 1 - Phi(x), sigma(-x) = 1 - sigma(x))
+    np.testing.assert_allclose(A.gelu(-x), A.gelu(x) - x, atol=1e-14)
+    np.testing.assert_allclose(A.silu(-x), A.silu(x) - x, atol=1e-14)
+    assert abs(A.gelu_grad(0.0) - 0.5) < 1e-15 and abs(A.silu_grad(0.0) - 0.5) < 1e-15
+    # sigma(1) = e / (1 + e)
+    assert abs(A.silu(1.0) - 0.7310585786300049) < 1e-15
+    # saturation: identity for large positive, zero for large negative inputs
+    assert A.gelu(40.0) == 40.0 and A.gelu(-1000.0) == 0.0
+    assert A.silu(40.0) == 40.0 and A.silu(-1000.0) == 0.0
+
+
+@pytest.mark.parametrize("fn,grad", [(A.gelu, A.gelu_grad), (A.silu, A.silu_grad)])
+def test_activation_derivative_finite_difference(fn, grad):
+    x = np.linspace(-5, 5, 57)
+    e = 1e-6
+    fd = (fn(x + e) - fn(x - e)) / (2 * e)
+    np.testing.assert_allclose(grad(x), fd, atol=1e-8)
+
+
+# -------------------------------------------------------------------- dropout
+
+def test_splitmix64_published_vectors():
+    g = json.load(open(os.path.join(GOLDEN, "splitmix64.json")))
+    for v in g["vectors"]:
+        want = [int(o, 0) for o in v["outputs"]]
+        got = [int(x) for x in dropout.splitmix64_nth(v["seed"], np.arange(1, len(want) + 1))]
+        assert got == want
+
+
+def test_dropout_threshold_and_identity():
+    assert dropout.drop_threshold(0.0) == 0
+    assert dropout.drop_threshold(0.5) == 2 ** 31
+    assert dropout.drop_threshold(0.25) == 2 ** 30
+    Y = _rng(0).standard_normal((5, 7))
+    np.testing.assert_array_equal(dropout.apply(Y, 123, 0.0), Y)
+    with pytest.raises(ValueError):
+        dropout.drop_threshold(1.0)
+
+
+def test_dropout_keep_fraction_and_values():
+    rows, cols, p = 2048, 1024, 0.1
+    m = dropout.keep_mask(2099, rows, cols, p)
+    n = rows * cols
+    frac = m.mean()
+    sigma = math.sqrt(p * (1 - p) / n)
+    assert abs(frac - (1 - p)) < 6 * sigma
+    Y = np.ones((4, 9))
+    out = dropout.apply(Y, 7, 0.25)
+    vals = set(np.unique(out).tolist())
+    assert vals <= {0.0, 1.0 / 0.75}
+
+
+def test_dropout_mask_depends_only_on_global_index():
+    """The mask of a row subset equals those rows of the full mask, so it is
+    the same whatever the TP degree or the tiling ([LP] II.V)."""
+    full = dropout.keep_mask(5, 64, 48, 0.3)
+    rows = np.array([0, 3, 17, 63])
+    np.testing.assert_array_equal(dropout.keep_mask(5, rows, 48, 0.3), full[rows])
+    # flat index r*cols + c: element (r, c) of a [64, 48] tensor and element r*48+c of a [1, 3072] one agree
+    flat = dropout.keep_mask(5, 1, 64 * 48, 0.3).reshape(64, 48)
+    np.testing.assert_array_equal(flat, full)
+
+
+# ------------------------------------------------------------------- MLP fwd
+
+def _brute_mlp(X, W1, W2, act, Wu=None, b1=None, b2=None):
+    """Pure-Python loops over the definition; math.erf / math.exp only."""
+    T, h = len(X), len(X[0])
+    f = len(W1[0])
+    out = [[0.0] * h for _ in range(T)]
+    for r in range(T):
+        Hrow = []
+        for j in range(f):
+            a = sum(X[r][k] * W1[k][j] for k in range(h))
+            if act == "gelu":
+                if b1 is not None:
+                    a += b1[j]
+                Hrow.append(a * 0.5 * (1.0 + math.erf(a / math.sqrt(2.0))))
+            else:
+                u = sum(X[r][k] * Wu[k][j] for k in range(h))
+                Hrow.append(a / (1.0 + math.exp(-a)) * u)
+        for c in range(h):
+            y = sum(Hrow[j] * W2[j][c] for j in range(f))
+            if b2 is not None:
+                y += b2[c]
+            out[r][c] = y
+    return np.array(out)
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_mlp_forward_brute_force(act):
+    g = _rng(1)
+    T, h, hf = 3, 4, 6
+    X = g.standard_normal((T, h))
+    W1 = g.standard_normal((h, hf))
+    Wu = g.standard_normal((h, hf)) if act == "swiglu" else None
+    W2 = g.standard_normal((hf, h))
+    b1 = g.standard_normal(hf) if act == "gelu" else None
+    b2 = g.standard_normal(h)
+    want = _brute_mlp(X.tolist(), W1.tolist(), W2.tolist(), act,
+                      None if Wu is None else Wu.tolist(),
+                      None if b1 is None else b1.tolist(), b2.tolist())
+    got = mlp.forward(X, W1, W2, act=act, Wu=Wu, b1=b1, b2=b2)["Out"]
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-13)
+
+
+def test_mlp_forward_saturated_integer_case():
+    """Pre-activations of +/-1000 make GeLU and SiLU exact identities or zeros,
+    so the layer is exactly linear in integers and checkable by hand.
+
+    X rows are one-hot, so row r of A is row r's one-hot pick of W1 plus b1;
+    the orientation of W1 and W2, the bias placement, the gate/up roles and the
+    single addition of b2 are all visible in the integers.
+    """
+    L = 1000.0
+    # h=3 inputs, h_ffn=4 intermediate, T=3 tokens
+    X = np.eye(3)
+    W1 = np.array([[L, -L, L, -L], [-L, L, L, -L], [L, L, -L, -L]])
+    b1 = np.array([1.0, 2.0, 3.0, -2.0])       # GeLU case: shifts but keeps signs
+    W2 = np.array([[1.0, 0.0, 2.0], [0.0, 3.0, 0.0], [1.0, 1.0, 1.0], [5.0, 5.0, 5.0]])
+    b2 = np.array([10.0, 20.0, 30.0])
+    out = mlp.forward(X, W1, W2, act="gelu", b1=b1, b2=b2)["Out"]
+    # token 0: A = [L+1, -L+2, L+3, -L-2] -> H = [L+1, 0, L+3, 0]
+    want0 = np.array([(L + 1) * 1 + (L + 3) * 1, (L + 3) * 1, (L + 1) * 2 + (L + 3) * 1]) + b2
+    np.testing.assert_array_equal(out[0], want0)
+    # token 2: A = [L+1, L+2, -L+3, -L-2] -> H = [L+1, L+2, 0, 0]
+    want2 = np.array([(L + 1), 3 * (L + 2), 2 * (L + 1)]) + b2
+    np.testing.assert_array_equal(out[2], want2)
+
+    # SwiGLU: SiLU on the gate (W1), identity factor from up (Wu)
+    Wu = np.array([[2.0, 3.0, 4.0, 5.0], [6.0, 7.0, 8.0, 9.0], [1.0, 1.0, 1.0, 1.0]])
+    out = mlp.forward(X, W1, W2, act="swiglu", Wu=Wu, b2=b2)["Out"]
+    # token 1: gate = [-L, L, L, -L] -> SiLU = [0, L, L, 0]; up = [6,7,8,9] -> H = [0, 7L, 8L, 0]
+    want1 = np.array([8 * L, 21 * L + 8 * L, 8 * L]) + b2
+    np.testing.assert_array_equal(out[1], want1)
+
+
+def _mlp_case(seed, T=5, h=6, hf=8, act="gelu", bias=True):
+    g = _rng(seed)
+    return dict(
+        X=g.standard_normal((T, h)), W1=g.standard_normal((h, hf)) / 2,
+        Wu=g.standard_normal((h, hf)) / 2 if act == "swiglu" else None,
+        W2=g.standard_normal((hf, h)) / 2,
+        b1=g.standard_normal(hf) if (bias and act == "gelu") else None,
+        b2=g.standard_normal(h) if bias else None,
+        dOut=g.standard_normal((T, h)))
+
+
+def _shards(c, t, act):
+    hf = c["W1"].shape[1]
+    res = []
+    for i in range(t):
+        sl = mlp.shard_cols(hf, t, i)
+        res.append(dict(W1=c["W1"][:, sl], W2=c["W2"][sl, :],
+                        Wu=None if c["Wu"] is None else c["Wu"][:, sl],
+                        b1=None if c["b1"] is None else c["b1"][sl]))
+    return res
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+@pytest.mark.parametrize("t", [1, 2, 4])
+def test_sum_of_partials_equals_unsharded(act, t):
+    """Sigma_i Z_i = H W2 ([L11] section 3; [TP1] MLP), column pieces of H and
+    dW1/db1 and row pieces of dW2 are the unsharded ones ([L11] section 2), and
+    Sigma_i dX_i = dX ([TP1] operator f)."""
+    c = _mlp_case(10 + t, act=act)
+    p, seed = 0.2, 77
+    full = mlp.backward(c["dOut"], c["X"], c["W1"], c["W2"], act=act, Wu=c["Wu"], b1=c["b1"],
+                        b2=c["b2"], p=p, seed=seed)
+    parts, dxs, Hs, dW1s, dW2s, db1s, dWus = [], [], [], [], [], [], []
+    for s in _shards(c, t, act):
+        fw, bw = mlp.shard_step(c["dOut"], c["X"], s["W1"], s["W2"], act=act, Wu_i=s["Wu"],
+                                b1_i=s["b1"], p=p, seed=seed)
+        parts.append(fw["Z"]); Hs.append(fw["H"]); dxs.append(bw["dX"])
+        dW1s.append(bw["dW1"]); dW2s.append(bw["dW2"])
+        if act == "gelu":
+            db1s.append(bw["db1"])
+        else:
+            dWus.append(bw["dWu"])
+    out = mlp.sum_partials(parts, c["b2"], p, seed)
+    rel = lambda a, b: np.abs(a - b).max() / np.abs(b).max()
+    assert rel(out, full["fwd"]["Out"]) < 1e-12
+    assert rel(np.concatenate(Hs, 1), full["fwd"]["H"]) < 1e-13
+    assert rel(mlp.sum_partials(dxs), full["dX"]) < 1e-12
+    assert rel(np.concatenate(dW1s, 1), full["dW1"]) < 1e-12
+    assert rel(np.concatenate(dW2s, 0), full["dW2"]) < 1e-12
+    if act == "gelu":
+        assert rel(np.concatenate(db1s), full["db1"]) < 1e-12
+    else:
+        assert rel(np.concatenate(dWus, 1), full["dWu"]) < 1e-12
+
+
+def test_bias_added_per_rank_is_counted_t_times():
+    """Adding the row-parallel output bias on every rank before the sum
+    counts it t times ([L11] section 3, last paragraph)."""
+    c = _mlp_case(3)
+    t = 4
+    parts = [mlp.shard_forward(c["X"], s["W1"], s["W2"], b1_i=s["b1"])["Z"] for s in _shards(c, t, "gelu")]
+    right = mlp.sum_partials(parts, c["b2"])
+    wrong = mlp.sum_partials([P + c["b2"] for P in parts])
+    np.testing.assert_allclose(wrong - right, np.broadcast_to((t - 1) * c["b2"], right.shape), atol=1e-12)
+
+
+def test_row_first_split_does_not_commute_with_gelu():
+    """GeLU(X1 A1 + X2 A2) != GeLU(X1 A1) + GeLU(X2 A2) ([TP1] row split)."""
+    g = _rng(4)
+    X, Aw = g.standard_normal((4, 6)), g.standard_normal((6, 5))
+    lhs = A.gelu(X[:, :3] @ Aw[:3] + X[:, 3:] @ Aw[3:])
+    rhs = A.gelu(X[:, :3] @ Aw[:3]) + A.gelu(X[:, 3:] @ Aw[3:])
+    assert np.abs(lhs - rhs).max() > 1e-2
+    # while the column split commutes ([TP1] column split)
+    np.testing.assert_allclose(A.gelu(X @ Aw), np.concatenate([A.gelu(X @ Aw[:, :2]), A.gelu(X @ Aw[:, 2:])], 1),
+                               atol=1e-14)
+
+
+# ------------------------------------------------------------------- MLP bwd
+
+def _loss(c, act, p, seed, **over):
+    cc = dict(c, **over)
+    o = mlp.forward(cc["X"], cc["W1"], cc["W2"], act=act, Wu=cc["Wu"], b1=cc["b1"], b2=cc["b2"],
+                    p=p, seed=seed)["Out"]
+    return float((o * c["dOut"]).sum())
+
+
+@pytest.mark.parametrize("act,p", [("gelu", 0.0), ("gelu", 0.3), ("swiglu", 0.0), ("swiglu", 0.25)])
+def test_backward_central_differences(act, p):
+    """Every gradient of L = <dOut, Out> against central differences of the
+    forward pass (T=4, h=5, h_ffn=6)."""
+    c = _mlp_case(20, T=4, h=5, hf=6, act=act)
+    seed = 31
+    g = mlp.backward(c["dOut"], c["X"], c["W1"], c["W2"], act=act, Wu=c["Wu"], b1=c["b1"], b2=c["b2"],
+                     p=p, seed=seed)
+    names = {"X": "dX", "W1": "dW1", "W2": "dW2", "b2": "db2"}
+    if act == "gelu":
+        names["b1"] = "db1"
+    else:
+        names["Wu"] = "dWu"
+    e = 1e-6
+    for name, gname in names.items():
+        base = c[name]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            plus, minus = base.copy(), base.copy()
+            plus[idx] += e
+            minus[idx] -= e
+            fd[idx] = (_loss(c, act, p, seed, **{name: plus}) - _loss(c, act, p, seed, **{name: minus})) / (2 * e)
+        np.testing.assert_allclose(g[gname], fd, rtol=1e-6, atol=1e-7 * max(1.0, np.abs(fd).max()),
+                                   err_msg=f"{act} p={p} {gname}")
+
+
+def test_t1_shard_equals_unsharded():
+    """t = 1 is the single-card layer ([L11] section 6: correctness against a
+    single-card baseline)."""
+    c = _mlp_case(6, act="swiglu", bias=False)
+    full = mlp.backward(c["dOut"], c["X"], c["W1"], c["W2"], act="swiglu", Wu=c["Wu"])
+    fw, bw = mlp.shard_step(c["dOut"], c["X"], c["W1"], c["W2"], act="swiglu", Wu_i=c["Wu"])
+    np.testing.assert_allclose(fw["Z"], full["fwd"]["Y"], rtol=1e-14, atol=1e-14)
+    for k in ("dX", "dW1", "dWu", "dW2"):
+        np.testing.assert_allclose(bw[k], full[k], rtol=1e-13, atol=1e-13)
+
+
+def test_column_sample_and_row_sample_match_full_shard():
+    c = _mlp_case(8, T=9, h=6, hf=10, act="gelu")
+    p, seed = 0.1, 5
+    fw, bw = mlp.shard_step(c["dOut"], c["X"], c["W1"], c["W2"], b1_i=c["b1"], p=p, seed=seed)
+    cols = np.array([0, 4, 9])
+    sub_fw, sub_bw = mlp.column_sample(c["dOut"], c["X"], c["W1"], c["W2"], cols, b1_i=c["b1"], p=p, seed=seed)
+    np.testing.assert_allclose(sub_bw["dW1"], bw["dW1"][:, cols], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(sub_bw["dW2"], bw["dW2"][cols], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(sub_bw["db1"], bw["db1"][cols], rtol=1e-13, atol=1e-14)
+    rows = np.array([1, 5, 8])
+    rfw, rbw = mlp.shard_step(c["dOut"][rows], c["X"][rows], c["W1"], c["W2"], b1_i=c["b1"], p=p, seed=seed,
+                              rows=rows)
+    np.testing.assert_allclose(rfw["Z"], fw["Z"][rows], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(rbw["dX"], bw["dX"][rows], rtol=1e-13, atol=1e-14)
+
+
+# ----------------------------------------------------------------- attention
+
+def _brute_attn(Q, K, V, b, s, n_q, n_kv, d):
+    group = n_q // n_kv
+    T = b * s
+    O = [[0.0] * (n_q * d) for _ in range(T)]
+    for beta in range(b):
+        for j in range(n_q):
+            g = j // group
+            for i in range(s):
+                r = beta * s + i
+                sc = []
+                for k in range(i + 1):
+                    rk = beta * s + k
+                    sc.append(sum(Q[r][j * d + e] * K[rk][g * d + e] for e in range(d)) / math.sqrt(d))
+                m = max(sc)
+                w = [math.exp(x - m) for x in sc]
+                z = sum(w)
+                for e in range(d):
+                    O[r][j * d + e] = sum(w[k] * V[beta * s + k][g * d + e] for k in range(i + 1)) / z
+    return np.array(O)
+
+
+def test_attention_brute_force_gqa():
+    g = _rng(12)
+    b, s, n_q, n_kv, d = 2, 5, 4, 2, 3
+    Q = g.standard_normal((b * s, n_q * d))
+    K = g.standard_normal((b * s, n_kv * d))
+    V = g.standard_normal((b * s, n_kv * d))
+    O, lse = att.core(Q, K, V, b=b, s=s, n_q=n_q, n_kv=n_kv, d=d)
+    want = _brute_attn(Q.tolist(), K.tolist(), V.tolist(), b, s, n_q, n_kv, d)
+    np.testing.assert_allclose(O, want, rtol=1e-13, atol=1e-13)
+
+
+def test_attention_closed_forms():
+    g = _rng(13)
+    b, s, n_q, n_kv, d = 2, 6, 4, 2, 8
+    K = g.standard_normal((b * s, n_kv * d))
+    V = g.standard_normal((b * s, n_kv * d))
+    # Q = 0: uniform weights over the causal prefix -> prefix mean, lse = log(count)
+    O, lse = att.core(np.zeros((b * s, n_q * d)), K, V, b=b, s=s, n_q=n_q, n_kv=n_kv, d=d)
+    for beta in range(b):
+        for j in range(n_q):
+            gh = j // (n_q // n_kv)
+            v = V[beta * s:(beta + 1) * s, gh * d:(gh + 1) * d]
+            want = np.cumsum(v, 0) / np.arange(1, s + 1)[:, None]
+            np.testing.assert_allclose(O[beta * s:(beta + 1) * s, j * d:(j + 1) * d], want, atol=1e-14)
+            np.testing.assert_allclose(lse[beta, j], np.log(np.arange(1, s + 1)), atol=1e-14)
+    # s = 1: the only visible key is the token itself -> O = V of the group's KV head
+    O1, _ = att.core(g.standard_normal((3, n_q * d)), K[:3], V[:3], b=3, s=1, n_q=n_q, n_kv=n_kv, d=d)
+    for j in range(n_q):
+        gh = j // 2
+        np.testing.assert_allclose(O1[:, j * d:(j + 1) * d], V[:3, gh * d:(gh + 1) * d], atol=1e-15)
+    # two keys with scaled scores 0 and ln 3: weights 1/4 and 3/4
+    dd = 4
+    q = np.zeros((2, dd)); q[1, 0] = 1.0
+    k = np.zeros((2, dd)); k[1, 0] = math.log(3.0) * math.sqrt(dd)
+    v = np.array([[1.0, 0, 0, 0], [0, 1.0, 0, 0]])
+    O2, lse2 = att.core(q, k, v, b=1, s=2, n_q=1, n_kv=1, d=dd)
+    np.testing.assert_allclose(O2[1], [0.25, 0.75, 0, 0], atol=1e-15)
+    assert abs(lse2[0, 0, 1] - math.log(4.0)) < 1e-14
+
+
+def test_attention_sum_over_ranks_equals_unsharded():
+    """Head-sharded QKV + row-parallel out-projection: Sigma_i Z_i = Z ([L11] section 4)."""
+    g = _rng(14)
+    b, s, h, n_q, n_kv, d, t = 2, 7, 16, 8, 4, 4, 2
+    X = g.standard_normal((b * s, h))
+    Wq, Wk, Wv = (g.standard_normal((h, n * d)) / 4 for n in (n_q, n_kv, n_kv))
+    Wo = g.standard_normal((n_q * d, h)) / 4
+    full = att.forward(X, Wq, Wk, Wv, Wo, b=b, s=s, n_q=n_q, n_kv=n_kv, d=d)
+    q, kv = n_q // t, n_kv // t
+    Z = np.zeros_like(full["Z"])
+    for i in range(t):
+        Wqkv = np.concatenate([Wq[:, i * q * d:(i + 1) * q * d], Wk[:, i * kv * d:(i + 1) * kv * d],
+                               Wv[:, i * kv * d:(i + 1) * kv * d]], 1)
+        sh = att.shard_forward(X, Wqkv, Wo[i * q * d:(i + 1) * q * d], b=b, s=s, q=q, kv=kv, d=d)
+        np.testing.assert_allclose(sh["O"], full["O"][:, i * q * d:(i + 1) * q * d], rtol=1e-13, atol=1e-14)
+        Z += sh["Z"]
+        rows = np.array([0, 3, 7, 13])
+        sr = att.shard_forward_rows(X, Wqkv, Wo[i * q * d:(i + 1) * q * d], rows, b=b, s=s, q=q, kv=kv, d=d)
+        np.testing.assert_allclose(sr["Z"], sh["Z"][rows], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(sr["lse"], sh["lse"].transpose(1, 0, 2).reshape(q, -1)[:, rows], atol=1e-12)
+    np.testing.assert_allclose(Z, full["Z"], rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------- comm
+
+def _ring_allreduce_bytes(t, n_per_chunk, delta, seed=0):
+    """Simulate a ring all-reduce (reduce-scatter then all-gather) of t vectors
+    and count the bytes each rank sends."""
+    g = _rng(seed)
+    data = [g.integers(-5, 5, size=t * n_per_chunk) for _ in range(t)]
+    want = sum(data)
+    buf = [d.copy().reshape(t, n_per_chunk) for d in data]
+    sent = [0] * t
+    for step in range(t - 1):        # reduce-scatter
+        msgs = []
+        for r in range(t):
+            c = (r - step) % t
+            msgs.append(((r + 1) % t, c, buf[r][c].copy()))
+            sent[r] += n_per_chunk * delta
+        for dst, c, v in msgs:
+            buf[dst][c] += v
+    for step in range(t - 1):        # all-gather
+        msgs = []
+        for r in range(t):
+            c = (r + 1 - step) % t
+            msgs.append(((r + 1) % t, c, buf[r][c].copy()))
+            sent[r] += n_per_chunk * delta
+        for dst, c, v in msgs:
+            buf[dst][c] = v
+    for r in range(t):
+        np.testing.assert_array_equal(buf[r].reshape(-1), want)
+    return sent
+
+
+@pytest.mark.parametrize("t", [1, 2, 3, 4, 8])
+def test_comm_bytes_against_simulated_ring(t):
+    tokens, h, delta = 6, 4 * t, 2          # payload splits into t equal chunks
+    r = comm.comm_bytes(tokens, h, t, delta)
+    sent = _ring_allreduce_bytes(t, tokens * h // t, delta)
+    assert all(x == sent[0] for x in sent)
+    assert r["ring_bytes_per_rank"] == sent[0]
+    assert r["payload_bytes"] == tokens * h * delta
+    assert r["n_allreduce_fwd"] + r["n_allreduce_bwd"] == 4     # [L11] section 5; [TP1] communication cost
+    assert r["layer_ring_bytes_per_rank"] == 4 * sent[0]
+
+
+def test_comm_bytes_large_t_limit_and_dtypes():
+    """[LP] II.II quotes 8 delta b S H per layer with (t-1)/t dropped."""
+    r = comm.comm_bytes(4096, 4096, 10 ** 6, 2)
+    assert abs(r["layer_ring_bytes_per_rank"] / (8 * 2 * 4096 * 4096) - 1) < 1e-5
+    assert comm.comm_bytes(64, 128, 2, 4)["payload_bytes"] == 32768     # fp32, delta = 4
+    assert comm.comm_bytes(64, 128, 1, 4)["ring_bytes_per_rank"] == 0
+
+
+# --------------------------------------------------------------------- flops
+
+def test_flops_match_page_totals():
+    """[HJ]: GeLU MLP with d_ff = 4d: forward 16 B S d^2, backward 32 B S d^2,
+    per rank /n; attention forward 8 B S d^2 + 4 B S^2 d without causal saving."""
+    B, S, d = 3, 5, 8
+    one = flops.mlp_shard(B * S, d, 4 * d, "gelu")
+    assert one["fwd"] == 16 * B * S * d * d and one["bwd"] == 32 * B * S * d * d
+    n = 4
+    per = flops.mlp_shard(B * S, d, 4 * d // n, "gelu")
+    assert per["fwd"] * n == one["fwd"] and per["bwd"] * n == one["bwd"]
+    heads, dh = 2, d // 2
+    a = flops.attention_shard_fwd(B, S, d, heads, heads, dh, causal=False)
+    assert a["total"] == 8 * B * S * d * d + 4 * B * S * S * d
