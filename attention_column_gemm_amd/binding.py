@@ -1,0 +1,151 @@
+"""Thin ctypes binding of libtpshard (include/tp_shard.h).
+
+Argument marshalling only: tensors become device pointers, the stream becomes
+a ``hipStream_t``, and a negative status becomes a :class:`TPError`.  Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback.  Functions carry the C names and argument order.
+
+Tensor arguments may be ``torch.Tensor`` objects on the GPU (their
+``data_ptr()`` is passed), plain integers (raw device addresses) or ``None``
+for optional NULL arguments.  ``stream=None`` means torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB_PATH = os.path.join(PKG, "libtpshard.so")
+HEADER = os.path.join(ROOT, "include", "tp_shard.h")
+
+TP_F32, TP_BF16 = 0, 1
+TP_GELU, TP_SWIGLU = 0, 1
+TP_OK, TP_EINVAL, TP_ENOTDIV, TP_EDTYPE, TP_EALIGN, TP_EHIP, TP_EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+
+
+class TPError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class tp_mlp_desc(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("h", ctypes.c_int64), ("h_ffn", ctypes.c_int64),
+                ("t", ctypes.c_int32), ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32), ("act", ctypes.c_int32)]
+
+
+class tp_attn_desc(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("s", ctypes.c_int64), ("h", ctypes.c_int64),
+                ("n_q", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("d", ctypes.c_int32), ("t", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32)]
+
+
+class tp_comm(ctypes.Structure):
+    _fields_ = [("n_allreduce_fwd", ctypes.c_int32), ("n_allreduce_bwd", ctypes.c_int32),
+                ("payload_bytes", ctypes.c_uint64), ("ring_bytes_per_rank", ctypes.c_double),
+                ("layer_payload_bytes", ctypes.c_uint64), ("layer_ring_bytes_per_rank", ctypes.c_double)]
+
+
+_lib = None
+_VP = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m attention_column_gemm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.tp_mlp_shard_fwd.argtypes = [ctypes.POINTER(tp_mlp_desc)] + [_VP] * 8 + [_VP]
+        L.tp_mlp_shard_bwd.argtypes = ([ctypes.POINTER(tp_mlp_desc), _VP, ctypes.c_float, ctypes.c_uint64]
+                                       + [_VP] * 6 + [_VP, _VP, _VP, _VP, _VP, _VP, _VP] + [_VP])
+        L.tp_attn_shard_fwd.argtypes = [ctypes.POINTER(tp_attn_desc)] + [_VP] * 7 + [_VP]
+        L.tp_sum_partials.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.POINTER(_VP), _VP, ctypes.c_float, ctypes.c_uint64, _VP, _VP]
+        L.tp_comm_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.POINTER(tp_comm)]
+        L.tp_status_string.argtypes = [ctypes.c_int]
+        L.tp_status_string.restype = ctypes.c_char_p
+        for name in ("tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_attn_shard_fwd", "tp_sum_partials", "tp_comm_bytes"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def declared_functions() -> list:
+    """Names of the functions include/tp_shard.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(tp_\w+)\s*\(", text, flags=re.M)))
+
+
+def status_string(status: int) -> str:
+    return lib().tp_status_string(int(status)).decode()
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        if hasattr(x, "is_cuda") and not x.is_cuda:
+            raise ValueError("tensor arguments must live in GPU memory")
+        return x.data_ptr()
+    raise TypeError(f"cannot pass {type(x)} as a device pointer")
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, where: str):
+    if rc != TP_OK:
+        raise TPError(rc, where)
+
+
+def tp_mlp_shard_fwd(desc: tp_mlp_desc, X, W1_i, Wu_i, b1_i, W2_i, saved_i, H_i, Z_i, stream=None):
+    _check(lib().tp_mlp_shard_fwd(ctypes.byref(desc), _ptr(X), _ptr(W1_i), _ptr(Wu_i), _ptr(b1_i), _ptr(W2_i),
+                                  _ptr(saved_i), _ptr(H_i), _ptr(Z_i), _stream(stream)), "tp_mlp_shard_fwd")
+
+
+def tp_mlp_shard_bwd(desc: tp_mlp_desc, dOut, p_drop: float, seed: int, X, W1_i, Wu_i, W2_i, saved_i, H_i,
+                     dY, db2, dA_i, dW1_i, db1_i, dW2_i, dX_i, stream=None):
+    _check(lib().tp_mlp_shard_bwd(ctypes.byref(desc), _ptr(dOut), float(p_drop), int(seed) & (2 ** 64 - 1),
+                                  _ptr(X), _ptr(W1_i), _ptr(Wu_i), _ptr(W2_i), _ptr(saved_i), _ptr(H_i), _ptr(dY),
+                                  _ptr(db2), _ptr(dA_i), _ptr(dW1_i), _ptr(db1_i), _ptr(dW2_i), _ptr(dX_i),
+                                  _stream(stream)), "tp_mlp_shard_bwd")
+
+
+def tp_attn_shard_fwd(desc: tp_attn_desc, X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, Z_i, stream=None):
+    _check(lib().tp_attn_shard_fwd(ctypes.byref(desc), _ptr(X), _ptr(Wqkv_i), _ptr(Wo_i), _ptr(QKV_i), _ptr(O_i),
+                                   _ptr(lse_i), _ptr(Z_i), _stream(stream)), "tp_attn_shard_fwd")
+
+
+def tp_sum_partials(rows: int, cols: int, t: int, dtype: int, partials, bias, p_drop: float, seed: int, out,
+                    stream=None):
+    arr = (_VP * max(1, len(partials)))(*[_ptr(p) for p in partials])
+    _check(lib().tp_sum_partials(int(rows), int(cols), int(t), int(dtype), arr, _ptr(bias), float(p_drop),
+                                 int(seed) & (2 ** 64 - 1), _ptr(out), _stream(stream)), "tp_sum_partials")
+
+
+def tp_comm_bytes(tokens: int, h: int, t: int, delta: int) -> tp_comm:
+    out = tp_comm()
+    _check(lib().tp_comm_bytes(int(tokens), int(h), int(t), int(delta), ctypes.byref(out)), "tp_comm_bytes")
+    return out
+
+
+def mlp_desc(tokens, h, h_ffn, t, rank=0, dtype=TP_BF16, act=TP_GELU) -> tp_mlp_desc:
+    return tp_mlp_desc(tokens, h, h_ffn, t, rank, dtype, act)
+
+
+def attn_desc(b, s, h, n_q, n_kv, d, t, rank=0, dtype=TP_BF16, causal=1) -> tp_attn_desc:
+    return tp_attn_desc(b, s, h, n_q, n_kv, d, t, rank, dtype, causal)

@@ -1,0 +1,83 @@
+// Shared device types and helpers for the gfx950 kernels of libtpshard.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// bf16 is carried as its raw 16 bits (uint16_t) in memory.
+__device__ __forceinline__ float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 with round-to-nearest-even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Storage policies: load/store 4 consecutive elements as float.
+template <class T> struct Elem;
+template <> struct Elem<uint16_t> {
+  __device__ __forceinline__ static void load4(const uint16_t* p, float (&v)[4]) {
+    u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    v[0] = bf16lo(w.x); v[1] = bf16hi(w.x); v[2] = bf16lo(w.y); v[3] = bf16hi(w.y);
+  }
+  __device__ __forceinline__ static void store4(uint16_t* p, const float (&v)[4]) {
+    u32x2 w;
+    w.x = pack_bf16x2(v[0], v[1]);
+    w.y = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<u32x2*>(p) = w;
+  }
+  __device__ __forceinline__ static float load1(const uint16_t* p) { return bf16_to_f32(*p); }
+};
+template <> struct Elem<float> {
+  __device__ __forceinline__ static void load4(const float* p, float (&v)[4]) {
+    f32x4 w = *reinterpret_cast<const f32x4*>(p);
+    v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+  }
+  __device__ __forceinline__ static void store4(float* p, const float (&v)[4]) {
+    f32x4 w = {v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(p) = w;
+  }
+  __device__ __forceinline__ static float load1(const float* p) { return *p; }
+};
+
+// SplitMix64 output number n (1-based) of the stream seeded with `seed`
+// (Steele, Lea & Flood, OOPSLA 2014; constants of the published reference
+// implementation).
+__device__ __forceinline__ uint64_t splitmix64_nth(uint64_t seed, uint64_t n) {
+  uint64_t z = seed + n * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Dropout decision for flat element index idx of the [rows, cols] output:
+// keep iff the high 32 bits of output idx+1 are >= thr = floor(p * 2^32).
+__device__ __forceinline__ bool dropout_keep(uint64_t seed, uint64_t idx, uint32_t thr) {
+  return (uint32_t)(splitmix64_nth(seed, idx + 1) >> 32) >= thr;
+}
+
+// ---- activations (fp32) ----------------------------------------------------
+// GeLU in its exact erf form x * Phi(x); SiLU(x) = x * sigmoid(x).
+__device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_grad_f(float x) {
+  // Phi(x) + x * phi(x)
+  return 0.5f * (1.0f + erff(x * 0.70710678118654752f)) + x * 0.39894228040143268f * __expf(-0.5f * x * x);
+}
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
+
+}  // namespace tp

@@ -1,0 +1,134 @@
+// HBM-bound kernels of the shard: the emulated all-reduce (rank-ordered sum
+// of partials, bias once, dropout), dropout backward, and deterministic
+// column sums for the bias gradients.
+//
+// All three stream 16-byte vectors (8 bf16 or 4 fp32) with grid-stride loops;
+// they do no reuse, so their roofline is HBM bandwidth.
+#pragma once
+
+#include "common.hpp"
+
+namespace tp {
+
+constexpr int MAX_PARTIALS = 64;
+struct PartialPtrs {
+  const void* p[MAX_PARTIALS];
+};
+
+template <class T> struct Vec;
+template <> struct Vec<uint16_t> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void load(const uint16_t* p, float (&v)[8]) {
+    u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[2 * i] = bf16lo(w[i]); v[2 * i + 1] = bf16hi(w[i]); }
+  }
+  __device__ __forceinline__ static void store(uint16_t* p, const float (&v)[8]) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    *reinterpret_cast<u32x4*>(p) = w;
+  }
+};
+template <> struct Vec<float> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void load(const float* p, float (&v)[4]) {
+    f32x4 w = *reinterpret_cast<const f32x4*>(p);
+    v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+  }
+  __device__ __forceinline__ static void store(float* p, const float (&v)[4]) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  }
+};
+
+// out = Dropout(sum_{i<t} P_i + bias).  The partials are summed in rank order
+// in fp32; the bias is added once, after the sum; the dropout decision of flat
+// element idx comes from dropout_keep(seed, idx, thr).  cols is a multiple of
+// the vector width, so one vector lies in one row.
+template <class T>
+__global__ void __launch_bounds__(256) sum_partials_kernel(int64_t n_vec, int64_t cols, int t, PartialPtrs P,
+                                                           const T* __restrict__ bias, uint32_t thr, float scale,
+                                                           uint64_t seed, T* __restrict__ out) {
+  constexpr int V = Vec<T>::N;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < n_vec; v += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e0 = v * V;
+    float acc[V];
+    Vec<T>::load(reinterpret_cast<const T*>(P.p[0]) + e0, acc);
+    for (int i = 1; i < t; ++i) {
+      float x[V];
+      Vec<T>::load(reinterpret_cast<const T*>(P.p[i]) + e0, x);
+#pragma unroll
+      for (int j = 0; j < V; ++j) acc[j] += x[j];
+    }
+    if (bias) {
+      float b[V];
+      Vec<T>::load(bias + (e0 % cols), b);
+#pragma unroll
+      for (int j = 0; j < V; ++j) acc[j] += b[j];
+    }
+    if (thr) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) acc[j] = dropout_keep(seed, (uint64_t)(e0 + j), thr) ? acc[j] * scale : 0.0f;
+    }
+    Vec<T>::store(out + e0, acc);
+  }
+}
+
+// dY = dOut * keep / (1 - p)  (thr = 0: plain copy).
+template <class T>
+__global__ void __launch_bounds__(256) dropout_bwd_kernel(int64_t n_vec, const T* __restrict__ dOut, uint32_t thr,
+                                                          float scale, uint64_t seed, T* __restrict__ dY) {
+  constexpr int V = Vec<T>::N;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < n_vec; v += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e0 = v * V;
+    float x[V];
+    Vec<T>::load(dOut + e0, x);
+    if (thr) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) x[j] = dropout_keep(seed, (uint64_t)(e0 + j), thr) ? x[j] * scale : 0.0f;
+    }
+    Vec<T>::store(dY + e0, x);
+  }
+}
+
+// out[c] = sum over rows of X[r, c] in fp32, in a fixed order (so repeated
+// runs agree bit for bit).  A work-group owns COLS_PER_WG columns: its threads
+// are (COLS_PER_WG / V) column vectors x ROW_LANES row lanes; lane l sums rows
+// l, l + ROW_LANES, ... and the lanes are then folded pairwise through LDS.
+template <class T>
+__global__ void __launch_bounds__(256) colsum_kernel(int64_t rows, int64_t cols, int64_t ld, const T* __restrict__ X,
+                                                     float* __restrict__ out) {
+  constexpr int V = Vec<T>::N;
+  constexpr int CV = 8;                      // column vectors per work-group
+  constexpr int ROW_LANES = 256 / CV;        // 32
+  __shared__ float red[ROW_LANES][CV * V + 1];
+  const int cv = threadIdx.x % CV, rl = threadIdx.x / CV;
+  const int64_t c0 = (int64_t)blockIdx.x * CV * V + cv * V;
+  float acc[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) acc[j] = 0.0f;
+  if (c0 < cols) {
+    for (int64_t r = rl; r < rows; r += ROW_LANES) {
+      float x[V];
+      Vec<T>::load(X + r * ld + c0, x);
+#pragma unroll
+      for (int j = 0; j < V; ++j) acc[j] += x[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < V; ++j) red[rl][cv * V + j] = acc[j];
+  __syncthreads();
+  for (int s = ROW_LANES / 2; s > 0; s >>= 1) {
+    if (rl < s) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) red[rl][cv * V + j] += red[rl + s][cv * V + j];
+    }
+    __syncthreads();
+  }
+  if (rl == 0 && c0 < cols) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) out[c0 + j] = red[0][cv * V + j];
+  }
+}
+
+}  // namespace tp

@@ -1,0 +1,256 @@
+// bf16 GEMM on the gfx950 matrix cores: C = sum over segments of A_s B_s,
+// fp32 accumulation, result handed to a fused epilogue.
+//
+// Used for every dense contraction of the shard: the column-parallel GEMM
+// with its activation, the row-parallel GEMM yielding a partial, their input-
+// and weight-gradient GEMMs, the QKV and output projections.
+//
+// Design (gfx950, 64-wide waves):
+//  * 256 threads = 4 waves in a 2x2 grid; block tile BM x BN (per B operand),
+//    K step 64; each wave owns a (BM/2) x (BN/2) sub-tile built from 32x32x16
+//    bf16 MFMAs (v_mfma_f32_32x32x16_bf16).
+//  * Both operands are staged through LDS as [rows][64] bf16 with K
+//    contiguous; the 16-byte chunk c of row r lives at chunk c ^ (r & 7) so the
+//    128-bit fragment reads of 8 consecutive rows hit distinct banks.
+//    Operands whose K is the slow dimension in HBM (A stored [K,M] or B stored
+//    [K,N]) are loaded as 8x8 bf16 blocks with 16-byte row reads and
+//    transposed in registers before the LDS write, so every layout feeds the
+//    same fragment reads.
+//  * Two LDS stages: the global loads of K-tile k+1 are issued before the
+//    MFMAs of tile k and written to the other stage after them; one barrier
+//    per K-tile.
+//  * The MFMA is issued with the B fragment as its first operand, so each
+//    lane's accumulators hold four consecutive output columns of one row:
+//    the epilogue stores 8 (bf16) or 16 (fp32) contiguous bytes per lane.
+//  * Up to two B operands share one A tile (SwiGLU gate and up; dWg and dWu),
+//    and up to two (A, B) segments accumulate into one result
+//    (dX_i = dG_i Wg_i^T + dU_i Wu_i^T).
+//  * Work-group -> tile mapping: the hardware deals work-groups to the 8 XCDs
+//    round-robin; the mapping hands each XCD a contiguous run of tiles and
+//    walks them in groups of GROUP_M tile rows so that the tiles resident on
+//    one XCD share A rows and B columns in that XCD's L2.
+#pragma once
+
+#include "common.hpp"
+
+namespace tp {
+
+enum OperandLayout {
+  KMAJOR = 0,   // A stored [M, K] / B stored [N, K]: K contiguous
+  MNMAJOR = 1,  // A stored [K, M] / B stored [K, N]: M or N contiguous
+};
+
+struct GemmProblem {
+  int M, N;
+  int nseg;                  // 1 or 2 K segments summed into one result
+  int K[2];
+  const uint16_t* A[2];      // [segment]
+  const uint16_t* B[2][2];   // [segment][B operand]
+  int64_t lda[2], ldb[2];    // leading dimensions (elements) per segment
+};
+
+namespace gemm {
+
+constexpr int BK = 64;
+constexpr int NTHREADS = 256;
+constexpr int GROUP_M = 4;
+
+// Element offset of 16-byte chunk `chunk` of LDS tile row `row`.
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
+
+template <int ROWS, int LAYOUT>
+struct TileLoader;
+
+// K contiguous in HBM: each thread moves 16-byte chunks (row, kc).
+template <int ROWS>
+struct TileLoader<ROWS, KMAJOR> {
+  static constexpr int PER = ROWS * (BK / 8) / NTHREADS;
+  u32x4 r[PER];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ g, int64_t ld, int row0, int nrows, int k0, int K) {
+    const int tid = threadIdx.x, kc = tid & 7;
+    const int k = k0 + kc * 8;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int gr = row0 + (tid >> 3) + 32 * i;
+      if (gr < nrows && k < K)
+        r[i] = *reinterpret_cast<const u32x4*>(g + (int64_t)gr * ld + k);
+      else
+        r[i] = u32x4{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* s) const {
+    const int tid = threadIdx.x, kc = tid & 7;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int row = (tid >> 3) + 32 * i;
+      *reinterpret_cast<u32x4*>(s + lds_off(row, kc)) = r[i];
+    }
+  }
+};
+
+// M/N contiguous in HBM: a thread loads an 8 (k) x 8 (rows) block with eight
+// 16-byte reads and writes it transposed as eight 16-byte LDS rows.
+template <int ROWS>
+struct TileLoader<ROWS, MNMAJOR> {
+  static constexpr int NBLK = ROWS;  // (ROWS/8 row groups) x (8 k groups)
+  static_assert(NBLK <= NTHREADS, "one 8x8 block per thread at most");
+  u32x4 r[8];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ g, int64_t ld, int row0, int nrows, int k0, int K) {
+    const int tid = threadIdx.x;
+    if (tid >= NBLK) return;
+    const int mg = tid % (ROWS / 8), kg = tid / (ROWS / 8);
+    const int gr = row0 + mg * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = k0 + kg * 8 + j;
+      if (gr < nrows && k < K)
+        r[j] = *reinterpret_cast<const u32x4*>(g + (int64_t)k * ld + gr);
+      else
+        r[j] = u32x4{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* s) const {
+    const int tid = threadIdx.x;
+    if (tid >= NBLK) return;
+    const int mg = tid % (ROWS / 8), kg = tid / (ROWS / 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      u32x4 w;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = r[2 * q][i >> 1], hi = r[2 * q + 1][i >> 1];
+        w[q] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      }
+      const int row = mg * 8 + i;
+      *reinterpret_cast<u32x4*>(s + lds_off(row, kg)) = w;
+    }
+  }
+};
+
+// Tile coordinates of this work-group (see the header comment).
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  const int w = blockIdx.x;
+  const int q = total >> 3, r = total & 7, x = w & 7;
+  const int L = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + (w >> 3);
+  const int per_group = GROUP_M * tiles_n;
+  const int g = L / per_group;
+  const int first_m = g * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int inner = L - g * per_group;
+  tm = first_m + inner % gsize;
+  tn = inner / gsize;
+}
+
+template <int BM, int BN, int AL, int BL, class Epi>
+__global__ void __launch_bounds__(NTHREADS, 1) gemm_bf16_kernel(GemmProblem p, Epi epi) {
+  constexpr int NB = Epi::NB;
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int STAGE = (BM + NB * BN) * BK;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  f32x16 acc[NB][TM][TN];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[b][i][j][e] = 0.0f;
+
+  TileLoader<BM, AL> la;
+  TileLoader<BN, BL> lb[NB];
+  const int nk0 = (p.K[0] + BK - 1) / BK;
+  const int nk = nk0 + (p.nseg > 1 ? (p.K[1] + BK - 1) / BK : 0);
+
+  auto issue = [&](int kt) {
+    const int s = kt < nk0 ? 0 : 1;
+    const int k0 = (kt - (s ? nk0 : 0)) * BK;
+    la.load(p.A[s], p.lda[s], m0, p.M, k0, p.K[s]);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) lb[b].load(p.B[s][b], p.ldb[s], n0, p.N, k0, p.K[s]);
+  };
+  auto commit = [&](int stage) {
+    uint16_t* s = smem + stage * STAGE;
+    la.store(s);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) lb[b].store(s + BM * BK + b * BN * BK);
+  };
+
+  if (nk > 0) {
+    issue(0);
+    commit(0);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int stage = kt & 1;
+    if (kt + 1 < nk) issue(kt + 1);
+    const uint16_t* As = smem + stage * STAGE;
+    const uint16_t* Bs = As + BM * BK;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int chunk = kk * 2 + (lane >> 5);
+      bf16x8 af[TM], bfr[NB][TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(As + lds_off(wm * WM + i * 32 + (lane & 31), chunk));
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          bfr[b][j] = *reinterpret_cast<const bf16x8*>(Bs + b * BN * BK + lds_off(wn * WN + j * 32 + (lane & 31), chunk));
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[b][j], af[i], acc[b][i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) commit(stage ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: lane holds, for tile (i, j), row m = .. + (lane & 31) and columns
+  // n = .. + 8*q4 + 4*(lane >> 5) + e, e = 0..3, in accumulator slots 4*q4 + e.
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + wm * WM + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int n = n0 + wn * WN + j * 32 + q4 * 8 + (lane >> 5) * 4;
+        float v[NB][4];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[b][e] = acc[b][i][j][q4 * 4 + e];
+        epi(m, n, v);
+      }
+    }
+  }
+}
+
+}  // namespace gemm
+
+// Host-side launcher: grid of ceil(M/BM) * ceil(N/BN) work-groups of 256 threads.
+template <int BM, int BN, int AL, int BL, class Epi>
+hipError_t launch_gemm_bf16(const GemmProblem& p, const Epi& epi, hipStream_t stream) {
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm::gemm_bf16_kernel<BM, BN, AL, BL, Epi>), dim3(tiles), dim3(gemm::NTHREADS), 0, stream, p, epi);
+  return hipGetLastError();
+}
+
+}  // namespace tp

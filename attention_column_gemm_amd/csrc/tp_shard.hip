@@ -1,0 +1,415 @@
+// libtpshard: C ABI of one tensor-parallel rank's Megatron-style layer shard
+// on gfx950.  Argument validation, tile-configuration choice and kernel
+// launches on the caller's stream; the kernels live in the headers next to
+// this file.  The interface is declared and documented in include/tp_shard.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <initializer_list>
+#include <type_traits>
+
+#include "../../include/tp_shard.h"
+#include "attention.hpp"
+#include "elementwise.hpp"
+#include "epilogues.hpp"
+#include "gemm_mfma.hpp"
+#include "gemm_simt.hpp"
+
+using namespace tp;
+
+namespace {
+
+constexpr int kNumCUs = 256;
+
+// Profiling aid (tp_profile_arm): events recorded around the next kernels.
+struct ProfileHook {
+  hipEvent_t ev[64];
+  int n_kernels = 0;  // kernels still to bracket
+  int next = 0;
+} g_prof;
+
+// Brackets one kernel launch with the armed events, if any.
+struct Probe {
+  hipStream_t st;
+  int idx = -1;
+  explicit Probe(hipStream_t s) : st(s) {
+    if (g_prof.next < g_prof.n_kernels) {
+      idx = g_prof.next++;
+      hipEventRecord(g_prof.ev[2 * idx], st);
+    }
+  }
+  ~Probe() {
+    if (idx >= 0) hipEventRecord(g_prof.ev[2 * idx + 1], st);
+  }
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool fits_int(int64_t v) { return v >= 0 && v <= INT32_MAX; }
+
+int check_dropout(float p, uint32_t* thr, float* scale) {
+  if (!(p >= 0.0f && p < 1.0f)) return TP_EINVAL;
+  // floor(p * 2^32), p taken exactly as the float it is.
+  *thr = (uint32_t)std::floor((double)p * 4294967296.0);
+  *scale = 1.0f / (1.0f - p);
+  return TP_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TP_OK : TP_EHIP; }
+
+GemmProblem problem(int M, int N, int K, const void* A, int64_t lda, const void* B0, const void* B1, int64_t ldb) {
+  GemmProblem p{};
+  p.M = M;
+  p.N = N;
+  p.nseg = 1;
+  p.K[0] = K;
+  p.K[1] = 0;
+  p.A[0] = static_cast<const uint16_t*>(A);
+  p.B[0][0] = static_cast<const uint16_t*>(B0);
+  p.B[0][1] = static_cast<const uint16_t*>(B1);
+  p.lda[0] = p.lda[1] = lda;
+  p.ldb[0] = p.ldb[1] = ldb;
+  return p;
+}
+
+// Tile choice: the large tile unless it leaves most of the 256 CUs idle, in
+// which case the quarter-size tile (more work-groups) is used.  Cost model:
+// waves of work-groups x tile area, with the small tile charged 1.3x per
+// element for its lower operand reuse.
+// TPSHARD_TILE=large|small overrides the choice (used by the tests to cover
+// both tile shapes at small sizes).
+bool use_small_tile(int M, int N, int bm, int bn) {
+  if (const char* force = std::getenv("TPSHARD_TILE")) {
+    if (!std::strcmp(force, "large")) return false;
+    if (!std::strcmp(force, "small")) return true;
+  }
+  auto waves = [](int64_t tiles) { return (tiles + kNumCUs - 1) / kNumCUs; };
+  const int64_t big = (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  const int64_t small = (int64_t)((M + bm / 2 - 1) / (bm / 2)) * ((N + bn / 2 - 1) / (bn / 2));
+  const double cost_big = (double)waves(big) * bm * bn;
+  const double cost_small = 1.3 * (double)waves(small) * (bm / 2) * (bn / 2);
+  return cost_small < cost_big;
+}
+
+template <int AL, int BL, class Epi>
+hipError_t gemm_bf16(const GemmProblem& p, const Epi& epi, hipStream_t st) {
+  if constexpr (Epi::NB == 1) {
+    Probe pr(st);
+    if (use_small_tile(p.M, p.N, 256, 256)) return launch_gemm_bf16<128, 128, AL, BL>(p, epi, st);
+    return launch_gemm_bf16<256, 256, AL, BL>(p, epi, st);
+  } else {
+    Probe pr(st);
+    if (use_small_tile(p.M, p.N, 256, 128)) return launch_gemm_bf16<128, 64, AL, BL>(p, epi, st);
+    return launch_gemm_bf16<256, 128, AL, BL>(p, epi, st);
+  }
+}
+
+// Operands stored in bf16 run on the matrix cores, operands stored in fp32 on
+// the vector ALUs (S is the operand storage type).
+template <class S, int AL, int BL, class Epi>
+hipError_t gemm_any(const GemmProblem& p, const Epi& epi, hipStream_t st) {
+  if constexpr (std::is_same_v<S, float>) {
+    Probe pr(st);
+    return launch_gemm_f32<AL, BL>(p, epi, st);
+  }
+  else
+    return gemm_bf16<AL, BL>(p, epi, st);
+}
+
+unsigned grid_for(int64_t n_vec) {
+  int64_t blocks = (n_vec + 255) / 256;
+  if (blocks > 16 * kNumCUs) blocks = 16 * kNumCUs;
+  return (unsigned)(blocks < 1 ? 1 : blocks);
+}
+
+template <class T>
+hipError_t dropout_bwd(int64_t n, const void* dOut, uint32_t thr, float scale, uint64_t seed, void* dY, hipStream_t st) {
+  const int64_t nv = n / Vec<T>::N;
+  if (nv == 0) return hipSuccess;
+  Probe pr(st);
+  hipLaunchKernelGGL(dropout_bwd_kernel<T>, dim3(grid_for(nv)), dim3(256), 0, st, nv, static_cast<const T*>(dOut), thr,
+                     scale, seed, static_cast<T*>(dY));
+  return hipGetLastError();
+}
+
+template <class T>
+hipError_t colsum(int64_t rows, int64_t cols, const void* X, float* out, hipStream_t st) {
+  const int64_t per_wg = 8 * Vec<T>::N;
+  const int64_t blocks = (cols + per_wg - 1) / per_wg;
+  if (blocks == 0) return hipSuccess;
+  Probe pr(st);
+  hipLaunchKernelGGL(colsum_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st, rows, cols, cols,
+                     static_cast<const T*>(X), out);
+  return hipGetLastError();
+}
+
+template <class T>
+int mlp_fwd_impl(const tp_mlp_desc& d, const void* X, const void* W1, const void* Wu, const void* b1,
+                 const void* W2, void* saved, void* H, void* Z, hipStream_t st) {
+  const int T_ = (int)d.tokens, h = (int)d.h, f = (int)(d.h_ffn / d.t);
+  hipError_t e;
+  if (d.act == TP_GELU) {
+    EpiGeluFwd<T> epi{static_cast<T*>(saved), static_cast<T*>(H), static_cast<const T*>(b1), f, T_, f};
+    e = gemm_any<T, KMAJOR, MNMAJOR>(problem(T_, f, h, X, h, W1, nullptr, f), epi, st);
+  } else {
+    T* G = static_cast<T*>(saved);
+    EpiSwigluFwd<T> epi{G, G + (int64_t)T_ * f, static_cast<T*>(H), f, T_, f};
+    e = gemm_any<T, KMAJOR, MNMAJOR>(problem(T_, f, h, X, h, W1, Wu, f), epi, st);
+  }
+  if (e != hipSuccess) return TP_EHIP;
+  EpiStore<T> epi2{static_cast<T*>(Z), h, T_, h};
+  return hip_status(gemm_any<T, KMAJOR, MNMAJOR>(problem(T_, h, f, H, f, W2, nullptr, h), epi2, st));
+}
+
+template <class T>
+int mlp_bwd_impl(const tp_mlp_desc& d, const void* dOut, uint32_t thr, float scale, uint64_t seed,
+                 const void* X, const void* W1, const void* Wu, const void* W2, const void* saved, const void* H,
+                 void* dY, float* db2, void* dA, float* dW1, float* db1, float* dW2, void* dX, hipStream_t st) {
+  const int T_ = (int)d.tokens, h = (int)d.h, f = (int)(d.h_ffn / d.t);
+  const int64_t Tf = (int64_t)T_ * f;
+  hipError_t e = hipSuccess;
+  // a4: dropout backward (or a copy when dY is requested with p = 0)
+  const void* dYp = dOut;
+  if (dY) {
+    if ((e = dropout_bwd<T>((int64_t)T_ * h, dOut, thr, scale, seed, dY, st)) != hipSuccess) return TP_EHIP;
+    dYp = dY;
+  }
+  if (db2 && (e = colsum<T>(T_, h, dYp, db2, st)) != hipSuccess) return TP_EHIP;
+  // a5: dH = dY W2^T with the activation backward fused
+  if (d.act == TP_GELU) {
+    EpiGeluBwd<T> epi{static_cast<const T*>(saved), static_cast<T*>(dA), f, T_, f};
+    e = gemm_any<T, KMAJOR, KMAJOR>(problem(T_, f, h, dYp, h, W2, nullptr, h), epi, st);
+  } else {
+    const T* G = static_cast<const T*>(saved);
+    T* dG = static_cast<T*>(dA);
+    EpiSwigluBwd<T> epi{G, G + Tf, dG, dG + Tf, f, T_, f};
+    e = gemm_any<T, KMAJOR, KMAJOR>(problem(T_, f, h, dYp, h, W2, nullptr, h), epi, st);
+  }
+  if (e != hipSuccess) return TP_EHIP;
+  if (db1 && (e = colsum<T>(T_, f, dA, db1, st)) != hipSuccess) return TP_EHIP;
+  // a5: dW2_i = H_i^T dY   ([f, h], K = tokens)
+  {
+    EpiStore<float> epi{dW2, h, f, h};
+    if ((e = gemm_any<T, MNMAJOR, MNMAJOR>(problem(f, h, T_, H, f, dYp, nullptr, h), epi, st)) != hipSuccess)
+      return TP_EHIP;
+  }
+  // a6: dW1_i = X^T dA_i  ([h, f], K = tokens); SwiGLU: dWg_i and dWu_i share the X^T tile
+  if (d.act == TP_GELU) {
+    EpiStore<float> epi{dW1, f, h, f};
+    e = gemm_any<T, MNMAJOR, MNMAJOR>(problem(h, f, T_, X, h, dA, nullptr, f), epi, st);
+  } else {
+    const T* dG = static_cast<const T*>(dA);
+    EpiStore2<float> epi{dW1, dW1 + (int64_t)h * f, f, h, f};
+    e = gemm_any<T, MNMAJOR, MNMAJOR>(problem(h, f, T_, X, h, dG, dG + Tf, f), epi, st);
+  }
+  if (e != hipSuccess) return TP_EHIP;
+  // a6: dX_i = dA_i W1_i^T  (SwiGLU: dG_i Wg_i^T + dU_i Wu_i^T, two K segments into one accumulator)
+  {
+    EpiStore<T> epi{static_cast<T*>(dX), h, T_, h};
+    GemmProblem p = problem(T_, h, f, dA, f, W1, nullptr, f);
+    if (d.act == TP_SWIGLU) {
+      p.nseg = 2;
+      p.K[1] = f;
+      p.A[1] = reinterpret_cast<const uint16_t*>(static_cast<const T*>(dA) + Tf);
+      p.B[1][0] = static_cast<const uint16_t*>(Wu);
+    }
+    e = gemm_any<T, KMAJOR, KMAJOR>(p, epi, st);
+  }
+  return hip_status(e);
+}
+
+int validate_mlp(const tp_mlp_desc* d, bool* bf16) {
+  if (!d) return TP_EINVAL;
+  if (d->dtype != TP_F32 && d->dtype != TP_BF16) return TP_EDTYPE;
+  if (d->act != TP_GELU && d->act != TP_SWIGLU) return TP_EDTYPE;
+  if (d->t < 1 || d->rank < 0 || d->rank >= d->t) return TP_EINVAL;
+  if (!fits_int(d->tokens) || !fits_int(d->h) || !fits_int(d->h_ffn)) return TP_EINVAL;
+  if (d->h_ffn % d->t) return TP_ENOTDIV;
+  *bf16 = d->dtype == TP_BF16;
+  const int vec = *bf16 ? 8 : 4;
+  if (d->h % vec || (d->h_ffn / d->t) % vec) return TP_EALIGN;
+  return TP_OK;
+}
+
+// A tensor argument is present when its pointer is non-null or it holds no elements.
+bool present(const void* p, int64_t n) { return p != nullptr || n == 0; }
+
+bool ptrs_aligned(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && !aligned16(p)) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_profile_arm(void* const* events, int32_t n_events) {
+  if (n_events < 0 || n_events > 64 || (n_events & 1) || (n_events && !events)) return TP_EINVAL;
+  for (int i = 0; i < n_events; ++i) {
+    if (!events[i]) return TP_EINVAL;
+    g_prof.ev[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  g_prof.n_kernels = n_events / 2;
+  g_prof.next = 0;
+  return TP_OK;
+}
+
+const char* tp_status_string(int s) {
+  switch (s) {
+    case TP_OK: return "TP_OK";
+    case TP_EINVAL: return "TP_EINVAL: invalid argument";
+    case TP_ENOTDIV: return "TP_ENOTDIV: size not divisible by the TP degree or head grouping";
+    case TP_EDTYPE: return "TP_EDTYPE: unsupported dtype or activation";
+    case TP_EALIGN: return "TP_EALIGN: pointer or width not aligned to 16 bytes";
+    case TP_EHIP: return "TP_EHIP: HIP runtime error at launch";
+    case TP_EUNSUPPORTED: return "TP_EUNSUPPORTED: size not implemented by the kernels";
+    default: return "unknown status";
+  }
+}
+
+int tp_comm_bytes(int64_t tokens, int64_t h, int32_t t, int32_t delta, tp_comm* out) {
+  if (!out || tokens < 0 || h < 0 || t < 1 || delta < 1) return TP_EINVAL;
+  const uint64_t payload = (uint64_t)tokens * (uint64_t)h * (uint64_t)delta;
+  out->n_allreduce_fwd = 2;
+  out->n_allreduce_bwd = 2;
+  out->payload_bytes = payload;
+  out->ring_bytes_per_rank = 2.0 * (double)(t - 1) / (double)t * (double)payload;
+  out->layer_payload_bytes = 4 * payload;
+  out->layer_ring_bytes_per_rank = 4.0 * out->ring_bytes_per_rank;
+  return TP_OK;
+}
+
+int tp_mlp_shard_fwd(const tp_mlp_desc* desc, const void* X, const void* W1_i, const void* Wu_i, const void* b1_i,
+                     const void* W2_i, void* saved_i, void* H_i, void* Z_i, void* stream) {
+  bool bf16 = false;
+  int rc = validate_mlp(desc, &bf16);
+  if (rc) return rc;
+  {
+    const int64_t T_ = desc->tokens, h = desc->h, f = desc->h_ffn / desc->t, ns = desc->act == TP_GELU ? 1 : 2;
+    if (!present(X, T_ * h) || !present(W1_i, h * f) || !present(W2_i, f * h) || !present(saved_i, ns * T_ * f) ||
+        !present(H_i, T_ * f) || !present(Z_i, T_ * h) || (desc->act == TP_SWIGLU && !present(Wu_i, h * f)))
+      return TP_EINVAL;
+  }
+  if (desc->act == TP_GELU ? (Wu_i != nullptr) : (b1_i != nullptr)) return TP_EINVAL;
+  if (!ptrs_aligned({X, W1_i, Wu_i, b1_i, W2_i, saved_i, H_i, Z_i})) return TP_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return bf16 ? mlp_fwd_impl<uint16_t>(*desc, X, W1_i, Wu_i, b1_i, W2_i, saved_i, H_i, Z_i, st)
+              : mlp_fwd_impl<float>(*desc, X, W1_i, Wu_i, b1_i, W2_i, saved_i, H_i, Z_i, st);
+}
+
+int tp_mlp_shard_bwd(const tp_mlp_desc* desc, const void* dOut, float p_drop, uint64_t seed, const void* X,
+                     const void* W1_i, const void* Wu_i, const void* W2_i, const void* saved_i, const void* H_i,
+                     void* dY, float* db2, void* dA_i, float* dW1_i, float* db1_i, float* dW2_i, void* dX_i,
+                     void* stream) {
+  bool bf16 = false;
+  int rc = validate_mlp(desc, &bf16);
+  if (rc) return rc;
+  uint32_t thr = 0;
+  float scale = 1.0f;
+  if ((rc = check_dropout(p_drop, &thr, &scale))) return rc;
+  {
+    const int64_t T_ = desc->tokens, h = desc->h, f = desc->h_ffn / desc->t, ns = desc->act == TP_GELU ? 1 : 2;
+    if (!present(dOut, T_ * h) || !present(X, T_ * h) || !present(W1_i, h * f) || !present(W2_i, f * h) ||
+        !present(saved_i, ns * T_ * f) || !present(H_i, T_ * f) || !present(dA_i, ns * T_ * f) ||
+        !present(dW1_i, ns * h * f) || !present(dW2_i, f * h) || !present(dX_i, T_ * h) ||
+        (desc->act == TP_SWIGLU && !present(Wu_i, h * f)))
+      return TP_EINVAL;
+  }
+  if (desc->act == TP_GELU ? (Wu_i != nullptr) : (db1_i != nullptr)) return TP_EINVAL;
+  if (thr != 0 && !dY) return TP_EINVAL;
+  if (!ptrs_aligned({dOut, X, W1_i, Wu_i, W2_i, saved_i, H_i, dY, db2, dA_i, dW1_i, db1_i, dW2_i, dX_i}))
+    return TP_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return bf16 ? mlp_bwd_impl<uint16_t>(*desc, dOut, thr, scale, seed, X, W1_i, Wu_i, W2_i, saved_i, H_i, dY,
+                                       db2, dA_i, dW1_i, db1_i, dW2_i, dX_i, st)
+              : mlp_bwd_impl<float>(*desc, dOut, thr, scale, seed, X, W1_i, Wu_i, W2_i, saved_i, H_i, dY, db2,
+                                    dA_i, dW1_i, db1_i, dW2_i, dX_i, st);
+}
+
+int tp_attn_shard_fwd(const tp_attn_desc* d, const void* X, const void* Wqkv_i, const void* Wo_i, void* QKV_i,
+                      void* O_i, float* lse_i, void* Z_i, void* stream) {
+  if (!d) return TP_EINVAL;
+  if (d->dtype != TP_BF16) return TP_EDTYPE;
+  if (d->b < 0 || d->s < 0 || d->h < 0 || d->n_q < 1 || d->n_kv < 1 || d->d < 1 || d->t < 1 || d->rank < 0 ||
+      d->rank >= d->t)
+    return TP_EINVAL;
+  if (d->n_q % d->t || d->n_kv % d->t || d->n_q % d->n_kv) return TP_ENOTDIV;
+  if (d->d != 64 && d->d != 128) return TP_EUNSUPPORTED;
+  if (!fits_int(d->b * d->s) || !fits_int(d->h)) return TP_EINVAL;
+  {
+    const int64_t T_ = d->b * d->s, nq = (int64_t)(d->n_q / d->t) * d->d, nkv = (int64_t)(d->n_kv / d->t) * d->d;
+    if (!present(X, T_ * d->h) || !present(Wqkv_i, d->h * (nq + 2 * nkv)) || !present(Wo_i, nq * d->h) ||
+        !present(QKV_i, T_ * (nq + 2 * nkv)) || !present(O_i, T_ * nq) || !present(Z_i, T_ * d->h))
+      return TP_EINVAL;
+  }
+  if (d->h % 8) return TP_EALIGN;
+  if (!ptrs_aligned({X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, Z_i})) return TP_EALIGN;
+  const int q = d->n_q / d->t, kv = d->n_kv / d->t, D = d->d;
+  const int T_ = (int)(d->b * d->s), h = (int)d->h;
+  const int nqkv = (q + 2 * kv) * D;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // QKV_i = X Wqkv_i
+  EpiStore<uint16_t> e1{static_cast<uint16_t*>(QKV_i), nqkv, T_, nqkv};
+  if (gemm_bf16<KMAJOR, MNMAJOR>(problem(T_, nqkv, h, X, h, Wqkv_i, nullptr, nqkv), e1, st) != hipSuccess)
+    return TP_EHIP;
+  // local heads' attention
+  attn::AttnArgs a{};
+  a.qkv = static_cast<const uint16_t*>(QKV_i);
+  a.o = static_cast<uint16_t*>(O_i);
+  a.lse = lse_i;
+  a.ld_qkv = nqkv;
+  a.ld_o = (int64_t)q * D;
+  a.b = (int)d->b;
+  a.s = (int)d->s;
+  a.q = q;
+  a.kv = kv;
+  const int group = q / kv;
+  a.hg = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+  a.causal = d->causal ? 1 : 0;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  hipError_t e;
+  {
+    Probe pr(st);
+    e = D == 128 ? launch_attn_fwd<128>(a, st) : launch_attn_fwd<64>(a, st);
+  }
+  if (e != hipSuccess) return TP_EHIP;
+  // Z_i = O_i Wo_i
+  EpiStore<uint16_t> e2{static_cast<uint16_t*>(Z_i), h, T_, h};
+  return hip_status(gemm_bf16<KMAJOR, MNMAJOR>(problem(T_, h, q * D, O_i, q * D, Wo_i, nullptr, h), e2, st));
+}
+
+int tp_sum_partials(int64_t rows, int64_t cols, int32_t t, int32_t dtype, const void* const* partials,
+                    const void* bias, float p_drop, uint64_t seed, void* out, void* stream) {
+  if (dtype != TP_F32 && dtype != TP_BF16) return TP_EDTYPE;
+  if (rows < 0 || cols < 0 || t < 1 || !partials || !present(out, rows * cols)) return TP_EINVAL;
+  if (t > MAX_PARTIALS) return TP_EUNSUPPORTED;
+  uint32_t thr = 0;
+  float scale = 1.0f;
+  int rc = check_dropout(p_drop, &thr, &scale);
+  if (rc) return rc;
+  const int vec = dtype == TP_BF16 ? 8 : 4;
+  if (cols % vec) return TP_EALIGN;
+  PartialPtrs P{};
+  for (int i = 0; i < t; ++i) {
+    if (!present(partials[i], rows * cols)) return TP_EINVAL;
+    if (!aligned16(partials[i])) return TP_EALIGN;
+    P.p[i] = partials[i];
+  }
+  if (!ptrs_aligned({bias, out})) return TP_EALIGN;
+  const int64_t nv = rows * cols / vec;
+  if (nv == 0) return TP_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Probe pr(st);
+  if (dtype == TP_BF16)
+    hipLaunchKernelGGL(sum_partials_kernel<uint16_t>, dim3(grid_for(nv)), dim3(256), 0, st, nv, cols, t, P,
+                       static_cast<const uint16_t*>(bias), thr, scale, seed, static_cast<uint16_t*>(out));
+  else
+    hipLaunchKernelGGL(sum_partials_kernel<float>, dim3(grid_for(nv)), dim3(256), 0, st, nv, cols, t, P,
+                       static_cast<const float*>(bias), thr, scale, seed, static_cast<float*>(out));
+  return hip_status(hipGetLastError());
+}
+
+}  // extern "C"

@@ -1,0 +1,340 @@
+"""Benchmark: one TP rank's layer shard on one MI355X, through the C ABI.
+
+A step is one pass of the whole hot path for rank 0 of the chosen workload:
+attention shard forward (QKV GEMM, causal GQA attention, output projection),
+its emulated all-reduce, the MLP shard forward, its emulated all-reduce, the
+MLP shard backward and its emulated all-reduce, plus the host-side
+all-reduce accounting.  Inputs are seeded synthetic tensors already resident
+in HBM when timing starts.
+
+The reported metric is the per-rank MLP forward+backward throughput
+(algorithmic FLOPs 18*T*h*f for SwiGLU, 12*T*h*f for GeLU, over the measured
+time of the MLP shard's forward and backward calls) and its fraction of the
+MI355X bf16 dense matrix-core peak; every kernel's time, the emulated
+all-reduces' HBM bandwidth and the attention shard are reported beside it.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg5|cfg3|cfg2] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak (published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E bandwidth (published)
+METRIC = "per-rank TP MLP fwd+bwd TFLOP/s and % of bf16 MFMA peak on 1 MI355X"
+
+WORKLOADS = {
+    # name: (mlp config id, attention config id or None)
+    "cfg5": (5, 5),
+    "cfg3": (3, 4),
+    "cfg2": (2, None),
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "attention_column_gemm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """Raw hipEvent_t handles for the library's per-kernel profiling hook."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            evs.append(e)
+        return evs
+
+    def elapsed_ms(self, a, b) -> float:
+        f = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(f), a, b)
+        assert rc == 0, f"hipEventElapsedTime failed ({rc})"
+        return f.value
+
+
+def kernel_plan(mc, ac):
+    """Kernels one step enqueues, in order: (label, row, flops, bytes)."""
+    T, h, f = mc.tokens, mc.h, mc.f
+    d = 2 if mc.bf16 else 4
+    plan = []
+    if ac is not None:
+        Ta, ha, q, kv, dh = ac.tokens, ac.h, ac.q, ac.kv, ac.d
+        plan += [("attn_qkv_gemm", "a8", 2 * Ta * ha * (q + 2 * kv) * dh, None),
+                 ("attn_core", "a8", 4 * dh * ac.b * q * (ac.s * (ac.s + 1) // 2), None),
+                 ("attn_out_gemm", "a8", 2 * Ta * q * dh * ha, None),
+                 ("allreduce_attn_sum", "a3", None, (ac.t + 1) * Ta * ha * 2)]
+    n1 = 1 if mc.act == "gelu" else 2
+    plan += [("mlp_fwd_col_gemm_act", "a1", 2 * T * h * f * n1, None),
+             ("mlp_fwd_row_gemm", "a2", 2 * T * f * h, None),
+             ("allreduce_fwd_sum", "a3", None, (mc.t + 1) * T * h * d + (h * d if mc.bias else 0))]
+    if mc.p_drop > 0:
+        plan.append(("mlp_bwd_dropout", "a4", None, 2 * T * h * d))
+    if mc.bias:
+        plan.append(("mlp_bwd_db2_colsum", "a4", None, T * h * d + 4 * h))
+    plan.append(("mlp_bwd_dH_gemm_act", "a5", 2 * T * h * f, None))
+    if mc.bias and mc.act == "gelu":
+        plan.append(("mlp_bwd_db1_colsum", "a5", None, T * f * d + 4 * f))
+    plan += [("mlp_bwd_dW2_gemm", "a5", 2 * T * f * h, None),
+             ("mlp_bwd_dW1_gemm", "a6", 2 * T * h * f * n1, None),
+             ("mlp_bwd_dX_gemm", "a6", 2 * T * f * h * n1, None),
+             ("allreduce_bwd_sum", "a7", None, (mc.t + 1) * T * h * d)]
+    return plan
+
+
+def cpu_baseline(mc, X, dOut, w, budget_s=12.0):
+    """The float64 oracle on a bounded token slice of the same rank-0 shard."""
+    import numpy as np
+    from oracle import mlp as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    W = {k: (None if v is None else np.asarray(v, dtype=np.float64)) for k, v in w.items()}
+    n, elapsed = 16, 0.0
+    while True:
+        t0 = time.perf_counter()
+        O.shard_step(dOut[:n], X[:n], W["W1"], W["W2"], act=mc.act, Wu_i=W["Wu"], b1_i=W["b1"], p=mc.p_drop,
+                     seed=mc.seed, rows=np.arange(n))
+        elapsed = time.perf_counter() - t0
+        if elapsed * 2 > budget_s or n * 2 > mc.tokens:
+            break
+        n *= 2
+    k = 12 if mc.act == "gelu" else 18
+    flops = k * n * mc.h * mc.f
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"rank-0 MLP shard fwd+bwd of workload {mc.cfg} on its first {n} of {mc.tokens} tokens "
+                      f"(all weights; {flops / 1e9:.1f} GFLOP in float64 numpy/BLAS, {elapsed:.1f} s)"}
+
+
+def load_traffic(kernel_label):
+    """HBM bytes per launch from the rocprofv3 PMC summary, if taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    ent = rec.get("kernels", {}).get(kernel_label)
+    return None if ent is None else ent.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="cfg5", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one rank's shard on ONE GPU; --gpus {args.gpus} is not supported "
+              "(the all-reduce is emulated on one device; multi-GPU runs are out of scope).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from attention_column_gemm_amd import binding as B
+    from attention_column_gemm_amd import inputs as I
+    from attention_column_gemm_amd.shard import AttnShard, MLPShard, sum_partials, to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    mcid, acid = WORKLOADS[args.workload]
+    mc = I.MLP_CONFIGS[mcid]
+    ac = I.ATTN_CONFIGS[acid] if acid is not None else None
+
+    log(f"[bench] workload {args.workload}: generating inputs")
+    X, dOut = I.mlp_activation(mc)
+    w = I.mlp_rank_weights(mc, 0)
+    mlp = MLPShard(mc.tokens, mc.h, mc.h_ffn, mc.t, 0, act=mc.act, dtype=mc.dtype)
+    mlp.load(X, w["W1"], w["Wu"], w["b1"], w["W2"], dOut)
+    b2 = to_device(w["b2"], mc.dtype)
+    attn = None
+    if ac is not None:
+        Xa = I.attn_activation(ac)
+        wa = I.attn_rank_weights(ac, 0)
+        attn = AttnShard(ac.b, ac.s, ac.h, ac.n_q, ac.n_kv, ac.d, ac.t, 0).load(Xa, wa["Wqkv"], wa["Wo"])
+        del Xa
+
+    # Rank 0's own partials come from its kernels each step; the other t-1
+    # ranks' partials are stand-ins holding rank 0's values (the reduction's
+    # cost does not depend on the values it reads).
+    def others(ref, t):
+        return [ref.clone() for _ in range(t - 1)]
+
+    mlp.forward()
+    mlp.backward(mc.p_drop, mc.seed, want_db2=mc.bias, want_db1=mc.bias)
+    z_others, dx_others = others(mlp.Z, mc.t), others(mlp.dX, mc.t)
+    out = torch.empty_like(mlp.Z)
+    dxsum = torch.empty_like(mlp.dX)
+    if attn is not None:
+        attn.forward(want_lse=False)
+        za_others = others(attn.Z, ac.t)
+        zasum = torch.empty_like(attn.Z)
+    torch.cuda.synchronize()
+
+    plan = kernel_plan(mc, ac)
+    nk = len(plan)
+    hip = HipEvents()
+    stream = torch.cuda.current_stream()
+    comm = B.tp_comm_bytes(mc.tokens, mc.h, mc.t, 2 if mc.bf16 else 4)
+
+    def step(kev=None):
+        if kev is not None:
+            arr = (ctypes.c_void_p * (2 * nk))(*[e.value for e in kev])
+            rc = B.lib().tp_profile_arm(arr, 2 * nk)
+            assert rc == 0
+        marks = []
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+        if attn is not None:
+            e0 = ev(); e0.record()
+            attn.forward(want_lse=False)
+            sum_partials([attn.Z] + za_others, None, 0.0, 0, out=zasum)
+            e1 = ev(); e1.record()
+            marks.append(("attention_fwd_and_allreduce", e0, e1))
+        e0 = ev(); e0.record()
+        mlp.forward()
+        e1 = ev(); e1.record()
+        sum_partials([mlp.Z] + z_others, b2, mc.p_drop, mc.seed, out=out)
+        e2 = ev(); e2.record()
+        mlp.backward(mc.p_drop, mc.seed, want_db2=mc.bias, want_db1=mc.bias)
+        e3 = ev(); e3.record()
+        sum_partials([mlp.dX] + dx_others, None, 0.0, 0, out=dxsum)
+        e4 = ev(); e4.record()
+        B.tp_comm_bytes(mc.tokens, mc.h, mc.t, 2 if mc.bf16 else 4)   # a9: host-only accounting
+        marks += [("mlp_fwd", e0, e1), ("mlp_bwd", e2, e3), ("allreduce_fwd", e1, e2), ("allreduce_bwd", e3, e4)]
+        return marks
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    kevs = [hip.create(2 * nk) for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    all_marks = [step(kevs[i]) for i in range(args.steps)]
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    kern_ms = np.zeros(nk)
+    for kev in kevs:
+        for i in range(nk):
+            kern_ms[i] += hip.elapsed_ms(kev[2 * i], kev[2 * i + 1])
+    kern_ms /= args.steps
+    span = {}
+    for marks in all_marks:
+        for name, a, b in marks:
+            span[name] = span.get(name, 0.0) + a.elapsed_time(b)
+    span = {k: v / args.steps for k, v in span.items()}
+
+    mlp_flops = mc.flops_per_rank()
+    mlp_ms = span["mlp_fwd"] + span["mlp_bwd"]
+    value = mlp_flops / (mlp_ms * 1e-3) / 1e12
+
+    kernels = []
+    for (label, row, flops, nbytes), ms in zip(plan, kern_ms):
+        k = {"kernel": label, "row": row, "avg_ms": round(ms, 5)}
+        if flops:
+            k["tflops"] = round(flops / (ms * 1e-3) / 1e12, 2)
+            k["frac_bf16_peak"] = round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        if nbytes:
+            k["gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+            k["frac_hbm_peak"] = round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        kernels.append(k)
+    # dominant kernel: the longest one
+    di = int(np.argmax(kern_ms))
+    dl, _, dflops, dbytes = plan[di]
+    if dflops:
+        ach = dflops / (kern_ms[di] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dl, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "flops_per_launch": dflops,
+                "avg_ms": round(float(kern_ms[di]), 5), "traffic": load_traffic(dl)}
+    else:
+        ach = dbytes / (kern_ms[di] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": dl, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "bytes_per_launch": dbytes,
+                "avg_ms": round(float(kern_ms[di]), 5), "traffic": load_traffic(dl)}
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if mc.bf16 else "f32",
+        "data": "synthetic",
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {
+            "workload": {"cfg5": "full per-rank layer shard (attention fwd + SwiGLU MLP fwd+bwd), rank 0 of t=8",
+                         "cfg3": "Llama SwiGLU MLP shard fwd+bwd + GQA attention shard fwd, rank 0 of t=8",
+                         "cfg2": "GPT GeLU MLP shard fwd+bwd with dropout 0.1, rank 0 of t=4"}[args.workload],
+            "tokens": mc.tokens, "b": mc.b, "s": mc.s, "h": mc.h, "h_ffn": mc.h_ffn, "t": mc.t, "f": mc.f,
+            "act": mc.act, "p_drop": mc.p_drop, "bias": mc.bias,
+            **({"attn": {"b": ac.b, "s": ac.s, "h": ac.h, "n_q": ac.n_q, "n_kv": ac.n_kv, "d": ac.d, "t": ac.t}}
+               if ac is not None else {}),
+        },
+        "mlp_ms_per_step": round(mlp_ms, 4),
+        "mlp_flops_per_step": mlp_flops,
+        "spans_ms": {k: round(v, 4) for k, v in span.items()},
+        "kernels": kernels,
+        "roofline": roof,
+        "comm": {"n_allreduce_per_layer": comm.n_allreduce_fwd + comm.n_allreduce_bwd,
+                 "payload_bytes": comm.payload_bytes, "ring_bytes_per_rank": comm.ring_bytes_per_rank},
+        "wall_s_timed": round(wall, 3),
+        "source_hash": source_hash(),
+    }
+    if attn is not None:
+        af = I.ATTN_CONFIGS[acid].flops_per_rank()
+        res["attention_fwd_tflops"] = round(af / (span["attention_fwd_and_allreduce"] * 1e-3) / 1e12, 2)
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        res["cpu_baseline"] = cpu_baseline(mc, X, dOut, w)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,222 @@
+/*
+ * tp_shard.h -- C ABI of libtpshard: one tensor-parallel (TP) rank's share of a
+ * Megatron-style Transformer layer on an AMD MI355X (gfx950).
+ *
+ * Pages this interface follows (cited by title and section):
+ *   [L11] grasp.study Lesson 11, "张量并行线性层分片与前反向通信量计算"
+ *         (tensor-parallel linear sharding and fwd/bwd communication volume)
+ *   [LP]  cnblogs "ラブパラ" (survey of parallelisms)
+ *   [HJ]  hjcheng0602.cn "tensorparallel/tp"
+ *   [TP1] "Tensor Parallelism张量并行（一）"
+ *
+ * Notation ([L11] section 1; [LP] O.I): T = b*s tokens of a microbatch, hidden
+ * size h, MLP intermediate size h_ffn, TP degree t, bytes per element delta;
+ * per-rank intermediate width f = h_ffn / t; q = n_q / t local query heads and
+ * kv = n_kv / t local KV heads of width d.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense and row-major; tokens are rows (row r = beta*s + sigma).
+ *    Weights are stored [in, out] so the layer computes X W (the semantic
+ *    orientation of [L11] section 1).
+ *  - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
+ *    aligned.  A tensor with no elements may be passed as NULL.  The library
+ *    never allocates, frees or keeps device memory, and holds no state
+ *    between calls other than the profiling hook of tp_profile_arm.
+ *    Outputs may not alias inputs.
+ *  - Storage type: TP_F32 means every activation, weight and bias is fp32;
+ *    TP_BF16 means they are bf16 (products accumulate in fp32).  Weight and
+ *    bias gradients (dW*, db*) are always fp32.
+ *  - For TP_BF16 the sizes h, f, (q + 2 kv) d and q d must be multiples of 8;
+ *    for TP_F32 multiples of 4 (vector width of 16 bytes).
+ *  - Every launch is asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL is the default stream).  Arguments are validated before any launch:
+ *    on a negative return nothing was enqueued.  Nothing is printed and no
+ *    C++ exception crosses the ABI.
+ *  - Calls on one stream run in order; the library adds no synchronisation.
+ */
+#ifndef TP_SHARD_H
+#define TP_SHARD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element storage type of activations and weights (delta = 4 or 2 bytes). */
+typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+/* MLP activation: exact-erf GeLU on (X W1 + b1), or SwiGLU SiLU(X Wg) * (X Wu). */
+typedef enum { TP_GELU = 0, TP_SWIGLU = 1 } tp_act;
+
+/* Status codes. */
+enum {
+  TP_OK = 0,
+  TP_EINVAL = -1,       /* NULL for a required non-empty tensor, size < 0, t < 1, rank >= t, p outside [0,1) */
+  TP_ENOTDIV = -2,      /* h_ffn % t, n_q % t, n_kv % t or n_q % n_kv is not 0 */
+  TP_EDTYPE = -3,       /* unknown dtype/activation, or a combination not provided (attention in fp32) */
+  TP_EALIGN = -4,       /* a pointer is not 16-byte aligned or a width is not a multiple of the vector width */
+  TP_EHIP = -5,         /* the HIP runtime reported an error when enqueuing a kernel */
+  TP_EUNSUPPORTED = -6  /* a size the kernels do not implement (head width other than 64 or 128, t > 64) */
+};
+
+/* One rank's MLP shard. */
+typedef struct {
+  int64_t tokens;   /* T = b*s */
+  int64_t h;        /* hidden size */
+  int64_t h_ffn;    /* full intermediate size; this rank holds f = h_ffn / t columns */
+  int32_t t;        /* TP degree (1 = unsharded layer) */
+  int32_t rank;     /* which slice this shard is, 0 <= rank < t (informational for the MLP) */
+  int32_t dtype;    /* tp_dtype */
+  int32_t act;      /* tp_act */
+} tp_mlp_desc;
+
+/* One rank's attention shard (forward). */
+typedef struct {
+  int64_t b, s, h;  /* sequences, sequence length, hidden size; T = b*s */
+  int32_t n_q;      /* query heads of the whole layer */
+  int32_t n_kv;     /* key/value heads of the whole layer (GQA when < n_q) */
+  int32_t d;        /* head width */
+  int32_t t;        /* TP degree */
+  int32_t rank;     /* 0 <= rank < t */
+  int32_t dtype;    /* tp_dtype; only TP_BF16 is provided */
+  int32_t causal;   /* 1: key position <= query position; 0: full attention */
+} tp_attn_desc;
+
+/* All-reduce accounting of one layer ([L11] section 5; [TP1] communication cost). */
+typedef struct {
+  int32_t n_allreduce_fwd;            /* 2: after the attention and the MLP output projections */
+  int32_t n_allreduce_bwd;            /* 2: at the MLP and the attention inputs */
+  uint64_t payload_bytes;             /* logical size of one all-reduce: tokens*h*delta */
+  double ring_bytes_per_rank;         /* bytes one rank sends in a ring all-reduce: 2(t-1)/t * payload */
+  uint64_t layer_payload_bytes;       /* 4 * payload_bytes */
+  double layer_ring_bytes_per_rank;   /* 4 * ring_bytes_per_rank */
+} tp_comm;
+
+/*
+ * tp_mlp_shard_fwd -- forward of one rank's MLP shard
+ * ([L11] sections 2-3; [TP1] column split and "MLP and attention"; [HJ] TP forward).
+ *
+ * Column-parallel GEMM with the activation fused in its epilogue, then the
+ * row-parallel GEMM that yields the partial Z_i (output bias NOT added: it is
+ * added once after the sum, see tp_sum_partials).
+ *   GeLU:   A_i = X W1_i + b1_i;  H_i = GeLU(A_i)
+ *   SwiGLU: G_i = X W1_i;  U_i = X Wu_i;  H_i = SiLU(G_i) * U_i
+ *   Z_i = H_i W2_i
+ * Arguments (T = tokens, f = h_ffn / t):
+ *   X     [T, h]   replicated input
+ *   W1_i  [h, f]   first-layer columns of this rank (the gate for SwiGLU)
+ *   Wu_i  [h, f]   SwiGLU up-projection columns; must be NULL for GeLU
+ *   b1_i  [f]      GeLU first-layer bias slice, or NULL; must be NULL for SwiGLU
+ *   W2_i  [f, h]   second-layer rows of this rank
+ *   saved_i        out: GeLU A_i [T, f]; SwiGLU G_i then U_i, two [T, f] blocks
+ *   H_i   [T, f]   out: activation
+ *   Z_i   [T, h]   out: partial output of this rank
+ */
+int tp_mlp_shard_fwd(const tp_mlp_desc* desc, const void* X, const void* W1_i, const void* Wu_i,
+                     const void* b1_i, const void* W2_i, void* saved_i, void* H_i, void* Z_i,
+                     void* stream);
+
+/*
+ * tp_mlp_shard_bwd -- backward of one rank's MLP shard
+ * ([L11] sections 2-3; [TP1] operator f; [HJ] single-card and TP backward).
+ *
+ *   dY    = dOut * keep / (1 - p)          (dropout backward; keep as in tp_sum_partials)
+ *   db2   = sum over tokens of dY          (output-bias gradient; replicated)
+ *   dW2_i = H_i^T dY;  dH_i = dY W2_i^T
+ *   GeLU:   dA_i = dH_i * GeLU'(A_i);  db1_i = sum over tokens of dA_i
+ *           dW1_i = X^T dA_i;  dX_i = dA_i W1_i^T
+ *   SwiGLU: dU_i = dH_i * SiLU(G_i);  dG_i = dH_i * U_i * SiLU'(G_i)
+ *           dWg_i = X^T dG_i;  dWu_i = X^T dU_i;  dX_i = dG_i Wg_i^T + dU_i Wu_i^T
+ * dX_i is this rank's partial input gradient; the backward all-reduce
+ * (tp_sum_partials with no bias and p = 0) sums it over ranks.
+ * Arguments:
+ *   dOut  [T, h]        gradient of the layer output (replicated)
+ *   p_drop, seed        the forward's dropout probability and seed
+ *   X, W1_i, Wu_i, W2_i as in tp_mlp_shard_fwd (Wu_i NULL for GeLU)
+ *   saved_i, H_i        as written by tp_mlp_shard_fwd
+ *   dY    [T, h]        out, act dtype.  May be NULL when p_drop == 0; dOut is then used as dY.
+ *   db2   [h] fp32      out, or NULL to skip
+ *   dA_i                out, act dtype: GeLU dA_i [T, f]; SwiGLU dG_i then dU_i, two [T, f] blocks
+ *   dW1_i fp32          out: GeLU dW1_i [h, f]; SwiGLU dWg_i then dWu_i, two [h, f] blocks
+ *   db1_i [f] fp32      out for GeLU, or NULL to skip; must be NULL for SwiGLU
+ *   dW2_i [f, h] fp32   out
+ *   dX_i  [T, h]        out, act dtype: partial input gradient
+ */
+int tp_mlp_shard_bwd(const tp_mlp_desc* desc, const void* dOut, float p_drop, uint64_t seed,
+                     const void* X, const void* W1_i, const void* Wu_i, const void* W2_i,
+                     const void* saved_i, const void* H_i, void* dY, float* db2, void* dA_i,
+                     float* dW1_i, float* db1_i, float* dW2_i, void* dX_i, void* stream);
+
+/*
+ * tp_attn_shard_fwd -- forward of one rank's attention shard
+ * ([L11] section 4; [LP] I.III; [HJ] Attention, single-card forward).
+ *
+ *   QKV_i = X Wqkv_i, columns [Q heads (q*d) | K heads (kv*d) | V heads (kv*d)], head-major
+ *   per sequence and local query head j (KV head j / (q/kv)):
+ *     O = softmax(Q K^T / sqrt(d) + mask) V, mask = -inf where key > query (causal)
+ *   Z_i = O_i Wo_i   (partial; summed over ranks by tp_sum_partials)
+ * Arguments:
+ *   X      [T, h]              replicated input, bf16
+ *   Wqkv_i [h, (q+2kv) d]      this rank's QKV column shard, bf16
+ *   Wo_i   [q d, h]            this rank's output-projection rows, bf16
+ *   QKV_i  [T, (q+2kv) d]      out, bf16 (also the attention's input)
+ *   O_i    [T, q d]            out, bf16, heads concatenated head-major
+ *   lse_i  [b, q, s] fp32      out, natural-log sum of exp of the scaled masked scores per row, or NULL
+ *   Z_i    [T, h]              out, bf16 partial
+ * Head widths 64 and 128 are provided.
+ */
+int tp_attn_shard_fwd(const tp_attn_desc* desc, const void* X, const void* Wqkv_i, const void* Wo_i,
+                      void* QKV_i, void* O_i, float* lse_i, void* Z_i, void* stream);
+
+/*
+ * tp_sum_partials -- the all-reduce of operators g/f, emulated on one device
+ * ([TP1] operators f and g; [L11] section 3 on the bias; [LP] I.III and [HJ] on dropout).
+ *
+ *   out = Dropout_{p, seed}( sum_{i=0}^{t-1} partials[i] + bias )
+ * The sum runs in rank order in fp32; the bias is added exactly once after it.
+ * Dropout keeps element (r, c) iff u >= floor(p * 2^32), where u is the high
+ * 32 bits of output number (r*cols + c + 1) of a SplitMix64 stream seeded with
+ * `seed` (Steele, Lea & Flood, OOPSLA 2014); kept elements are scaled by
+ * 1/(1-p) in fp32.  The mask depends on neither t nor the tiling.
+ * Arguments:
+ *   rows, cols   tensor shape ([T, h] for the layer's all-reduces)
+ *   t            number of partials, 1 <= t <= 64
+ *   dtype        storage type of partials, bias and out
+ *   partials     HOST array of t device pointers, each [rows, cols]
+ *   bias         [cols] or NULL
+ *   p_drop, seed dropout; p_drop = 0 disables it
+ *   out          [rows, cols]; may alias none of the partials
+ */
+int tp_sum_partials(int64_t rows, int64_t cols, int32_t t, int32_t dtype, const void* const* partials,
+                    const void* bias, float p_drop, uint64_t seed, void* out, void* stream);
+
+/*
+ * tp_comm_bytes -- host-only all-reduce accounting of one layer per microbatch
+ * ([L11] section 5; [TP1] communication cost; [LP] II.II).  4 all-reduces
+ * per layer (2 forward, 2 backward) of tokens*h*delta bytes each; a ring
+ * all-reduce sends 2(t-1)/t of that per rank.  Touches no device.
+ * Returns TP_EINVAL for tokens < 0, h < 0, t < 1, delta < 1 or out == NULL.
+ */
+int tp_comm_bytes(int64_t tokens, int64_t h, int32_t t, int32_t delta, tp_comm* out);
+
+/*
+ * tp_profile_arm -- profiling aid: bracket the library's next kernels with events.
+ * `events` is a host array of n_events hipEvent_t handles (as void*), n_events
+ * even and at most 64.  Each of the next n_events/2 kernels the library
+ * enqueues records events[2i] just before and events[2i+1] just after kernel i,
+ * on that kernel's stream; after that the hook is idle again.  n_events = 0
+ * disarms it.  Process-wide and not thread-safe (one profiling client).
+ * Returns TP_EINVAL for an odd or out-of-range count or a NULL handle.
+ */
+int tp_profile_arm(void* const* events, int32_t n_events);
+
+/* Human-readable name of a status code (static string; never NULL). */
+const char* tp_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_SHARD_H */

@@ -1,0 +1,143 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, its host-only accounting agrees with the oracle, and
+invalid arguments are rejected before anything is launched."""
+import ctypes
+
+import pytest
+
+from attention_column_gemm_amd import binding as B
+from oracle import comm
+
+
+def test_library_exports_every_declared_function():
+    names = B.declared_functions()
+    assert set(names) >= {"tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_attn_shard_fwd", "tp_sum_partials",
+                          "tp_comm_bytes", "tp_status_string"}
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+@pytest.mark.parametrize("tokens,h,t,delta", [
+    (64, 128, 2, 4), (2048, 1024, 4, 2), (4096, 4096, 8, 2), (8192, 8192, 8, 2), (7, 9, 1, 2), (0, 16, 3, 2)])
+def test_comm_bytes_matches_oracle(tokens, h, t, delta):
+    got = B.tp_comm_bytes(tokens, h, t, delta)
+    ref = comm.comm_bytes(tokens, h, t, delta)
+    assert got.n_allreduce_fwd == ref["n_allreduce_fwd"] and got.n_allreduce_bwd == ref["n_allreduce_bwd"]
+    assert got.payload_bytes == ref["payload_bytes"]
+    assert got.layer_payload_bytes == ref["layer_payload_bytes"]
+    assert got.ring_bytes_per_rank == pytest.approx(ref["ring_bytes_per_rank"], rel=1e-15)
+    assert got.layer_ring_bytes_per_rank == pytest.approx(ref["layer_ring_bytes_per_rank"], rel=1e-15)
+
+
+def test_comm_bytes_rejects_bad_arguments():
+    for args in [(-1, 4, 2, 2), (4, -1, 2, 2), (4, 4, 0, 2), (4, 4, 2, 0)]:
+        with pytest.raises(B.TPError) as e:
+            B.tp_comm_bytes(*args)
+        assert e.value.status == B.TP_EINVAL
+    assert B.lib().tp_comm_bytes(1, 1, 1, 1, None) == B.TP_EINVAL
+
+
+# Fake, never-dereferenced device addresses: every case below fails validation
+# before any launch, so nothing touches them.
+A16 = 0x10000          # 16-byte aligned
+MIS = 0x10002          # misaligned
+
+
+def _mlp(**kw):
+    d = dict(tokens=64, h=128, h_ffn=512, t=2, rank=0, dtype=B.TP_BF16, act=B.TP_GELU)
+    d.update(kw)
+    return B.tp_mlp_desc(d["tokens"], d["h"], d["h_ffn"], d["t"], d["rank"], d["dtype"], d["act"])
+
+
+def _fwd(desc, **ptrs):
+    p = dict(X=A16, W1=A16, Wu=None, b1=None, W2=A16, saved=A16, H=A16, Z=A16)
+    p.update(ptrs)
+    return B.lib().tp_mlp_shard_fwd(ctypes.byref(desc) if desc is not None else None, p["X"], p["W1"], p["Wu"],
+                                    p["b1"], p["W2"], p["saved"], p["H"], p["Z"], None)
+
+
+@pytest.mark.parametrize("desc,ptrs,code", [
+    (None, {}, B.TP_EINVAL),
+    (_mlp(dtype=7), {}, B.TP_EDTYPE),
+    (_mlp(act=5), {}, B.TP_EDTYPE),
+    (_mlp(rank=2), {}, B.TP_EINVAL),
+    (_mlp(t=0), {}, B.TP_EINVAL),
+    (_mlp(tokens=-1), {}, B.TP_EINVAL),
+    (_mlp(h_ffn=513), {}, B.TP_ENOTDIV),
+    (_mlp(h=100), {}, B.TP_EALIGN),
+    (_mlp(h_ffn=2 * 12), {}, B.TP_EALIGN),
+    (_mlp(), {"X": None}, B.TP_EINVAL),
+    (_mlp(), {"Wu": A16}, B.TP_EINVAL),
+    (_mlp(act=B.TP_SWIGLU), {"Wu": None}, B.TP_EINVAL),
+    (_mlp(act=B.TP_SWIGLU), {"Wu": A16, "b1": A16}, B.TP_EINVAL),
+    (_mlp(), {"W2": MIS}, B.TP_EALIGN),
+    (_mlp(dtype=B.TP_F32, h=130), {}, B.TP_EALIGN),
+])
+def test_mlp_fwd_validation(desc, ptrs, code):
+    assert _fwd(desc, **ptrs) == code
+
+
+def test_mlp_bwd_validation():
+    L = B.lib()
+    d = _mlp()
+    base = [A16, 0.0, 1, A16, A16, None, A16, A16, A16, None, None, A16, A16, None, A16, A16]
+
+    def call(*over):
+        a = list(base)
+        for i, v in over:
+            a[i] = v
+        return L.tp_mlp_shard_bwd(ctypes.byref(d), *a, None)
+
+    assert call((1, 1.0)) == B.TP_EINVAL             # p = 1
+    assert call((1, -0.1)) == B.TP_EINVAL            # p < 0
+    assert call((1, float("nan"))) == B.TP_EINVAL
+    assert call((1, 0.1)) == B.TP_EINVAL             # p > 0 needs dY
+    assert call((0, None)) == B.TP_EINVAL            # dOut missing
+    assert call((15, MIS)) == B.TP_EALIGN            # dX misaligned
+    dsw = _mlp(act=B.TP_SWIGLU)
+    a = list(base)
+    a[5] = A16        # Wu
+    a[13] = A16       # db1 for SwiGLU: not allowed
+    assert L.tp_mlp_shard_bwd(ctypes.byref(dsw), *a, None) == B.TP_EINVAL
+
+
+def test_attention_validation():
+    L = B.lib()
+
+    def call(**kw):
+        d = dict(b=2, s=64, h=256, n_q=8, n_kv=2, d=128, t=2, rank=0, dtype=B.TP_BF16, causal=1)
+        d.update(kw)
+        desc = B.tp_attn_desc(**d)
+        return L.tp_attn_shard_fwd(ctypes.byref(desc), A16, A16, A16, A16, A16, None, A16, None)
+
+    assert call(dtype=B.TP_F32) == B.TP_EDTYPE
+    assert call(n_q=9) == B.TP_ENOTDIV
+    assert call(n_kv=3) == B.TP_ENOTDIV
+    assert call(d=96) == B.TP_EUNSUPPORTED
+    assert call(rank=2) == B.TP_EINVAL
+    assert call(h=100) == B.TP_EALIGN
+    assert L.tp_attn_shard_fwd(None, A16, A16, A16, A16, A16, None, A16, None) == B.TP_EINVAL
+
+
+def test_sum_partials_validation():
+    L = B.lib()
+    arr = (ctypes.c_void_p * 2)(A16, A16)
+    f = L.tp_sum_partials
+    assert f(4, 8, 2, 9, arr, None, 0.0, 0, A16, None) == B.TP_EDTYPE
+    assert f(4, 8, 0, B.TP_BF16, arr, None, 0.0, 0, A16, None) == B.TP_EINVAL
+    assert f(4, 8, 65, B.TP_BF16, arr, None, 0.0, 0, A16, None) == B.TP_EUNSUPPORTED
+    assert f(4, 12, 2, B.TP_BF16, arr, None, 0.0, 0, A16, None) == B.TP_EALIGN
+    assert f(4, 8, 2, B.TP_BF16, arr, None, 1.5, 0, A16, None) == B.TP_EINVAL
+    assert f(4, 8, 2, B.TP_BF16, arr, MIS, 0.0, 0, A16, None) == B.TP_EALIGN
+    bad = (ctypes.c_void_p * 2)(A16, None)
+    assert f(4, 8, 2, B.TP_BF16, bad, None, 0.0, 0, A16, None) == B.TP_EINVAL
+    # empty tensors need no storage and launch nothing
+    empty = (ctypes.c_void_p * 2)(None, None)
+    assert f(0, 8, 2, B.TP_BF16, empty, None, 0.0, 0, None, None) == B.TP_OK
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert B.status_string(code).startswith("TP_")
+    assert B.status_string(-99) == "unknown status"
