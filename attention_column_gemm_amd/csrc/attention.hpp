@@ -50,7 +50,9 @@ __device__ __forceinline__ int k_off(int row, int chunk) {  // K tile [64][D], D
   return row * D + ((chunk ^ (row & 7)) << 3);
 }
 __device__ __forceinline__ int vt_off(int row, int chunk) {  // V^T tile [D][64], 8 chunks per row
-  return row * BKV + ((chunk ^ (row & 7)) << 3);
+  // rows are written 8 apart by the transposing loader and read 8 consecutive
+  // at a time, so the swizzle mixes bits 0-2 and 3-5 of the row
+  return row * BKV + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 3);
 }
 
 template <int D>
@@ -92,8 +94,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnArgs a) {
 
   const int kv_end = a.causal ? min(a.s, pos0 + rows_per_wg) : a.s;
   const int nkb = (kv_end + BKV - 1) / BKV;
-  const uint16_t* kbase = a.qkv + tok0 * a.ld_qkv + (int64_t)(a.q + g) * D;
-  const uint16_t* vbase = a.qkv + tok0 * a.ld_qkv + (int64_t)(a.q + a.kv + g) * D;
+  // this sequence's rows of QKV behind a buffer resource (zeros past its end)
+  const uint32_t ldb = (uint32_t)a.ld_qkv * 2u;
+  const rsrc_t seq = make_rsrc(a.qkv + tok0 * a.ld_qkv, (uint32_t)a.s * ldb);
+  const uint32_t kcol = (uint32_t)(a.q + g) * D * 2u, vcol = (uint32_t)(a.q + a.kv + g) * D * 2u;
 
   u32x4 kreg[KPER];
   u32x4 vreg[8];
@@ -103,16 +107,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnArgs a) {
     for (int i = 0; i < KPER; ++i) {
       const int c = tid + NTHREADS * i;
       const int row = c / KCH, ch = c % KCH;
-      kreg[i] = u32x4{0, 0, 0, 0};
-      if (key0 + row < a.s) kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(key0 + row) * a.ld_qkv + ch * 8);
+      kreg[i] = buf_load16(seq, key0 + row < a.s ? (uint32_t)(key0 + row) * ldb + kcol + ch * 16u : kOOB);
     }
     if (tid < D) {  // D blocks of 8 keys x 8 dims
       const int dg = tid % KCH, kg = tid / KCH;
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int key = key0 + kg * 8 + r;
-        vreg[r] = u32x4{0, 0, 0, 0};
-        if (key < a.s) vreg[r] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * a.ld_qkv + dg * 8);
+        vreg[r] = buf_load16(seq, key < a.s ? (uint32_t)key * ldb + vcol + dg * 16u : kOOB);
       }
     }
   };

@@ -12,6 +12,22 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// ---- buffer loads ----------------------------------------------------------
+// Raw buffer loads through a buffer resource descriptor: the hardware returns
+// zeros for any byte offset at or beyond the descriptor's size, so ragged
+// tile edges are handled by pointing invalid lanes at kOOB instead of
+// branching around the load.  Operands handed to these loads are < 2 GiB.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+  // dword 3 = 0x00020000: 32-bit data format, the raw-buffer setting on gfx9 parts
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
 // bf16 is carried as its raw 16 bits (uint16_t) in memory.
 __device__ __forceinline__ float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -10,8 +10,11 @@
 //    K step 64; each wave owns a (BM/2) x (BN/2) sub-tile built from 32x32x16
 //    bf16 MFMAs (v_mfma_f32_32x32x16_bf16).
 //  * Both operands are staged through LDS as [rows][64] bf16 with K
-//    contiguous; the 16-byte chunk c of row r lives at chunk c ^ (r & 7) so the
-//    128-bit fragment reads of 8 consecutive rows hit distinct banks.
+//    contiguous; the 16-byte chunks of a row are XOR-swizzled by the row index
+//    so that the 128-bit fragment reads and the transposed block writes hit
+//    distinct banks.
+//  * Global reads are raw buffer loads: lanes past a ragged tile edge point
+//    their offset past the buffer's end and receive zeros, with no branches.
 //    Operands whose K is the slow dimension in HBM (A stored [K,M] or B stored
 //    [K,N]) are loaded as 8x8 bf16 blocks with 16-byte row reads and
 //    transposed in registers before the LDS write, so every layout feeds the
@@ -55,8 +58,31 @@ constexpr int BK = 64;
 constexpr int NTHREADS = 256;
 constexpr int GROUP_M = 4;
 
-// Element offset of 16-byte chunk `chunk` of LDS tile row `row`.
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
+// Element offset of 16-byte chunk `chunk` of LDS tile row `row`.  The chunk is
+// XOR-swizzled with bits 0-2 and 3-5 of the row, so that any 8 consecutive
+// rows (fragment reads) and any 8 rows spaced by 8 (transposed block writes)
+// hit 8 different chunks.
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * BK + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 3);
+}
+
+// One operand of one K segment: a row-major matrix behind a buffer resource.
+struct Operand {
+  rsrc_t rsrc;
+  uint32_t ld_bytes;  // leading dimension in bytes
+  int rows;           // extent of the M (or N) dimension
+  int K;              // extent of the K dimension
+};
+
+__device__ __forceinline__ Operand make_operand(const uint16_t* p, int64_t ld, int rows, int K, int layout) {
+  Operand o;
+  const uint32_t slow = layout == KMAJOR ? (uint32_t)rows : (uint32_t)K;
+  o.rsrc = make_rsrc(p, slow * (uint32_t)ld * 2u);
+  o.ld_bytes = (uint32_t)ld * 2u;
+  o.rows = rows;
+  o.K = K;
+  return o;
+}
 
 template <int ROWS, int LAYOUT>
 struct TileLoader;
@@ -66,16 +92,14 @@ template <int ROWS>
 struct TileLoader<ROWS, KMAJOR> {
   static constexpr int PER = ROWS * (BK / 8) / NTHREADS;
   u32x4 r[PER];
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ g, int64_t ld, int row0, int nrows, int k0, int K) {
+  __device__ __forceinline__ void load(const Operand& op, int row0, int k0) {
     const int tid = threadIdx.x, kc = tid & 7;
-    const int k = k0 + kc * 8;
+    const bool kok = k0 + kc * 8 < op.K;
+    const uint32_t base = (uint32_t)(row0 + (tid >> 3)) * op.ld_bytes + (uint32_t)(k0 + kc * 8) * 2u;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int gr = row0 + (tid >> 3) + 32 * i;
-      if (gr < nrows && k < K)
-        r[i] = *reinterpret_cast<const u32x4*>(g + (int64_t)gr * ld + k);
-      else
-        r[i] = u32x4{0, 0, 0, 0};
+      const bool ok = kok && row0 + (tid >> 3) + 32 * i < op.rows;
+      r[i] = buf_load16(op.rsrc, ok ? base + (uint32_t)(32 * i) * op.ld_bytes : kOOB);
     }
   }
   __device__ __forceinline__ void store(uint16_t* s) const {
@@ -95,23 +119,22 @@ struct TileLoader<ROWS, MNMAJOR> {
   static constexpr int NBLK = ROWS;  // (ROWS/8 row groups) x (8 k groups)
   static_assert(NBLK <= NTHREADS, "one 8x8 block per thread at most");
   u32x4 r[8];
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ g, int64_t ld, int row0, int nrows, int k0, int K) {
+  __device__ __forceinline__ void load(const Operand& op, int row0, int k0) {
     const int tid = threadIdx.x;
-    if (tid >= NBLK) return;
+    if (NBLK < NTHREADS && tid >= NBLK) return;
     const int mg = tid % (ROWS / 8), kg = tid / (ROWS / 8);
-    const int gr = row0 + mg * 8;
+    const bool rok = row0 + mg * 8 < op.rows;
+    const int kb = k0 + kg * 8;
+    const uint32_t base = (uint32_t)kb * op.ld_bytes + (uint32_t)(row0 + mg * 8) * 2u;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int k = k0 + kg * 8 + j;
-      if (gr < nrows && k < K)
-        r[j] = *reinterpret_cast<const u32x4*>(g + (int64_t)k * ld + gr);
-      else
-        r[j] = u32x4{0, 0, 0, 0};
+      const bool ok = rok && kb + j < op.K;
+      r[j] = buf_load16(op.rsrc, ok ? base + (uint32_t)j * op.ld_bytes : kOOB);
     }
   }
   __device__ __forceinline__ void store(uint16_t* s) const {
     const int tid = threadIdx.x;
-    if (tid >= NBLK) return;
+    if (NBLK < NTHREADS && tid >= NBLK) return;
     const int mg = tid % (ROWS / 8), kg = tid / (ROWS / 8);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -171,13 +194,20 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_bf16_kernel(GemmProblem p, E
   TileLoader<BN, BL> lb[NB];
   const int nk0 = (p.K[0] + BK - 1) / BK;
   const int nk = nk0 + (p.nseg > 1 ? (p.K[1] + BK - 1) / BK : 0);
+  Operand opa[2], opb[2][NB];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    opa[s] = make_operand(p.A[s], p.lda[s], p.M, p.K[s], AL);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) opb[s][b] = make_operand(p.B[s][b], p.ldb[s], p.N, p.K[s], BL);
+  }
 
   auto issue = [&](int kt) {
     const int s = kt < nk0 ? 0 : 1;
     const int k0 = (kt - (s ? nk0 : 0)) * BK;
-    la.load(p.A[s], p.lda[s], m0, p.M, k0, p.K[s]);
+    la.load(opa[s], m0, k0);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) lb[b].load(p.B[s][b], p.ldb[s], n0, p.N, k0, p.K[s]);
+    for (int b = 0; b < NB; ++b) lb[b].load(opb[s][b], n0, k0);
   };
   auto commit = [&](int stage) {
     uint16_t* s = smem + stage * STAGE;

@@ -220,6 +220,10 @@ int mlp_bwd_impl(const tp_mlp_desc& d, const void* dOut, uint32_t thr, float sca
   return hip_status(e);
 }
 
+// The matrix-core kernels address each operand through a buffer resource with
+// 32-bit byte offsets; every operand must stay below 2 GiB.
+bool buffer_ok(int64_t elems, int64_t elem_bytes) { return elems * elem_bytes < ((int64_t)1 << 31); }
+
 int validate_mlp(const tp_mlp_desc* d, bool* bf16) {
   if (!d) return TP_EINVAL;
   if (d->dtype != TP_F32 && d->dtype != TP_BF16) return TP_EDTYPE;
@@ -230,6 +234,9 @@ int validate_mlp(const tp_mlp_desc* d, bool* bf16) {
   *bf16 = d->dtype == TP_BF16;
   const int vec = *bf16 ? 8 : 4;
   if (d->h % vec || (d->h_ffn / d->t) % vec) return TP_EALIGN;
+  const int64_t f = d->h_ffn / d->t;
+  if (*bf16 && (!buffer_ok(d->tokens * d->h, 2) || !buffer_ok(d->tokens * f, 2) || !buffer_ok(d->h * f, 2)))
+    return TP_EUNSUPPORTED;
   return TP_OK;
 }
 
@@ -347,6 +354,10 @@ int tp_attn_shard_fwd(const tp_attn_desc* d, const void* X, const void* Wqkv_i, 
   }
   if (d->h % 8) return TP_EALIGN;
   if (!ptrs_aligned({X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, Z_i})) return TP_EALIGN;
+  {
+    const int64_t T_ = d->b * d->s, nqkv = (int64_t)(d->n_q + 2 * d->n_kv) / d->t * d->d;
+    if (!buffer_ok(T_ * d->h, 2) || !buffer_ok(T_ * nqkv, 2) || !buffer_ok(d->h * nqkv, 2)) return TP_EUNSUPPORTED;
+  }
   const int q = d->n_q / d->t, kv = d->n_kv / d->t, D = d->d;
   const int T_ = (int)(d->b * d->s), h = (int)d->h;
   const int nqkv = (q + 2 * kv) * D;
