@@ -1,0 +1,329 @@
+// bf16 GEMM on the gfx950 matrix cores with LDS-direct loads and a four-stage
+// K pipeline: C = sum over segments of A_s B_s, fp32 accumulation, result
+// handed to a fused epilogue (same problem description and epilogues as
+// gemm_mfma.hpp).
+//
+// Why this shape (gfx950):
+//  * Operand tiles go from HBM straight into LDS with 16-byte buffer loads
+//    that write LDS ("buffer_load_dwordx4 ... lds"): no staging registers,
+//    no ds_write instructions, and ragged edges read zeros because their
+//    offsets point past the buffer resource's end.
+//  * K advances in tiles of BK (32 or 64) through NSTAGE LDS stages; the
+//    loads of a tile are issued NSTAGE-1 tiles before it is consumed.  One
+//    barrier per tile; the wait before it names an exact outstanding-load
+//    count so the loads of later tiles stay in flight across it, and it sits
+//    before the tile's last 16-deep k step so that the next tile's first
+//    fragments are read from LDS while that step's MFMAs execute.  The
+//    configuration used for large problems is BK = 64 with 2 stages (one
+//    barrier per 64 k, prefetch one tile ahead), which measured faster than
+//    BK = 32 with 3 or 4 stages on gfx950.
+//  * K-contiguous operands live in LDS as [rows][BK] with the 16-byte chunks
+//    of a row XOR-swizzled by the row index (conflict-free 128-bit fragment
+//    reads).  M/N-contiguous operands (weights stored [K,N], the
+//    transposed activations of the weight gradients) live as [BK][rows] with
+//    their 16-byte chunks swizzled by k, and are read into the MFMA's
+//    K-contiguous register layout with ds_read_b64_tr_b16 (gfx950's
+//    transposing LDS read): no transposition ever goes through registers.
+//  * v_mfma_f32_32x32x16_bf16 with the B fragment as first operand, so a
+//    lane's accumulators are four consecutive output columns (8- or 16-byte
+//    stores).
+//  * The blockIdx -> tile map is the XCD-aware grouped map of gemm_mfma.hpp.
+#pragma once
+
+#include "common.hpp"
+#include "gemm_mfma.hpp"
+
+namespace tp {
+namespace gemm3 {
+
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor in four SGPRs (base, stride 0, size, raw dword format).
+__device__ __forceinline__ u32x4 sgpr_rsrc(const void* base, uint32_t num_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, num_bytes, 0x00020000u};
+}
+
+// One 16-byte load per lane from `rsrc` at byte offset `voff` into LDS at
+// m0 + 16 * lane.  Written in assembly so that the compiler neither inserts
+// conservative waits for it nor reorders LDS accesses across it; completion
+// is tracked explicitly with wait_vmcnt.
+__device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(n) leaving the other counters untouched (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Byte offset of 16-byte chunk c of row `row` in a K-contiguous [ROWS][32] tile.
+// Rows of BK = 32 are 64 bytes (4 chunks, swizzled by row bits 2-3); rows of
+// BK = 64 are 128 bytes (8 chunks, swizzled by row bits 0-2 xor 3-5).  Either
+// way 16 consecutive rows at one logical chunk hit 16 distinct bank groups.
+template <int BK>
+__device__ __forceinline__ uint32_t kofs(int row, int c) {
+  if (BK == 32) return row * 64 + ((c ^ ((row >> 2) & 3)) << 4);
+  return row * 128 + ((c ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
+
+// Byte offset of 16-byte chunk c of k-row k in an M/N-contiguous [32][ROWS] tile.
+template <int ROWS>
+__device__ __forceinline__ uint32_t mofs(int k, int c) {
+  constexpr int NCH = ROWS / 8;
+  return k * ROWS * 2 + ((c ^ (((k & 7) << 1) & (NCH - 1))) << 4);
+}
+
+struct DOperand {
+  u32x4 rsrc;
+  uint32_t ld_bytes;
+  int rows, K;
+};
+
+__device__ __forceinline__ DOperand make_doperand(const uint16_t* p, int64_t ld, int rows, int K, int layout) {
+  DOperand o;
+  const uint32_t slow = layout == KMAJOR ? (uint32_t)rows : (uint32_t)K;
+  o.rsrc = sgpr_rsrc(p, slow * (uint32_t)ld * 2u);
+  o.ld_bytes = (uint32_t)ld * 2u;
+  o.rows = rows;
+  o.K = K;
+  return o;
+}
+
+// Per-lane source coordinates of the LDS-direct loads of one operand tile.
+// The tile is ROWS * 64 bytes = ROWS/16 wave-instructions of 1 KiB; wave w
+// issues instructions w*PER .. w*PER+PER-1, lane l fills LDS chunk
+// q = instr*64 + l.
+template <int ROWS, int LAYOUT, int NW, int BK>
+struct DmaLoader {
+  static constexpr int INSTR = ROWS * BK * 2 / 1024;
+  static constexpr int PER = INSTR / NW;
+  static_assert(PER >= 1 && PER * NW == INSTR, "tile instructions must divide evenly over the waves");
+  int a[PER];   // KMAJOR: row in tile; MNMAJOR: k in tile
+  int b[PER];   // KMAJOR: k offset (elements) in tile; MNMAJOR: row offset in tile
+  __device__ __forceinline__ void init() {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = (wave * PER + i) * 64 + lane;
+      if (LAYOUT == KMAJOR && BK == 32) {
+        const int row = q >> 2, p = q & 3;
+        a[i] = row;
+        b[i] = (p ^ ((row >> 2) & 3)) * 8;
+      } else if (LAYOUT == KMAJOR) {
+        const int row = q >> 3, p = q & 7;
+        a[i] = row;
+        b[i] = (p ^ ((row ^ (row >> 3)) & 7)) * 8;
+      } else {
+        constexpr int NCH = ROWS / 8;
+        const int k = q / NCH, p = q % NCH;
+        a[i] = k;
+        b[i] = (p ^ (((k & 7) << 1) & (NCH - 1))) * 8;
+      }
+    }
+  }
+  __device__ __forceinline__ void issue(const DOperand& op, int row0, int k0, uint32_t lds_tile) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, so m0 stays scalar
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      uint32_t off;
+      if (LAYOUT == KMAJOR) {
+        const int r = row0 + a[i], k = k0 + b[i];
+        off = (r < op.rows && k < op.K) ? (uint32_t)r * op.ld_bytes + (uint32_t)k * 2u : kOOB;
+      } else {
+        const int k = k0 + a[i], r = row0 + b[i];
+        off = (r < op.rows && k < op.K) ? (uint32_t)k * op.ld_bytes + (uint32_t)r * 2u : kOOB;
+      }
+      dma16(op.rsrc, off, lds_tile + (uint32_t)(wave * PER + i) * 1024u);
+    }
+  }
+};
+
+// MFMA operand fragment (32 rows x 16 k) of the tile row block starting at
+// `tr`, k step kk (0 .. BK/16-1), from an LDS tile of the given layout.
+template <int ROWS, int LAYOUT, int BK>
+__device__ __forceinline__ bf16x8 fragment(const lds_u8* tile, int tr, int kk) {
+  const int lane = threadIdx.x & 63;
+  if (LAYOUT == KMAJOR) {
+    const int row = tr + (lane & 31), c = kk * 2 + (lane >> 5);
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(tile + kofs<BK>(row, c));
+  } else {
+    // ds_read_b64_tr_b16: within each 16-lane group, lane R supplies the
+    // address of 4 consecutive rows at k-row kb + R/4, rows m_base + 4*(R%4);
+    // lane i then holds rows m_base + i at k = kb .. kb+3.
+    const int g = lane >> 4, R = lane & 15;
+    const int m = tr + 16 * (g & 1) + 4 * (R & 3);
+    v4i16 h[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int k = kk * 16 + 8 * (g >> 1) + 4 * half + (R >> 2);
+      const uint32_t off = mofs<ROWS>(k, m >> 3) + (m & 7) * 2;
+      h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<__attribute__((address_space(3))) v4i16*>(const_cast<lds_u8*>(tile) + off));
+    }
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    v8i16 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int BK, int NSTAGE, int AL, int BL, class Epi>
+__global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem p, Epi epi) {
+  constexpr int NW = WGM * WGN;
+  constexpr int NB = Epi::NB;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  static_assert(TM >= 1 && TN >= 1, "wave sub-tile must hold whole 32x32 MFMA tiles");
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  constexpr int STAGE = A_BYTES + NB * B_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
+
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  int tm, tn;
+  gemm::tile_coords(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const lds_u8* lds = (const lds_u8*)smem;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+  f32x16 acc[NB][TM][TN];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[b][i][j][e] = 0.0f;
+
+  DmaLoader<BM, AL, NW, BK> la;
+  DmaLoader<BN, BL, NW, BK> lb;
+  la.init();
+  lb.init();
+  constexpr int LPT = DmaLoader<BM, AL, NW, BK>::PER + NB * DmaLoader<BN, BL, NW, BK>::PER;  // loads per wave per tile
+  static_assert(LPT * (NSTAGE - 2) < 64 && NSTAGE >= 2 && NSTAGE <= 4, "vmcnt range / stage count");
+
+  const int nk0 = (p.K[0] + BK - 1) / BK;
+  const int nk = nk0 + (p.nseg > 1 ? (p.K[1] + BK - 1) / BK : 0);
+  DOperand opa[2], opb[2][NB];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    opa[s] = make_doperand(p.A[s], p.lda[s], p.M, p.K[s], AL);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) opb[s][b] = make_doperand(p.B[s][b], p.ldb[s], p.N, p.K[s], BL);
+  }
+
+  auto issue = [&](int kt) {
+    const int s = kt < nk0 ? 0 : 1;
+    const int k0 = (kt - (s ? nk0 : 0)) * BK;
+    const uint32_t st = lds_base + (uint32_t)(kt % NSTAGE) * STAGE;
+    la.issue(opa[s], m0, k0, st);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) lb.issue(opb[s][b], n0, k0, st + A_BYTES + b * B_BYTES);
+  };
+
+  // Fragments of one k step (16 of the tile's 32 k) for all of this wave's MFMA tiles.
+  struct Frags {
+    bf16x8 a[TM], b[NB][TN];
+  };
+  auto load_frags = [&](Frags& F, int kt, int kk) {
+    const lds_u8* As = lds + (kt % NSTAGE) * STAGE;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) F.a[i] = fragment<BM, AL, BK>(As, wm * WM + i * 32, kk);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) F.b[b][j] = fragment<BN, BL, BK>(As + A_BYTES + b * B_BYTES, wn * WN + j * 32, kk);
+  };
+  auto mfmas = [&](const Frags& F) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.b[b][j], F.a[i], acc[b][i][j], 0, 0, 0);
+  };
+  // Wait until tile t has landed in LDS for every wave (at most `ahead`
+  // later tiles still in flight), with this wave's LDS reads drained.
+  auto sync_tile = [&](int t) {
+    const int ahead = min(nk - 1, t + NSTAGE - 2) - t;
+    if (ahead >= 2)
+      wait_vmcnt<2 * LPT>();
+    else if (ahead == 1)
+      wait_vmcnt<LPT>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    barrier();
+  };
+
+  // Pipeline: tile t's loads are issued NSTAGE-1 tiles ahead; fragments of
+  // k step kk+1 are read while the MFMAs of step kk run, and the barrier that
+  // publishes the next tile sits before the last k step, so the next tile's
+  // first fragments are read while this tile's last MFMAs run.
+#pragma unroll
+  for (int t = 0; t < NSTAGE - 1; ++t)
+    if (t < nk) issue(t);
+  Frags F[2];
+  constexpr int KK = BK / 16;
+  if (nk > 0) {
+    sync_tile(0);
+    load_frags(F[0], 0, 0);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + NSTAGE - 1 < nk) issue(kt + NSTAGE - 1);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK) {
+        load_frags(F[(kk + 1) & 1], kt, kk + 1);
+      } else if (kt + 1 < nk) {
+        sync_tile(kt + 1);
+        load_frags(F[(kk + 1) & 1], kt + 1, 0);
+      }
+      mfmas(F[kk & 1]);
+    }
+  }
+
+  // Epilogue: lane holds, for tile (i, j), row m = .. + (lane & 31) and columns
+  // n = .. + 8*q4 + 4*(lane >> 5) + e, e = 0..3, in accumulator slots 4*q4 + e.
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + wm * WM + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int n = n0 + wn * WN + j * 32 + q4 * 8 + (lane >> 5) * 4;
+        float v[NB][4];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[b][e] = acc[b][i][j][q4 * 4 + e];
+        epi(m, n, v);
+      }
+    }
+  }
+}
+
+}  // namespace gemm3
+
+// Host-side launcher: grid of ceil(M/BM) * ceil(N/BN) work-groups of 64 * WGM * WGN threads.
+template <int BM, int BN, int WGM, int WGN, int BK, int NSTAGE, int AL, int BL, class Epi>
+hipError_t launch_gemm_dma(const GemmProblem& p, const Epi& epi, hipStream_t stream) {
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm3::gemm_dma_kernel<BM, BN, WGM, WGN, BK, NSTAGE, AL, BL, Epi>), dim3(tiles), dim3(64 * WGM * WGN), 0,
+                     stream, p, epi);
+  return hipGetLastError();
+}
+
+}  // namespace tp

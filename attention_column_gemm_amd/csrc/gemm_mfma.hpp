@@ -34,6 +34,8 @@
 //    one XCD share A rows and B columns in that XCD's L2.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace tp {
@@ -55,7 +57,6 @@ struct GemmProblem {
 namespace gemm {
 
 constexpr int BK = 64;
-constexpr int NTHREADS = 256;
 constexpr int GROUP_M = 4;
 
 // Element offset of 16-byte chunk `chunk` of LDS tile row `row`.  The chunk is
@@ -84,13 +85,15 @@ __device__ __forceinline__ Operand make_operand(const uint16_t* p, int64_t ld, i
   return o;
 }
 
-template <int ROWS, int LAYOUT>
+template <int ROWS, int LAYOUT, int NT>
 struct TileLoader;
 
-// K contiguous in HBM: each thread moves 16-byte chunks (row, kc).
-template <int ROWS>
-struct TileLoader<ROWS, KMAJOR> {
-  static constexpr int PER = ROWS * (BK / 8) / NTHREADS;
+// K contiguous in HBM: the tile is ROWS x 8 chunks of 16 bytes; chunk item
+// tid + NT*i is (row, kc) = (item / 8, item % 8).
+template <int ROWS, int NT>
+struct TileLoader<ROWS, KMAJOR, NT> {
+  static constexpr int PER = ROWS * (BK / 8) / NT;
+  static_assert(PER * NT == ROWS * (BK / 8), "chunks must divide evenly over the threads");
   u32x4 r[PER];
   __device__ __forceinline__ void load(const Operand& op, int row0, int k0) {
     const int tid = threadIdx.x, kc = tid & 7;
@@ -98,54 +101,70 @@ struct TileLoader<ROWS, KMAJOR> {
     const uint32_t base = (uint32_t)(row0 + (tid >> 3)) * op.ld_bytes + (uint32_t)(k0 + kc * 8) * 2u;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const bool ok = kok && row0 + (tid >> 3) + 32 * i < op.rows;
-      r[i] = buf_load16(op.rsrc, ok ? base + (uint32_t)(32 * i) * op.ld_bytes : kOOB);
+      const bool ok = kok && row0 + (tid >> 3) + (NT / 8) * i < op.rows;
+      r[i] = buf_load16(op.rsrc, ok ? base + (uint32_t)((NT / 8) * i) * op.ld_bytes : kOOB);
     }
   }
   __device__ __forceinline__ void store(uint16_t* s) const {
     const int tid = threadIdx.x, kc = tid & 7;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int row = (tid >> 3) + 32 * i;
+      const int row = (tid >> 3) + (NT / 8) * i;
       *reinterpret_cast<u32x4*>(s + lds_off(row, kc)) = r[i];
     }
   }
 };
 
-// M/N contiguous in HBM: a thread loads an 8 (k) x 8 (rows) block with eight
-// 16-byte reads and writes it transposed as eight 16-byte LDS rows.
-template <int ROWS>
-struct TileLoader<ROWS, MNMAJOR> {
-  static constexpr int NBLK = ROWS;  // (ROWS/8 row groups) x (8 k groups)
-  static_assert(NBLK <= NTHREADS, "one 8x8 block per thread at most");
-  u32x4 r[8];
+// M/N contiguous in HBM: a thread loads an 8 (k) x BW (rows) block, BW = 8 or
+// 4, with eight row reads of 2*BW bytes and writes it transposed as BW LDS
+// rows of 16 bytes (8 k values each).  BW = 4 is used when 8-wide blocks
+// would leave threads idle.
+template <int ROWS, int NT>
+struct TileLoader<ROWS, MNMAJOR, NT> {
+  static constexpr int BW = (ROWS >= NT) ? 8 : 4;
+  static constexpr int NG = ROWS / BW;               // row groups
+  static constexpr int NBLK = NG * (BK / 8);         // blocks of 8 k x BW rows
+  static constexpr int PER = NBLK >= NT ? NBLK / NT : 1;
+  static_assert(NBLK < NT || PER * NT == NBLK, "blocks must divide evenly over the threads");
+  typedef typename std::conditional<BW == 8, u32x4, u32x2>::type vec_t;
+  vec_t r[PER][8];
   __device__ __forceinline__ void load(const Operand& op, int row0, int k0) {
-    const int tid = threadIdx.x;
-    if (NBLK < NTHREADS && tid >= NBLK) return;
-    const int mg = tid % (ROWS / 8), kg = tid / (ROWS / 8);
-    const bool rok = row0 + mg * 8 < op.rows;
-    const int kb = k0 + kg * 8;
-    const uint32_t base = (uint32_t)kb * op.ld_bytes + (uint32_t)(row0 + mg * 8) * 2u;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool ok = rok && kb + j < op.K;
-      r[j] = buf_load16(op.rsrc, ok ? base + (uint32_t)j * op.ld_bytes : kOOB);
+    for (int b = 0; b < PER; ++b) {
+      const int blk = threadIdx.x + NT * b;
+      if (NBLK < NT && blk >= NBLK) return;
+      const int mg = blk % NG, kg = blk / NG;
+      const bool rok = row0 + mg * BW < op.rows;
+      const int kb = k0 + kg * 8;
+      const uint32_t base = (uint32_t)kb * op.ld_bytes + (uint32_t)(row0 + mg * BW) * 2u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool ok = rok && kb + j < op.K;
+        const uint32_t off = ok ? base + (uint32_t)j * op.ld_bytes : kOOB;
+        if constexpr (BW == 8)
+          r[b][j] = buf_load16(op.rsrc, off);
+        else
+          r[b][j] = __builtin_amdgcn_raw_buffer_load_b64(op.rsrc, off, 0, 0);
+      }
     }
   }
   __device__ __forceinline__ void store(uint16_t* s) const {
-    const int tid = threadIdx.x;
-    if (NBLK < NTHREADS && tid >= NBLK) return;
-    const int mg = tid % (ROWS / 8), kg = tid / (ROWS / 8);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      u32x4 w;
+    for (int b = 0; b < PER; ++b) {
+      const int blk = threadIdx.x + NT * b;
+      if (NBLK < NT && blk >= NBLK) return;
+      const int mg = blk % NG, kg = blk / NG;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = r[2 * q][i >> 1], hi = r[2 * q + 1][i >> 1];
-        w[q] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      for (int i = 0; i < BW; ++i) {
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = r[b][2 * q][i >> 1], hi = r[b][2 * q + 1][i >> 1];
+          w[q] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+        }
+        const int row = mg * BW + i;
+        *reinterpret_cast<u32x4*>(s + lds_off(row, kg)) = w;
       }
-      const int row = mg * 8 + i;
-      *reinterpret_cast<u32x4*>(s + lds_off(row, kg)) = w;
     }
   }
 };
@@ -165,11 +184,15 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   tn = inner / gsize;
 }
 
-template <int BM, int BN, int AL, int BL, class Epi>
-__global__ void __launch_bounds__(NTHREADS, 1) gemm_bf16_kernel(GemmProblem p, Epi epi) {
+// Block tile BM x BN computed by WGM x WGN waves, each owning a
+// (BM/WGM) x (BN/WGN) sub-tile of 32x32 MFMA tiles.
+template <int BM, int BN, int WGM, int WGN, int AL, int BL, class Epi>
+__global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_bf16_kernel(GemmProblem p, Epi epi) {
+  constexpr int NT = 64 * WGM * WGN;
   constexpr int NB = Epi::NB;
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
+  static_assert(TM >= 1 && TN >= 1, "wave sub-tile must hold whole 32x32 MFMA tiles");
   constexpr int STAGE = (BM + NB * BN) * BK;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
 
@@ -178,7 +201,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_bf16_kernel(GemmProblem p, E
   tile_coords(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   f32x16 acc[NB][TM][TN];
 #pragma unroll
@@ -190,8 +213,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_bf16_kernel(GemmProblem p, E
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[b][i][j][e] = 0.0f;
 
-  TileLoader<BM, AL> la;
-  TileLoader<BN, BL> lb[NB];
+  TileLoader<BM, AL, NT> la;
+  TileLoader<BN, BL, NT> lb[NB];
   const int nk0 = (p.K[0] + BK - 1) / BK;
   const int nk = nk0 + (p.nseg > 1 ? (p.K[1] + BK - 1) / BK : 0);
   Operand opa[2], opb[2][NB];
@@ -274,12 +297,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_bf16_kernel(GemmProblem p, E
 
 }  // namespace gemm
 
-// Host-side launcher: grid of ceil(M/BM) * ceil(N/BN) work-groups of 256 threads.
-template <int BM, int BN, int AL, int BL, class Epi>
+// Host-side launcher: grid of ceil(M/BM) * ceil(N/BN) work-groups of
+// 64 * WGM * WGN threads.
+template <int BM, int BN, int WGM, int WGN, int AL, int BL, class Epi>
 hipError_t launch_gemm_bf16(const GemmProblem& p, const Epi& epi, hipStream_t stream) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm::gemm_bf16_kernel<BM, BN, AL, BL, Epi>), dim3(tiles), dim3(gemm::NTHREADS), 0, stream, p, epi);
+  hipLaunchKernelGGL((gemm::gemm_bf16_kernel<BM, BN, WGM, WGN, AL, BL, Epi>), dim3(tiles), dim3(64 * WGM * WGN), 0,
+                     stream, p, epi);
   return hipGetLastError();
 }
 
