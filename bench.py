@@ -154,6 +154,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="cfg5", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB (a known-size reference for "
+                         "HBM traffic counters); not part of the timed region")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one rank's shard on ONE GPU; --gpus {args.gpus} is not supported "
@@ -328,6 +331,15 @@ def main():
     if attn is not None:
         af = I.ATTN_CONFIGS[acid].flops_per_rank()
         res["attention_fwd_tflops"] = round(af / (span["attention_fwd_and_allreduce"] * 1e-3) / 1e12, 2)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 2
+        src = torch.empty(n, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_mib"] = args.copy_calibration_mib
+        del src, dst
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(mc, X, dOut, w)
