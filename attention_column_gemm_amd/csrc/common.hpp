@@ -46,6 +46,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Storage policies: load/store 4 consecutive elements as float.
 template <class T> struct Elem;
 template <> struct Elem<uint16_t> {
+  typedef u32x2 raw_t;  // 4 elements as loaded, unpacked later
+  __device__ __forceinline__ static raw_t load_raw(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+  __device__ __forceinline__ static void unpack(const raw_t& w, float (&v)[4]) {
+    v[0] = bf16lo(w.x); v[1] = bf16hi(w.x); v[2] = bf16lo(w.y); v[3] = bf16hi(w.y);
+  }
   __device__ __forceinline__ static void load4(const uint16_t* p, float (&v)[4]) {
     u32x2 w = *reinterpret_cast<const u32x2*>(p);
     v[0] = bf16lo(w.x); v[1] = bf16hi(w.x); v[2] = bf16lo(w.y); v[3] = bf16hi(w.y);
@@ -59,6 +64,11 @@ template <> struct Elem<uint16_t> {
   __device__ __forceinline__ static float load1(const uint16_t* p) { return bf16_to_f32(*p); }
 };
 template <> struct Elem<float> {
+  typedef f32x4 raw_t;
+  __device__ __forceinline__ static raw_t load_raw(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+  __device__ __forceinline__ static void unpack(const raw_t& w, float (&v)[4]) {
+    v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+  }
   __device__ __forceinline__ static void load4(const float* p, float (&v)[4]) {
     f32x4 w = *reinterpret_cast<const f32x4*>(p);
     v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;

@@ -3,6 +3,12 @@
 // columns n..n+3 (n a multiple of 4, N a multiple of 4) and the NB accumulator
 // values of those columns, one set per B operand.
 //
+// Epilogues that read saved tensors (the backward ones) do so in two phases:
+// load(m, n, aux) issues the reads into an Aux record, and the call operator
+// consumes it.  The GEMM kernels issue the loads of many (m, n) groups before
+// consuming any, so the memory latency is paid once per batch rather than once
+// per group.
+//
 // The fusions follow where the pages put the elementwise work of an MLP shard:
 // the activation (GeLU or SwiGLU's SiLU-gated product) runs locally on the
 // column-parallel GEMM's output columns ([L11] section 2 -- "[L11]" is the
@@ -20,10 +26,12 @@ namespace tp {
 template <class T>
 struct EpiStore {
   static constexpr int NB = 1;
+  struct Aux {};
   T* C;
   int64_t ldc;
   int M, N;
-  __device__ __forceinline__ void operator()(int m, int n, const float (&v)[NB][4]) const {
+  __device__ __forceinline__ void load(int, int, Aux&) const {}
+  __device__ __forceinline__ void operator()(int m, int n, const float (&v)[NB][4], const Aux& = Aux()) const {
     if (m >= M || n >= N) return;
     Elem<T>::store4(C + (int64_t)m * ldc + n, v[0]);
   }
@@ -33,11 +41,13 @@ struct EpiStore {
 template <class T>
 struct EpiStore2 {
   static constexpr int NB = 2;
+  struct Aux {};
   T* C0;
   T* C1;
   int64_t ldc;
   int M, N;
-  __device__ __forceinline__ void operator()(int m, int n, const float (&v)[NB][4]) const {
+  __device__ __forceinline__ void load(int, int, Aux&) const {}
+  __device__ __forceinline__ void operator()(int m, int n, const float (&v)[NB][4], const Aux& = Aux()) const {
     if (m >= M || n >= N) return;
     Elem<T>::store4(C0 + (int64_t)m * ldc + n, v[0]);
     Elem<T>::store4(C1 + (int64_t)m * ldc + n, v[1]);
@@ -48,12 +58,14 @@ struct EpiStore2 {
 template <class T>
 struct EpiGeluFwd {
   static constexpr int NB = 1;
+  struct Aux {};
   T* A;
   T* H;
   const T* b1;
   int64_t ld;
   int M, N;
-  __device__ __forceinline__ void operator()(int m, int n, const float (&v)[NB][4]) const {
+  __device__ __forceinline__ void load(int, int, Aux&) const {}
+  __device__ __forceinline__ void operator()(int m, int n, const float (&v)[NB][4], const Aux& = Aux()) const {
     if (m >= M || n >= N) return;
     float a[4] = {v[0][0], v[0][1], v[0][2], v[0][3]};
     if (b1) {
@@ -74,12 +86,14 @@ struct EpiGeluFwd {
 template <class T>
 struct EpiSwigluFwd {
   static constexpr int NB = 2;
+  struct Aux {};
   T* G;
   T* U;
   T* H;
   int64_t ld;
   int M, N;
-  __device__ __forceinline__ void operator()(int m, int n, const float (&v)[NB][4]) const {
+  __device__ __forceinline__ void load(int, int, Aux&) const {}
+  __device__ __forceinline__ void operator()(int m, int n, const float (&v)[NB][4], const Aux& = Aux()) const {
     if (m >= M || n >= N) return;
     float hv[4];
 #pragma unroll
@@ -95,15 +109,21 @@ struct EpiSwigluFwd {
 template <class T>
 struct EpiGeluBwd {
   static constexpr int NB = 1;
+  struct Aux {
+    typename Elem<T>::raw_t a;
+  };
   const T* A;
   T* dA;
   int64_t ld;
   int M, N;
-  __device__ __forceinline__ void operator()(int m, int n, const float (&v)[NB][4]) const {
+  __device__ __forceinline__ void load(int m, int n, Aux& x) const {
+    if (m < M && n < N) x.a = Elem<T>::load_raw(A + (int64_t)m * ld + n);
+  }
+  __device__ __forceinline__ void operator()(int m, int n, const float (&v)[NB][4], const Aux& x) const {
     if (m >= M || n >= N) return;
     const int64_t o = (int64_t)m * ld + n;
     float a[4], r[4];
-    Elem<T>::load4(A + o, a);
+    Elem<T>::unpack(x.a, a);
 #pragma unroll
     for (int j = 0; j < 4; ++j) r[j] = v[0][j] * gelu_grad_f(a[j]);
     Elem<T>::store4(dA + o, r);
@@ -115,18 +135,28 @@ struct EpiGeluBwd {
 template <class T>
 struct EpiSwigluBwd {
   static constexpr int NB = 1;
+  struct Aux {
+    typename Elem<T>::raw_t g, u;
+  };
   const T* G;
   const T* U;
   T* dG;
   T* dU;
   int64_t ld;
   int M, N;
-  __device__ __forceinline__ void operator()(int m, int n, const float (&v)[NB][4]) const {
+  __device__ __forceinline__ void load(int m, int n, Aux& x) const {
+    if (m < M && n < N) {
+      const int64_t o = (int64_t)m * ld + n;
+      x.g = Elem<T>::load_raw(G + o);
+      x.u = Elem<T>::load_raw(U + o);
+    }
+  }
+  __device__ __forceinline__ void operator()(int m, int n, const float (&v)[NB][4], const Aux& x) const {
     if (m >= M || n >= N) return;
     const int64_t o = (int64_t)m * ld + n;
     float g[4], u[4], dg[4], du[4];
-    Elem<T>::load4(G + o, g);
-    Elem<T>::load4(U + o, u);
+    Elem<T>::unpack(x.g, g);
+    Elem<T>::unpack(x.u, u);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float s = sigmoid_f(g[j]);

@@ -1,7 +1,7 @@
 // bf16 GEMM on the gfx950 matrix cores with LDS-direct loads and a four-stage
 // K pipeline: C = sum over segments of A_s B_s, fp32 accumulation, result
 // handed to a fused epilogue (same problem description and epilogues as
-// gemm_mfma.hpp).
+// gemm_common.hpp).
 //
 // Why this shape (gfx950):
 //  * Operand tiles go from HBM straight into LDS with 16-byte buffer loads
@@ -27,11 +27,11 @@
 //  * v_mfma_f32_32x32x16_bf16 with the B fragment as first operand, so a
 //    lane's accumulators are four consecutive output columns (8- or 16-byte
 //    stores).
-//  * The blockIdx -> tile map is the XCD-aware grouped map of gemm_mfma.hpp.
+//  * The blockIdx -> tile map is the XCD-aware grouped map of gemm_common.hpp.
 #pragma once
 
 #include "common.hpp"
-#include "gemm_mfma.hpp"
+#include "gemm_common.hpp"
 
 namespace tp {
 namespace gemm3 {
@@ -106,42 +106,45 @@ struct DmaLoader {
   static constexpr int INSTR = ROWS * BK * 2 / 1024;
   static constexpr int PER = INSTR / NW;
   static_assert(PER >= 1 && PER * NW == INSTR, "tile instructions must divide evenly over the waves");
-  int a[PER];   // KMAJOR: row in tile; MNMAJOR: k in tile
-  int b[PER];   // KMAJOR: k offset (elements) in tile; MNMAJOR: row offset in tile
-  __device__ __forceinline__ void init() {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t base[PER];  // byte offset of this lane's chunk for k0 = 0
+  int kloc[PER];       // k index of the chunk within the tile; 2^30 if its M/N row is outside the matrix
+  uint32_t m0off;      // this wave's first LDS destination within a tile (bytes)
+
+  // row0: first M/N row of the tile; ld_bytes, rows: the operand's leading
+  // dimension and M/N extent (the same for every K segment).
+  __device__ __forceinline__ void init(int row0, uint32_t ld_bytes, int rows) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, so m0 stays scalar
+    m0off = (uint32_t)(wave * PER) * 1024u;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int q = (wave * PER + i) * 64 + lane;
+      int r, k;
       if (LAYOUT == KMAJOR && BK == 32) {
         const int row = q >> 2, p = q & 3;
-        a[i] = row;
-        b[i] = (p ^ ((row >> 2) & 3)) * 8;
+        r = row;
+        k = (p ^ ((row >> 2) & 3)) * 8;
       } else if (LAYOUT == KMAJOR) {
         const int row = q >> 3, p = q & 7;
-        a[i] = row;
-        b[i] = (p ^ ((row ^ (row >> 3)) & 7)) * 8;
+        r = row;
+        k = (p ^ ((row ^ (row >> 3)) & 7)) * 8;
       } else {
         constexpr int NCH = ROWS / 8;
-        const int k = q / NCH, p = q % NCH;
-        a[i] = k;
-        b[i] = (p ^ (((k & 7) << 1) & (NCH - 1))) * 8;
+        const int kk = q / NCH, p = q % NCH;
+        k = kk;
+        r = (p ^ (((kk & 7) << 1) & (NCH - 1))) * 8;
       }
+      r += row0;
+      kloc[i] = r < rows ? k : (1 << 30);
+      base[i] = LAYOUT == KMAJOR ? (uint32_t)r * ld_bytes + (uint32_t)k * 2u : (uint32_t)k * ld_bytes + (uint32_t)r * 2u;
     }
   }
-  __device__ __forceinline__ void issue(const DOperand& op, int row0, int k0, uint32_t lds_tile) const {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, so m0 stays scalar
+  // Loads of the K tile starting at k0 into the LDS tile at lds_tile.
+  __device__ __forceinline__ void issue(const DOperand& op, int k0, uint32_t lds_tile) const {
+    const uint32_t kbytes = LAYOUT == KMAJOR ? (uint32_t)k0 * 2u : (uint32_t)k0 * op.ld_bytes;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      uint32_t off;
-      if (LAYOUT == KMAJOR) {
-        const int r = row0 + a[i], k = k0 + b[i];
-        off = (r < op.rows && k < op.K) ? (uint32_t)r * op.ld_bytes + (uint32_t)k * 2u : kOOB;
-      } else {
-        const int k = k0 + a[i], r = row0 + b[i];
-        off = (r < op.rows && k < op.K) ? (uint32_t)k * op.ld_bytes + (uint32_t)r * 2u : kOOB;
-      }
-      dma16(op.rsrc, off, lds_tile + (uint32_t)(wave * PER + i) * 1024u);
+      dma16(op.rsrc, kloc[i] + k0 < op.K ? base[i] + kbytes : kOOB, lds_tile + m0off + (uint32_t)i * 1024u);
     }
   }
 };
@@ -206,8 +209,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem
 
   DmaLoader<BM, AL, NW, BK> la;
   DmaLoader<BN, BL, NW, BK> lb;
-  la.init();
-  lb.init();
+  // every K segment shares the leading dimensions of segment 0 (host contract)
+  la.init(m0, (uint32_t)p.lda[0] * 2u, p.M);
+  lb.init(n0, (uint32_t)p.ldb[0] * 2u, p.N);
   constexpr int LPT = DmaLoader<BM, AL, NW, BK>::PER + NB * DmaLoader<BN, BL, NW, BK>::PER;  // loads per wave per tile
   static_assert(LPT * (NSTAGE - 2) < 64 && NSTAGE >= 2 && NSTAGE <= 4, "vmcnt range / stage count");
 
@@ -225,9 +229,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem
     const int s = kt < nk0 ? 0 : 1;
     const int k0 = (kt - (s ? nk0 : 0)) * BK;
     const uint32_t st = lds_base + (uint32_t)(kt % NSTAGE) * STAGE;
-    la.issue(opa[s], m0, k0, st);
+    la.issue(opa[s], k0, st);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) lb.issue(opb[s][b], n0, k0, st + A_BYTES + b * B_BYTES);
+    for (int b = 0; b < NB; ++b) lb.issue(opb[s][b], k0, st + A_BYTES + b * B_BYTES);
   };
 
   // Fragments of one k step (16 of the tile's 32 k) for all of this wave's MFMA tiles.
@@ -295,9 +299,16 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem
 
   // Epilogue: lane holds, for tile (i, j), row m = .. + (lane & 31) and columns
   // n = .. + 8*q4 + 4*(lane >> 5) + e, e = 0..3, in accumulator slots 4*q4 + e.
+  // The saved inputs an epilogue reads are loaded for a whole 32-row block
+  // before any of it is consumed.
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int m = m0 + wm * WM + i * 32 + (lane & 31);
+    typename Epi::Aux aux[TN][4];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) epi.load(m, n0 + wn * WN + j * 32 + q4 * 8 + (lane >> 5) * 4, aux[j][q4]);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
 #pragma unroll
@@ -308,7 +319,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem
         for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[b][e] = acc[b][i][j][q4 * 4 + e];
-        epi(m, n, v);
+        epi(m, n, v, aux[j][q4]);
       }
     }
   }

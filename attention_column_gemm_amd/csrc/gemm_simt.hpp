@@ -8,7 +8,7 @@
 #pragma once
 
 #include "common.hpp"
-#include "gemm_mfma.hpp"
+#include "gemm_common.hpp"
 
 namespace tp {
 namespace simt {
@@ -61,6 +61,9 @@ __global__ void __launch_bounds__(NTHREADS) gemm_f32_kernel(GemmProblem p, Epi e
       __syncthreads();
     }
   }
+  typename Epi::Aux aux[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) epi.load(m0 + ty * 4 + i, n0 + tx * 4, aux[i]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float v[NB][4];
@@ -68,7 +71,7 @@ __global__ void __launch_bounds__(NTHREADS) gemm_f32_kernel(GemmProblem p, Epi e
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[b][j] = acc[b][i][j];
-    epi(m0 + ty * 4 + i, n0 + tx * 4, v);
+    epi(m0 + ty * 4 + i, n0 + tx * 4, v, aux[i]);
   }
 }
 
