@@ -16,7 +16,7 @@
 #include "elementwise.hpp"
 #include "epilogues.hpp"
 #include "gemm_dma.hpp"
-#include "gemm_mfma.hpp"
+#include "gemm_common.hpp"
 #include "gemm_simt.hpp"
 
 using namespace tp;
