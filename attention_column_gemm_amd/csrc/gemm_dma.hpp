@@ -1,22 +1,25 @@
-// bf16 GEMM on the gfx950 matrix cores with LDS-direct loads and a four-stage
-// K pipeline: C = sum over segments of A_s B_s, fp32 accumulation, result
-// handed to a fused epilogue (same problem description and epilogues as
-// gemm_common.hpp).
+// bf16 GEMM on the gfx950 matrix cores with LDS-direct loads and a
+// two-stage K pipeline: C = sum over segments of A_s B_s, fp32 accumulation,
+// result handed to a fused epilogue (same problem description and epilogues
+// as gemm_common.hpp).
 //
 // Why this shape (gfx950):
 //  * Operand tiles go from HBM straight into LDS with 16-byte buffer loads
 //    that write LDS ("buffer_load_dwordx4 ... lds"): no staging registers,
 //    no ds_write instructions, and ragged edges read zeros because their
 //    offsets point past the buffer resource's end.
-//  * K advances in tiles of BK (32 or 64) through NSTAGE LDS stages; the
-//    loads of a tile are issued NSTAGE-1 tiles before it is consumed.  One
-//    barrier per tile; the wait before it names an exact outstanding-load
-//    count so the loads of later tiles stay in flight across it, and it sits
+//  * K advances in tiles of BK = 64 through two LDS stages; the loads of tile
+//    t+1 are in flight while tile t is consumed.  One barrier per tile, placed
 //    before the tile's last 16-deep k step so that the next tile's first
-//    fragments are read from LDS while that step's MFMAs execute.  The
-//    configuration used for large problems is BK = 64 with 2 stages (one
-//    barrier per 64 k, prefetch one tile ahead), which measured faster than
-//    BK = 32 with 3 or 4 stages on gfx950.
+//    fragments are read from LDS while that step's MFMAs execute.  BK = 64
+//    with two stages measured faster than BK = 32 with three or four (fewer
+//    barriers), and an explicit L2 warm-up of the tile after next did not
+//    help: the loop is limited by the CU's LDS and vector-memory pipelines,
+//    not by load latency.
+//  * The waves split into two halves, one wave of each on every SIMD; the
+//    halves issue their share of a tile's loads one k step apart, so that on
+//    every SIMD one wave can issue MFMAs while the other is handing loads to
+//    the memory pipeline (measured 3-4% over issuing all loads at once).
 //  * K-contiguous operands live in LDS as [rows][BK] with the 16-byte chunks
 //    of a row XOR-swizzled by the row index (conflict-free 128-bit fragment
 //    reads).  M/N-contiguous operands (weights stored [K,N], the
@@ -26,7 +29,7 @@
 //    transposing LDS read): no transposition ever goes through registers.
 //  * v_mfma_f32_32x32x16_bf16 with the B fragment as first operand, so a
 //    lane's accumulators are four consecutive output columns (8- or 16-byte
-//    stores).
+//    stores).  Accumulators stay in arch VGPRs (the AGPR form measured slower).
 //  * The blockIdx -> tile map is the XCD-aware grouped map of gemm_common.hpp.
 #pragma once
 
@@ -177,7 +180,7 @@ __device__ __forceinline__ bf16x8 fragment(const lds_u8* tile, int tr, int kk) {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NSTAGE, int AL, int BL, class Epi>
+template <int BM, int BN, int WGM, int WGN, int BK, int AL, int BL, class Epi>
 __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem p, Epi epi) {
   constexpr int NW = WGM * WGN;
   constexpr int NB = Epi::NB;
@@ -186,6 +189,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem
   static_assert(TM >= 1 && TN >= 1, "wave sub-tile must hold whole 32x32 MFMA tiles");
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   constexpr int STAGE = A_BYTES + NB * B_BYTES;
+  constexpr int NSTAGE = 2, KK = BK / 16;
+  static_assert(KK >= 3 && NW % 2 == 0, "staggered issue needs at least three k steps and paired waves");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
 
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
@@ -212,8 +217,6 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem
   // every K segment shares the leading dimensions of segment 0 (host contract)
   la.init(m0, (uint32_t)p.lda[0] * 2u, p.M);
   lb.init(n0, (uint32_t)p.ldb[0] * 2u, p.N);
-  constexpr int LPT = DmaLoader<BM, AL, NW, BK>::PER + NB * DmaLoader<BN, BL, NW, BK>::PER;  // loads per wave per tile
-  static_assert(LPT * (NSTAGE - 2) < 64 && NSTAGE >= 2 && NSTAGE <= 4, "vmcnt range / stage count");
 
   const int nk0 = (p.K[0] + BK - 1) / BK;
   const int nk = nk0 + (p.nseg > 1 ? (p.K[1] + BK - 1) / BK : 0);
@@ -256,41 +259,35 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem
         for (int j = 0; j < TN; ++j)
           acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.b[b][j], F.a[i], acc[b][i][j], 0, 0, 0);
   };
-  // Wait until tile t has landed in LDS for every wave (at most `ahead`
-  // later tiles still in flight), with this wave's LDS reads drained.
-  auto sync_tile = [&](int t) {
-    const int ahead = min(nk - 1, t + NSTAGE - 2) - t;
-    if (ahead >= 2)
-      wait_vmcnt<2 * LPT>();
-    else if (ahead == 1)
-      wait_vmcnt<LPT>();
-    else
-      wait_vmcnt<0>();
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  // Waves 0 .. NW/2-1 form half 0, the rest half 1; wave w runs on SIMD w % 4,
+  // so with eight waves every SIMD holds one wave of each half.  Half 0
+  // issues its share of tile t+1 right after the barrier that frees the
+  // stage (one k step before tile t starts), half 1 one k step into tile t.
+  // Each wave waits for its own loads (vmcnt 0) before the next barrier.
+  const int half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / (NW / 2);
+  auto sync_next = [&]() {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
     barrier();
   };
-
-  // Pipeline: tile t's loads are issued NSTAGE-1 tiles ahead; fragments of
-  // k step kk+1 are read while the MFMAs of step kk run, and the barrier that
-  // publishes the next tile sits before the last k step, so the next tile's
-  // first fragments are read while this tile's last MFMAs run.
-#pragma unroll
-  for (int t = 0; t < NSTAGE - 1; ++t)
-    if (t < nk) issue(t);
   Frags F[2];
-  constexpr int KK = BK / 16;
   if (nk > 0) {
-    sync_tile(0);
+    issue(0);
+    sync_next();
+    if (half == 0 && nk > 1) issue(1);
     load_frags(F[0], 0, 0);
   }
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + NSTAGE - 1 < nk) issue(kt + NSTAGE - 1);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       if (kk + 1 < KK) {
+        if (kk == 1 && half == 1 && kt + 1 < nk) issue(kt + 1);
         load_frags(F[(kk + 1) & 1], kt, kk + 1);
       } else if (kt + 1 < nk) {
-        sync_tile(kt + 1);
+        // tile kt+1 has landed and every read of tile kt's stage is done, so
+        // half 0 may refill it with tile kt+2
+        sync_next();
+        if (half == 0 && kt + 2 < nk) issue(kt + 2);
         load_frags(F[(kk + 1) & 1], kt + 1, 0);
       }
       mfmas(F[kk & 1]);
@@ -328,12 +325,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem
 }  // namespace gemm3
 
 // Host-side launcher: grid of ceil(M/BM) * ceil(N/BN) work-groups of 64 * WGM * WGN threads.
-template <int BM, int BN, int WGM, int WGN, int BK, int NSTAGE, int AL, int BL, class Epi>
+template <int BM, int BN, int WGM, int WGN, int BK, int AL, int BL, class Epi>
 hipError_t launch_gemm_dma(const GemmProblem& p, const Epi& epi, hipStream_t stream) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm3::gemm_dma_kernel<BM, BN, WGM, WGN, BK, NSTAGE, AL, BL, Epi>), dim3(tiles), dim3(64 * WGM * WGN), 0,
-                     stream, p, epi);
+  hipLaunchKernelGGL((gemm3::gemm_dma_kernel<BM, BN, WGM, WGN, BK, AL, BL, Epi>), dim3(tiles),
+                     dim3(64 * WGM * WGN), 0, stream, p, epi);
   return hipGetLastError();
 }
 

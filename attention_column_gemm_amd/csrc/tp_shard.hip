@@ -98,12 +98,12 @@ template <int AL, int BL, class Epi>
 hipError_t gemm_bf16(const GemmProblem& p, const Epi& epi, hipStream_t st) {
   if constexpr (Epi::NB == 1) {
     Probe pr(st);
-    if (use_small_tile(p.M, p.N, 256, 256)) return launch_gemm_dma<128, 128, 2, 2, 64, 2, AL, BL>(p, epi, st);
-    return launch_gemm_dma<256, 256, 4, 2, 64, 2, AL, BL>(p, epi, st);
+    if (use_small_tile(p.M, p.N, 256, 256)) return launch_gemm_dma<128, 128, 2, 2, 64, AL, BL>(p, epi, st);
+    return launch_gemm_dma<256, 256, 4, 2, 64, AL, BL>(p, epi, st);
   } else {
     Probe pr(st);
-    if (use_small_tile(p.M, p.N, 256, 128)) return launch_gemm_dma<128, 64, 2, 2, 64, 2, AL, BL>(p, epi, st);
-    return launch_gemm_dma<256, 128, 4, 2, 64, 2, AL, BL>(p, epi, st);
+    if (use_small_tile(p.M, p.N, 256, 128)) return launch_gemm_dma<128, 64, 2, 2, 64, AL, BL>(p, epi, st);
+    return launch_gemm_dma<256, 128, 4, 2, 64, AL, BL>(p, epi, st);
   }
 }
 
