@@ -29,7 +29,8 @@ Modules:
 * :mod:`oracle.dropout`     - the counter-based dropout mask.
 * :mod:`oracle.mlp`         - unsharded and per-shard MLP forward/backward,
                               and the emulated all-reduce (sum of partials).
-* :mod:`oracle.attention`   - causal GQA attention, unsharded and per shard.
+* :mod:`oracle.attention`   - causal GQA attention, unsharded and per shard,
+                              forward and backward.
 * :mod:`oracle.comm`        - all-reduce count and bytes per layer.
 * :mod:`oracle.flops`       - algorithmic FLOP counts.
 

@@ -1,4 +1,4 @@
-"""Causal grouped-query self-attention, unsharded and per TP rank (forward).
+"""Causal grouped-query self-attention, unsharded and per TP rank, forward and backward.
 
 Test infrastructure (see ``oracle``).  All arithmetic in float64.
 
@@ -121,3 +121,85 @@ def shard_forward_rows(X, Wqkv_i, Wo_i, rows, *, b, s, q, kv, d):
             O[n, j * d:(j + 1) * d] = (e @ v) / e.sum()
             lse[j, n] = m + np.log(e.sum())
     return dict(O=O, lse=lse, Z=O @ _f64(Wo_i))
+
+
+def core_backward(Q, K, V, dO, *, b, s, n_q, n_kv, d, causal=True):
+    """Gradients of the attention core with respect to ``Q, K, V``.
+
+    [HJ] Attention, single-card backward: with ``P`` the row softmax of the
+    scaled, masked scores, ``dV = P^T dO`` and ``dP = dO V^T``; the softmax
+    backward of a row ``y = softmax(x)`` is ``dx = y * (dy - <dy, y>)``, so
+    ``dS = P * (dP - rowsum(P * dP))``; then ``dQ = dS K / sqrt(d)`` and
+    ``dK = dS^T Q / sqrt(d)``.  [LP] I.O: the scores are recomputed here, not
+    stored.  With grouped-query attention the gradients of a KV head add up
+    over the query heads that read it (the chain rule through the shared use).
+    Returns ``dQ [T, n_q d]``, ``dK, dV [T, n_kv d]``.
+    """
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    if n_q % n_kv:
+        raise ValueError("n_q must divide by n_kv")
+    group = n_q // n_kv
+    T = b * s
+    dQ = np.zeros((T, n_q * d))
+    dK = np.zeros((T, n_kv * d))
+    dV = np.zeros((T, n_kv * d))
+    scale = 1.0 / np.sqrt(d)
+    allowed = np.tril(np.ones((s, s), dtype=bool)) if causal else np.ones((s, s), dtype=bool)
+    for beta in range(b):
+        rows = slice(beta * s, (beta + 1) * s)
+        for j in range(n_q):
+            g = j // group
+            q = Q[rows, j * d:(j + 1) * d]
+            k = K[rows, g * d:(g + 1) * d]
+            v = V[rows, g * d:(g + 1) * d]
+            do = dO[rows, j * d:(j + 1) * d]
+            S = np.where(allowed, (q @ k.T) * scale, -np.inf)
+            E = np.exp(S - S.max(axis=1, keepdims=True))
+            P = E / E.sum(axis=1, keepdims=True)
+            dP = do @ v.T
+            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dQ[rows, j * d:(j + 1) * d] = (dS @ k) * scale
+            dK[rows, g * d:(g + 1) * d] += (dS.T @ q) * scale
+            dV[rows, g * d:(g + 1) * d] += P.T @ do
+    return dQ, dK, dV
+
+
+def backward(dZ, X, Wq, Wk, Wv, Wo, *, b, s, n_q, n_kv, d, causal=True):
+    """Unsharded attention sublayer backward for the upstream gradient ``dZ``.
+
+    [HJ] Attention, single-card backward, in its order: ``dWo = O^T dZ``,
+    ``dO = dZ Wo^T``; the core's ``dQ, dK, dV``; then the projection weights
+    ``dWq = X^T dQ`` (likewise K, V) and the input gradient
+    ``dX = dQ Wq^T + dK Wk^T + dV Wv^T``.
+    """
+    X, dZ = _f64(X), _f64(dZ)
+    Wq, Wk, Wv, Wo = _f64(Wq), _f64(Wk), _f64(Wv), _f64(Wo)
+    f = forward(X, Wq, Wk, Wv, Wo, b=b, s=s, n_q=n_q, n_kv=n_kv, d=d, causal=causal)
+    dWo = f["O"].T @ dZ
+    dO = dZ @ Wo.T
+    dQ, dK, dV = core_backward(f["Q"], f["K"], f["V"], dO, b=b, s=s, n_q=n_q, n_kv=n_kv, d=d, causal=causal)
+    return dict(dO=dO, dQ=dQ, dK=dK, dV=dV, dWq=X.T @ dQ, dWk=X.T @ dK, dWv=X.T @ dV, dWo=dWo,
+                dX=dQ @ Wq.T + dK @ Wk.T + dV @ Wv.T)
+
+
+def shard_backward(dZ, X, Wqkv_i, Wo_i, *, b, s, q, kv, d, causal=True):
+    """One rank's attention backward.
+
+    The upstream gradient ``dZ`` of the sublayer output is the same on every
+    rank (the backward of the forward all-reduce is the identity; [TP1]
+    operators f and g).  The rank forms ``dWo_i = O_i^T dZ`` and
+    ``dO_i = dZ Wo_i^T`` for its heads, its heads' ``dQ, dK, dV`` packed like
+    ``QKV_i`` (``[Q heads | K heads | V heads]``), ``dWqkv_i = X^T dQKV_i`` and
+    the partial input gradient ``dX_i = dQKV_i Wqkv_i^T``, which the backward
+    all-reduce at the QKV input sums over ranks ([TP1], attention's
+    communication; [L11] section 4).
+    """
+    X, dZ, Wqkv_i, Wo_i = _f64(X), _f64(dZ), _f64(Wqkv_i), _f64(Wo_i)
+    f = shard_forward(X, Wqkv_i, Wo_i, b=b, s=s, q=q, kv=kv, d=d, causal=causal)
+    QKV = f["QKV"]
+    dO = dZ @ Wo_i.T
+    dQ, dK, dV = core_backward(QKV[:, :q * d], QKV[:, q * d:(q + kv) * d], QKV[:, (q + kv) * d:], dO,
+                               b=b, s=s, n_q=q, n_kv=kv, d=d, causal=causal)
+    dQKV = np.concatenate([dQ, dK, dV], axis=1)
+    return dict(QKV=QKV, O=f["O"], lse=f["lse"], dO=dO, dQKV=dQKV, dWo=f["O"].T @ dZ,
+                dWqkv=X.T @ dQKV, dX=dQKV @ Wqkv_i.T)

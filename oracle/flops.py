@@ -5,7 +5,10 @@ neglects the activation, dropout and the all-reduce's additions (MLP,
 single-card forward and backward; TP forward).  Its totals for a GeLU MLP
 with ``d_ff = 4 d``: forward ``16 B S d^2``, backward twice that, and ``1/n``
 of each per rank under ``n``-way TP.  For attention (MHA, no causal saving):
-forward ``8 B S d^2 + 4 B S^2 d``, backward twice that.
+forward ``8 B S d^2 + 4 B S^2 d``, backward ``16 B S d^2 + 8 B S^2 d``
+(Attention, single-card backward): every projection GEMM and both core
+products get an input-gradient and a weight-gradient (or second-operand)
+product; recomputing the scores is not counted.
 """
 
 
@@ -35,3 +38,12 @@ def attention_shard_fwd(b: int, s: int, h: int, q: int, kv: int, d: int, causal:
     core = 2 * (2 * d) * b * q * pairs
     out = gemm(T, q * d, h)
     return dict(qkv=qkv, core=core, out=out, total=qkv + core + out)
+
+
+def attention_shard_bwd(b: int, s: int, h: int, q: int, kv: int, d: int, causal: bool = True) -> dict:
+    """Per-rank backward FLOPs: twice each forward term ([HJ] Attention,
+    single-card backward) -- ``dWo`` and ``dO`` for the output projection,
+    ``dP``/``dV`` and ``dQ``/``dK`` for the core over the computed pairs,
+    ``dWqkv`` and ``dX`` for the QKV projection."""
+    f = attention_shard_fwd(b, s, h, q, kv, d, causal)
+    return dict(qkv=2 * f["qkv"], core=2 * f["core"], out=2 * f["out"], total=2 * f["total"])

@@ -401,6 +401,95 @@ def test_attention_sum_over_ranks_equals_unsharded():
     np.testing.assert_allclose(Z, full["Z"], rtol=1e-12, atol=1e-13)
 
 
+def _attn_case(seed, b=2, s=4, h=6, n_q=4, n_kv=2, d=3):
+    g = _rng(seed)
+    X = g.standard_normal((b * s, h))
+    Wq, Wk, Wv = (g.standard_normal((h, n * d)) / 2 for n in (n_q, n_kv, n_kv))
+    Wo = g.standard_normal((n_q * d, h)) / 2
+    dZ = g.standard_normal((b * s, h))
+    return dict(X=X, Wq=Wq, Wk=Wk, Wv=Wv, Wo=Wo, dZ=dZ, b=b, s=s, n_q=n_q, n_kv=n_kv, d=d)
+
+
+def test_attention_backward_central_differences():
+    """Every gradient of L = <dZ, Z> against central differences (GQA, causal, two sequences)."""
+    c = _attn_case(21)
+    kw = dict(b=c["b"], s=c["s"], n_q=c["n_q"], n_kv=c["n_kv"], d=c["d"])
+    got = att.backward(c["dZ"], c["X"], c["Wq"], c["Wk"], c["Wv"], c["Wo"], **kw)
+    names = ["X", "Wq", "Wk", "Wv", "Wo"]
+
+    def loss():
+        return float((att.forward(*(c[n] for n in names), **kw)["Z"] * c["dZ"]).sum())
+
+    eps = 1e-6
+    for n in names:
+        arr = c[n]
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            keep = arr[idx]
+            arr[idx] = keep + eps
+            lp = loss()
+            arr[idx] = keep - eps
+            lm = loss()
+            arr[idx] = keep
+            num[idx] = (lp - lm) / (2 * eps)
+        g = got["d" + n]
+        assert np.abs(num - g).max() <= 1e-6 * np.abs(g).max(), n
+
+
+def test_attention_backward_closed_forms():
+    g = _rng(22)
+    b, s, n_q, n_kv, d = 2, 6, 4, 2, 5
+    group = n_q // n_kv
+    K = g.standard_normal((b * s, n_kv * d))
+    V = g.standard_normal((b * s, n_kv * d))
+    dO = g.standard_normal((b * s, n_q * d))
+    # Q = 0: every visible key has weight 1/(i+1), so dV[k] = sum over the group's heads and over
+    # queries i >= k of dO[i] / (i+1), and dK = dS^T Q / sqrt(d) = 0.
+    dQ, dK, dV = att.core_backward(np.zeros((b * s, n_q * d)), K, V, dO, b=b, s=s, n_q=n_q, n_kv=n_kv, d=d)
+    np.testing.assert_allclose(dK, 0.0, atol=1e-15)
+    for beta in range(b):
+        for gh in range(n_kv):
+            want = np.zeros((s, d))
+            for j in range(gh * group, (gh + 1) * group):
+                do = dO[beta * s:(beta + 1) * s, j * d:(j + 1) * d]
+                w = do / np.arange(1, s + 1)[:, None]
+                want += np.cumsum(w[::-1], 0)[::-1]
+            np.testing.assert_allclose(dV[beta * s:(beta + 1) * s, gh * d:(gh + 1) * d], want, atol=1e-13)
+    # s = 1: one visible key with weight 1 -> dS = 0, so dQ = dK = 0 and dV = the group's summed dO
+    Q1 = g.standard_normal((3, n_q * d))
+    dQ1, dK1, dV1 = att.core_backward(Q1, K[:3], V[:3], dO[:3], b=3, s=1, n_q=n_q, n_kv=n_kv, d=d)
+    np.testing.assert_allclose(dQ1, 0.0, atol=1e-15)
+    np.testing.assert_allclose(dK1, 0.0, atol=1e-15)
+    for gh in range(n_kv):
+        want = sum(dO[:3, j * d:(j + 1) * d] for j in range(gh * group, (gh + 1) * group))
+        np.testing.assert_allclose(dV1[:, gh * d:(gh + 1) * d], want, atol=1e-15)
+
+
+def test_attention_backward_shards_match_unsharded():
+    """Rank i's dWqkv_i holds the unsharded dWq/dWk/dWv columns of its heads, dWo_i the
+    unsharded dWo rows of its heads, and the backward all-reduce of dX_i gives dX
+    ([TP1] operators f and g; [L11] section 4)."""
+    g = _rng(23)
+    b, s, h, n_q, n_kv, d, t = 2, 5, 12, 8, 4, 3, 2
+    X = g.standard_normal((b * s, h))
+    Wq, Wk, Wv = (g.standard_normal((h, n * d)) / 3 for n in (n_q, n_kv, n_kv))
+    Wo = g.standard_normal((n_q * d, h)) / 3
+    dZ = g.standard_normal((b * s, h))
+    full = att.backward(dZ, X, Wq, Wk, Wv, Wo, b=b, s=s, n_q=n_q, n_kv=n_kv, d=d)
+    q, kv = n_q // t, n_kv // t
+    dX = np.zeros_like(full["dX"])
+    for i in range(t):
+        cq, ckv = slice(i * q * d, (i + 1) * q * d), slice(i * kv * d, (i + 1) * kv * d)
+        Wqkv = np.concatenate([Wq[:, cq], Wk[:, ckv], Wv[:, ckv]], 1)
+        sh = att.shard_backward(dZ, X, Wqkv, Wo[cq], b=b, s=s, q=q, kv=kv, d=d)
+        want = np.concatenate([full["dWq"][:, cq], full["dWk"][:, ckv], full["dWv"][:, ckv]], 1)
+        np.testing.assert_allclose(sh["dWqkv"], want, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(sh["dWo"], full["dWo"][cq], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(sh["dO"], full["dO"][:, cq], rtol=1e-12, atol=1e-12)
+        dX += sh["dX"]
+    np.testing.assert_allclose(dX, full["dX"], rtol=1e-11, atol=1e-12)
+
+
 # ---------------------------------------------------------------------- comm
 
 def _ring_allreduce_bytes(t, n_per_chunk, delta, seed=0):
@@ -466,3 +555,5 @@ def test_flops_match_page_totals():
     heads, dh = 2, d // 2
     a = flops.attention_shard_fwd(B, S, d, heads, heads, dh, causal=False)
     assert a["total"] == 8 * B * S * d * d + 4 * B * S * S * d
+    ab = flops.attention_shard_bwd(B, S, d, heads, heads, dh, causal=False)
+    assert ab["total"] == 16 * B * S * d * d + 8 * B * S * S * d
