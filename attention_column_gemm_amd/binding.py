@@ -63,13 +63,15 @@ def lib() -> ctypes.CDLL:
         L.tp_mlp_shard_bwd.argtypes = ([ctypes.POINTER(tp_mlp_desc), _VP, ctypes.c_float, ctypes.c_uint64]
                                        + [_VP] * 6 + [_VP, _VP, _VP, _VP, _VP, _VP, _VP] + [_VP])
         L.tp_attn_shard_fwd.argtypes = [ctypes.POINTER(tp_attn_desc)] + [_VP] * 7 + [_VP]
+        L.tp_attn_shard_bwd.argtypes = [ctypes.POINTER(tp_attn_desc)] + [_VP] * 13 + [_VP]
         L.tp_sum_partials.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.POINTER(_VP), _VP, ctypes.c_float, ctypes.c_uint64, _VP, _VP]
         L.tp_comm_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.POINTER(tp_comm)]
         L.tp_status_string.argtypes = [ctypes.c_int]
         L.tp_status_string.restype = ctypes.c_char_p
-        for name in ("tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_attn_shard_fwd", "tp_sum_partials", "tp_comm_bytes"):
+        for name in ("tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_attn_shard_fwd", "tp_attn_shard_bwd",
+                     "tp_sum_partials", "tp_comm_bytes"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -128,6 +130,13 @@ def tp_mlp_shard_bwd(desc: tp_mlp_desc, dOut, p_drop: float, seed: int, X, W1_i,
 def tp_attn_shard_fwd(desc: tp_attn_desc, X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, Z_i, stream=None):
     _check(lib().tp_attn_shard_fwd(ctypes.byref(desc), _ptr(X), _ptr(Wqkv_i), _ptr(Wo_i), _ptr(QKV_i), _ptr(O_i),
                                    _ptr(lse_i), _ptr(Z_i), _stream(stream)), "tp_attn_shard_fwd")
+
+
+def tp_attn_shard_bwd(desc: tp_attn_desc, dZ, X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, dO_i, stats_i, dQKV_i, dWqkv_i,
+                      dWo_i, dX_i, stream=None):
+    _check(lib().tp_attn_shard_bwd(ctypes.byref(desc), _ptr(dZ), _ptr(X), _ptr(Wqkv_i), _ptr(Wo_i), _ptr(QKV_i),
+                                   _ptr(O_i), _ptr(lse_i), _ptr(dO_i), _ptr(stats_i), _ptr(dQKV_i), _ptr(dWqkv_i),
+                                   _ptr(dWo_i), _ptr(dX_i), _stream(stream)), "tp_attn_shard_bwd")
 
 
 def tp_sum_partials(rows: int, cols: int, t: int, dtype: int, partials, bias, p_drop: float, seed: int, out,

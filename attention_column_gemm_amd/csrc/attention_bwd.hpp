@@ -1,0 +1,473 @@
+// Causal grouped-query attention backward of one TP rank's local heads, on
+// the gfx950 matrix cores, flash style.
+//
+// What it computes ([HJ] hjcheng0602.cn "tensorparallel/tp", Attention,
+// single-card backward; [LP] "ラブパラ" I.O on recomputing the scores in the
+// backward pass): per sequence and local query head j with KV head
+// g = j / (q/kv), scale c = 1/sqrt(d), P = softmax(c Q K^T + causal mask),
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - Delta),  Delta_i = rowsum(dO * O)_i,
+//   dQ = c dS K,  dK = c dS^T Q,
+// with the KV gradients summed over the query heads of the group.  P is
+// recomputed from the forward's per-row log-sum-exp; Delta_i equals
+// rowsum(P * dP)_i because O = P V.
+//
+// Three kernels:
+//  * stats: per (sequence, head, row) the pair {lse * log2(e), Delta}.
+//  * dK/dV: a work-group owns 32 keys of one KV head; its four waves take
+//    every fourth (query head, 32-row query tile) item of the causal range,
+//    each wave streaming its own Q and dO tiles into LDS with LDS-direct
+//    loads (double buffered), and the four waves' partial sums are added in a
+//    fixed order through LDS at the end (deterministic, no atomics).
+//  * dQ: the forward's layout (waves own 32 query rows; the work-group shares
+//    64-key K and V blocks in LDS).
+// Operand layouts: with v_mfma_f32_32x32x16_bf16 computing C[i][j] += sum_k
+// X[i][k] Y[j][k], lane l holding column j = l % 32 of C, the score tile is
+// formed so that the lane's column is the index the next product keeps
+// (keys for dK/dV, queries for dQ) and the contracted index lies in its
+// registers; those registers are used directly as the Y operand of the
+// next product, in a permuted k order, and the matching X operand (Q^T,
+// dO^T or K^T) is read with ds_read_b64_tr_b16 from the row-major LDS tile
+// in that same order, so no tile is ever stored transposed.
+#pragma once
+
+#include "common.hpp"
+#include "lds_dma.hpp"
+
+namespace tp {
+namespace attnb {
+
+using lds::lds_u8;
+using lds::v4i16;
+
+constexpr int NTHREADS = 256;
+constexpr int KEY_BLOCK = 32;   // keys per dK/dV work-group
+constexpr int Q_TILE = 32;      // query rows per dK/dV item
+constexpr int DQ_KEYS = 64;     // keys per dQ block
+
+struct BwdArgs {
+  const uint16_t* qkv;  // [T, (q + 2kv) d] forward projections
+  const uint16_t* o;    // [T, q d] forward output
+  const uint16_t* dO;   // [T, q d] gradient of O
+  const float* lse;     // [b, q, s] forward log-sum-exp (natural log)
+  float* stats;         // [b, q, s, 2] {lse * log2(e), Delta}
+  uint16_t* dqkv;       // [T, (q + 2kv) d]
+  int64_t ld_qkv, ld_o;
+  int b, s, q, kv;
+  int causal;
+  float scale;       // 1 / sqrt(d)
+  float scale_log2;  // log2(e) / sqrt(d)
+};
+
+// 16-byte chunk permutation of a row-major [rows][D] bf16 tile: logical chunk
+// c of row r sits at chunk c ^ swz(r).  Sixteen consecutive rows at one
+// logical chunk (a 128-bit fragment read) and four consecutive rows at one
+// aligned chunk pair (a transposing read) both land on distinct banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+  return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);  // D = 64: row parity picks the bank half
+}
+template <int D>
+__device__ __forceinline__ uint32_t tile_off(int r, int c) {
+  return (uint32_t)(r * D * 2 + ((c ^ swz<D>(r)) << 4));
+}
+
+// 16-byte row fragment (rows r0 + lane%32, k step kk) of a row-major tile.
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const lds_u8* tile, int r0, int kk) {
+  const int lane = threadIdx.x & 63;
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+      tile + tile_off<D>(r0 + (lane & 31), kk * 2 + (lane >> 5)));
+}
+
+// Transposed fragment of a row-major tile T[row][col]: lane l gets column
+// 32 dt + l % 32 at the eight rows that the registers 8 jj .. 8 jj + 7 of a
+// 32x32 accumulator hold for its half h = l / 32, i.e. rows
+// r0 + 16 jj + 4 h + {0..3} and r0 + 16 jj + 8 + 4 h + {0..3}.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const lds_u8* tile, int r0, int dt, int jj) {
+  const int lane = threadIdx.x & 63;
+  const int g4 = lane >> 4, R = lane & 15, h = lane >> 5;
+  const int col = 32 * dt + 16 * (g4 & 1) + 4 * (R & 3);
+  v4i16 part[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int row = r0 + 16 * jj + 4 * h + 8 * half + (R >> 2);
+    part[half] = lds::read_tr16(tile, tile_off<D>(row, col >> 3) + (col & 7) * 2);
+  }
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  v8i16 v = {part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// LDS-direct load of rows [row0, row0 + ROWS) x D bf16 columns starting at
+// byte column col_bytes of a row-major matrix (ld_bytes per row, nrows rows,
+// behind `rsrc`) into a swizzled [ROWS][D] tile at LDS byte address dst.
+// This wave issues the tile's 1 KiB instructions i0, i0 + step, ...
+template <int D, int ROWS>
+__device__ __forceinline__ void dma_tile(const u32x4& rsrc, uint32_t ld_bytes, int row0, int nrows,
+                                         uint32_t col_bytes, uint32_t dst, int i0, int step) {
+  constexpr int NI = ROWS * D * 2 / 1024;
+  const int lane = threadIdx.x & 63;
+  for (int i = i0; i < NI; i += step) {
+    const int o = i * 1024 + 16 * lane;
+    const int r = o / (2 * D), pos = (o % (2 * D)) >> 4;
+    const int c = pos ^ swz<D>(r);
+    const uint32_t voff =
+        row0 + r < nrows ? (uint32_t)(row0 + r) * ld_bytes + col_bytes + (uint32_t)c * 16u : kOOB;
+    lds::dma16(rsrc, voff, dst + (uint32_t)i * 1024u);
+  }
+}
+
+// One 4-byte load per lane from `rsrc` at `voff` into LDS at m0 + 4 * lane.
+__device__ __forceinline__ void dma4(const u32x4& rsrc, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float* v) {
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// ---- stats -------------------------------------------------------------------
+// Row r = (beta q + j) s + i: stats[2r] = lse * log2(e), stats[2r+1] = Delta.
+// D/8 lanes per row, eight elements each, folded with cross-lane adds.
+template <int D>
+__global__ void __launch_bounds__(NTHREADS) attn_bwd_stats_kernel(BwdArgs a, int64_t nrows) {
+  constexpr int LPR = D / 8;
+  const int64_t r = (int64_t)blockIdx.x * (NTHREADS / LPR) + threadIdx.x / LPR;
+  const int sub = threadIdx.x % LPR;
+  float acc = 0.0f;
+  int64_t beta = 0, j = 0, i = 0;
+  if (r < nrows) {
+    i = r % a.s;
+    j = (r / a.s) % a.q;
+    beta = r / ((int64_t)a.s * a.q);
+    const int64_t off = (beta * a.s + i) * a.ld_o + j * D + sub * 8;
+    float x[8], y[8];
+    Elem<uint16_t>::load4(a.dO + off, *reinterpret_cast<float(*)[4]>(x));
+    Elem<uint16_t>::load4(a.dO + off + 4, *reinterpret_cast<float(*)[4]>(x + 4));
+    Elem<uint16_t>::load4(a.o + off, *reinterpret_cast<float(*)[4]>(y));
+    Elem<uint16_t>::load4(a.o + off + 4, *reinterpret_cast<float(*)[4]>(y + 4));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += x[e] * y[e];
+  }
+#pragma unroll
+  for (int m = LPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m);
+  if (r < nrows && sub == 0) {
+    a.stats[2 * r] = a.lse[r] * 1.4426950408889634f;
+    a.stats[2 * r + 1] = acc;
+  }
+}
+
+// ---- dK, dV ----------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(NTHREADS, 1) attn_bwd_dkv_kernel(BwdArgs a) {
+  constexpr int DT = D / 32, KK = D / 16;
+  constexpr int TILE = Q_TILE * D * 2;   // one 32-row tile
+  constexpr int TI = TILE / 1024;        // its LDS-direct instructions
+  constexpr int STAGE = 2 * TILE + 256;  // Q tile, dO tile, 32 x {lse2, Delta}
+  constexpr int WAVE_LDS = 2 * STAGE;
+  static_assert(4 * 2 * DT * 16 * 64 * 4 <= 4 * WAVE_LDS, "reduction space");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * WAVE_LDS];
+  const lds_u8* lds = (const lds_u8*)smem;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+  const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kb = blockIdx.x, k0 = kb * KEY_BLOCK;
+  const int beta = blockIdx.y / a.kv, g = blockIdx.y % a.kv;
+  const int group = a.q / a.kv;
+  const int64_t tok0 = (int64_t)beta * a.s;
+  const uint32_t ldq = (uint32_t)a.ld_qkv * 2u, ldo = (uint32_t)a.ld_o * 2u;
+
+  // this block's keys and values as MFMA operands (zeros past the sequence)
+  bf16x8 kf[KK], vf[KK];
+  {
+    const rsrc_t seq = make_rsrc(a.qkv + tok0 * a.ld_qkv, (uint32_t)a.s * ldq);
+    const int key = k0 + l32;
+    const uint32_t kc = (uint32_t)(a.q + g) * D * 2u, vc = (uint32_t)(a.q + a.kv + g) * D * 2u;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const uint32_t base = (uint32_t)key * ldq + (uint32_t)(16 * kk + 8 * h) * 2u;
+      kf[kk] = __builtin_bit_cast(bf16x8, buf_load16(seq, key < a.s ? base + kc : kOOB));
+      vf[kk] = __builtin_bit_cast(bf16x8, buf_load16(seq, key < a.s ? base + vc : kOOB));
+    }
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): keep these out of the tile pipeline's counts
+
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dk[t][e] = dv[t][e] = 0.0f;
+
+  const int nqt = (a.s + Q_TILE - 1) / Q_TILE;
+  const int qt0 = a.causal ? (k0 / Q_TILE) : 0;
+  const int ntile = nqt - qt0;
+  const int nitems = group * ntile;
+  const u32x4 rq = lds::sgpr_rsrc(a.qkv + tok0 * a.ld_qkv, (uint32_t)a.s * ldq);
+  const u32x4 rdo = lds::sgpr_rsrc(a.dO + tok0 * a.ld_o, (uint32_t)a.s * ldo);
+  const u32x4 rst = lds::sgpr_rsrc(a.stats + (int64_t)beta * a.q * a.s * 2, (uint32_t)a.q * a.s * 8u);
+  const uint32_t wl = lds_base + (uint32_t)wave * WAVE_LDS;
+
+  auto item = [&](int n, int& j, int& i0) {
+    j = g * group + n / ntile;
+    i0 = (qt0 + n % ntile) * Q_TILE;
+  };
+  auto issue = [&](int n, int st) {
+    int j, i0;
+    item(n, j, i0);
+    const uint32_t dst = wl + (uint32_t)st * STAGE;
+    dma_tile<D, Q_TILE>(rq, ldq, i0, a.s, (uint32_t)j * D * 2u, dst, 0, 1);
+    dma_tile<D, Q_TILE>(rdo, ldo, i0, a.s, (uint32_t)j * D * 2u, dst + TILE, 0, 1);
+    // lanes 2i, 2i+1: the {lse2, Delta} pair of row i0 + i
+    const int row = i0 + (lane >> 1);
+    dma4(rst, row < a.s ? ((uint32_t)j * a.s + row) * 8u + (lane & 1) * 4u : kOOB, dst + 2 * TILE);
+  };
+
+  if (wave < nitems) issue(wave, 0);
+  int it = 0;
+  for (int n = wave; n < nitems; n += 4, ++it) {
+    const int st = it & 1;
+    lds::wait_lgkm0();  // this wave's reads of the other stage are done
+    if (n + 4 < nitems) {
+      issue(n + 4, st ^ 1);
+      lds::wait_vmcnt<2 * TI + 1>();
+    } else {
+      lds::wait_vmcnt<0>();
+    }
+    int j, i0;
+    item(n, j, i0);
+    const lds_u8* tq = lds + (wave * WAVE_LDS + st * STAGE);
+    const lds_u8* tdo = tq + TILE;
+    const lds_u8* tst = tq + 2 * TILE;
+
+    // S = Q K^T and dP = dO V^T for 32 queries x 32 keys: lane = key, registers = queries
+    f32x16 sacc, pacc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[e] = pacc[e] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(tq, 0, kk), kf[kk], sacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(tdo, 0, kk), vf[kk], pacc, 0, 0, 0);
+    }
+    // P = exp2(S c log2e - lse2), dS = P (dP - Delta); register r holds query 8(r/4) + 4h + r%4
+    const int key = k0 + l32;
+    float p[16], ds[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int ir = 8 * q4 + 4 * h;  // first of this group's four queries within the tile
+      const f32x4 s0 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(tst + ir * 8);
+      const f32x4 s1 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(tst + ir * 8 + 16);
+      const float lse2[4] = {s0.x, s0.z, s1.x, s1.z}, dlt[4] = {s0.y, s0.w, s1.y, s1.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * q4 + e, qi = i0 + ir + e;
+        const bool ok = qi < a.s && (!a.causal || key <= qi);
+        p[r] = ok ? exp2f(sacc[r] * a.scale_log2 - lse2[e]) : 0.0f;
+        ds[r] = p[r] * (pacc[r] - dlt[e]);
+      }
+    }
+    bf16x8 pf[2], df[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      pf[jj] = pack8(p + 8 * jj);
+      df[jj] = pack8(ds + 8 * jj);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS: lane = key, registers = head dims
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(tdo, 0, dt, jj), pf[jj], dv[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(tq, 0, dt, jj), df[jj], dk[dt], 0, 0, 0);
+      }
+  }
+
+  // add the four waves' partial sums in wave order and store
+  lds::wait_vmcnt<0>();
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);  // [wave][2 DT][16][64]
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      red[((wave * 2 * DT + t) * 16 + e) * 64 + lane] = dk[t][e];
+      red[((wave * 2 * DT + DT + t) * 16 + e) * 64 + lane] = dv[t][e];
+    }
+  __syncthreads();
+  const int key = k0 + l32;
+  for (int u = wave; u < 2 * DT; u += 4) {
+    const bool is_k = u < DT;
+    const int dt = is_k ? u : u - DT;
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float x = red[((0 * 2 * DT + u) * 16 + e) * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) x += red[((w * 2 * DT + u) * 16 + e) * 64 + lane];
+      v[e] = is_k ? x * a.scale : x;
+    }
+    if (key < a.s) {
+      uint16_t* dst = a.dqkv + (tok0 + key) * a.ld_qkv + (int64_t)(is_k ? a.q + g : a.q + a.kv + g) * D + 32 * dt;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float w4[4] = {v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]};
+        Elem<uint16_t>::store4(dst + 8 * q4 + 4 * h, w4);
+      }
+    }
+  }
+}
+
+// ---- dQ ----------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(NTHREADS, 1) attn_bwd_dq_kernel(BwdArgs a, int hg) {
+  constexpr int DT = D / 32, KK = D / 16;
+  constexpr int TILE = DQ_KEYS * D * 2;  // one 64-key K or V tile
+  constexpr int TI = TILE / 1024;
+  constexpr int STAGE = 2 * TILE;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  const lds_u8* lds = (const lds_u8*)smem;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+  const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rows_per_wg = 32 * (4 / hg);
+  const int npb = (a.s + rows_per_wg - 1) / rows_per_wg;
+  const int pb = npb - 1 - (int)blockIdx.x;  // latest rows (most keys) first
+  const int group = a.q / a.kv;
+  const int sub_per_kv = group / hg;
+  const int beta = blockIdx.y / (a.kv * sub_per_kv);
+  const int rem = blockIdx.y % (a.kv * sub_per_kv);
+  const int g = rem / sub_per_kv;
+  const int j = g * group + (rem % sub_per_kv) * hg + (wave % hg);
+  const int pos0 = pb * rows_per_wg;
+  const int rp0 = pos0 + (wave / hg) * 32;
+  const int my_row = rp0 + l32;
+  const int64_t tok0 = (int64_t)beta * a.s;
+  const uint32_t ldq = (uint32_t)a.ld_qkv * 2u, ldo = (uint32_t)a.ld_o * 2u;
+
+  // this lane's query row of Q and dO as MFMA operands, and its statistics
+  bf16x8 qf[KK], of[KK];
+  float lse2 = 0.0f, dlt = 0.0f;
+  {
+    const rsrc_t rq = make_rsrc(a.qkv + tok0 * a.ld_qkv, (uint32_t)a.s * ldq);
+    const rsrc_t ro = make_rsrc(a.dO + tok0 * a.ld_o, (uint32_t)a.s * ldo);
+    const bool ok = my_row < a.s;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const uint32_t c = (uint32_t)(j * D + 16 * kk + 8 * h) * 2u;
+      qf[kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, ok ? (uint32_t)my_row * ldq + c : kOOB));
+      of[kk] = __builtin_bit_cast(bf16x8, buf_load16(ro, ok ? (uint32_t)my_row * ldo + c : kOOB));
+    }
+    if (ok) {
+      const int64_t r = ((int64_t)beta * a.q + j) * a.s + my_row;
+      lse2 = a.stats[2 * r];
+      dlt = a.stats[2 * r + 1];
+    }
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+
+  f32x16 dq[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dq[t][e] = 0.0f;
+
+  const int kv_end = a.causal ? min(a.s, pos0 + rows_per_wg) : a.s;
+  const int nkb = (kv_end + DQ_KEYS - 1) / DQ_KEYS;
+  const u32x4 rkv = lds::sgpr_rsrc(a.qkv + tok0 * a.ld_qkv, (uint32_t)a.s * ldq);
+  const uint32_t kcol = (uint32_t)(a.q + g) * D * 2u, vcol = (uint32_t)(a.q + a.kv + g) * D * 2u;
+  auto issue = [&](int kb, int st) {
+    const uint32_t dst = lds_base + (uint32_t)st * STAGE;
+    dma_tile<D, DQ_KEYS>(rkv, ldq, kb * DQ_KEYS, a.s, kcol, dst, wave, 4);
+    dma_tile<D, DQ_KEYS>(rkv, ldq, kb * DQ_KEYS, a.s, vcol, dst + TILE, wave, 4);
+  };
+  if (nkb > 0) issue(0, 0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int st = kb & 1;
+    lds::wait_vmcnt<0>();
+    lds::wait_lgkm0();
+    lds::barrier();  // block kb is in LDS for every wave; every wave is done with block kb-1
+    if (kb + 1 < nkb) issue(kb + 1, st ^ 1);
+    const int key0 = kb * DQ_KEYS;
+    if (a.causal && key0 > rp0 + 31) continue;
+    const lds_u8* tk = lds + st * STAGE;
+    const lds_u8* tv = tk + TILE;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      // S^T = K Q^T and dP^T = V dO^T: lane = query, registers = keys
+      f32x16 sacc, pacc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[e] = pacc[e] = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(tk, 32 * kt, kk), qf[kk], sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(tv, 32 * kt, kk), of[kk], pacc, 0, 0, 0);
+      }
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * h + (r & 3);
+        const bool ok = key < a.s && (!a.causal || key <= my_row);
+        const float p = ok ? exp2f(sacc[r] * a.scale_log2 - lse2) : 0.0f;
+        ds[r] = p * (pacc[r] - dlt);
+      }
+      const bf16x8 df0 = pack8(ds), df1 = pack8(ds + 8);
+      // dQ^T += K^T dS^T: lane = query, registers = head dims
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(tk, 32 * kt, dt, 0), df0, dq[dt], 0, 0, 0);
+        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(tk, 32 * kt, dt, 1), df1, dq[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  if (my_row < a.s) {
+    uint16_t* dst = a.dqkv + (tok0 + my_row) * a.ld_qkv + (int64_t)j * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float w4[4] = {dq[dt][4 * q4] * a.scale, dq[dt][4 * q4 + 1] * a.scale, dq[dt][4 * q4 + 2] * a.scale,
+                             dq[dt][4 * q4 + 3] * a.scale};
+        Elem<uint16_t>::store4(dst + 32 * dt + 8 * q4 + 4 * h, w4);
+      }
+  }
+}
+
+}  // namespace attnb
+
+template <int D>
+hipError_t launch_attn_bwd_stats(const attnb::BwdArgs& a, hipStream_t stream) {
+  const int64_t nrows = (int64_t)a.b * a.q * a.s;
+  if (nrows == 0) return hipSuccess;
+  constexpr int RPB = attnb::NTHREADS / (D / 8);
+  hipLaunchKernelGGL((attnb::attn_bwd_stats_kernel<D>), dim3((unsigned)((nrows + RPB - 1) / RPB)),
+                     dim3(attnb::NTHREADS), 0, stream, a, nrows);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_attn_bwd_dkv(const attnb::BwdArgs& a, hipStream_t stream) {
+  const int nkb = (a.s + attnb::KEY_BLOCK - 1) / attnb::KEY_BLOCK;
+  if (nkb == 0 || a.b * a.kv == 0) return hipSuccess;
+  hipLaunchKernelGGL((attnb::attn_bwd_dkv_kernel<D>), dim3(nkb, a.b * a.kv), dim3(attnb::NTHREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_attn_bwd_dq(const attnb::BwdArgs& a, int hg, hipStream_t stream) {
+  const int rows_per_wg = 32 * (4 / hg);
+  const int npb = (a.s + rows_per_wg - 1) / rows_per_wg;
+  const int ny = a.b * a.kv * ((a.q / a.kv) / hg);
+  if (npb == 0 || ny == 0) return hipSuccess;
+  hipLaunchKernelGGL((attnb::attn_bwd_dq_kernel<D>), dim3(npb, ny), dim3(attnb::NTHREADS), 0, stream, a, hg);
+  return hipGetLastError();
+}
+
+}  // namespace tp

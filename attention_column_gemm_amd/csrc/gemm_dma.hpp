@@ -35,37 +35,17 @@
 
 #include "common.hpp"
 #include "gemm_common.hpp"
+#include "lds_dma.hpp"
 
 namespace tp {
 namespace gemm3 {
 
-
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor in four SGPRs (base, stride 0, size, raw dword format).
-__device__ __forceinline__ u32x4 sgpr_rsrc(const void* base, uint32_t num_bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, num_bytes, 0x00020000u};
-}
-
-// One 16-byte load per lane from `rsrc` at byte offset `voff` into LDS at
-// m0 + 16 * lane.  Written in assembly so that the compiler neither inserts
-// conservative waits for it nor reorders LDS accesses across it; completion
-// is tracked explicitly with wait_vmcnt.
-__device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc)
-               : "memory");
-}
-
-// s_waitcnt vmcnt(n) leaving the other counters untouched (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+using lds::lds_u8;
+using lds::v4i16;
+using lds::sgpr_rsrc;
+using lds::dma16;
+using lds::wait_vmcnt;
+using lds::barrier;
 
 // Byte offset of 16-byte chunk c of row `row` in a K-contiguous [ROWS][32] tile.
 // Rows of BK = 32 are 64 bytes (4 chunks, swizzled by row bits 2-3); rows of

@@ -13,6 +13,7 @@
 
 #include "../../include/tp_shard.h"
 #include "attention.hpp"
+#include "attention_bwd.hpp"
 #include "elementwise.hpp"
 #include "epilogues.hpp"
 #include "gemm_dma.hpp"
@@ -337,8 +338,8 @@ int tp_mlp_shard_bwd(const tp_mlp_desc* desc, const void* dOut, float p_drop, ui
                                     dA_i, dW1_i, db1_i, dW2_i, dX_i, st);
 }
 
-int tp_attn_shard_fwd(const tp_attn_desc* d, const void* X, const void* Wqkv_i, const void* Wo_i, void* QKV_i,
-                      void* O_i, float* lse_i, void* Z_i, void* stream) {
+// Descriptor checks shared by the attention entry points.
+int check_attn_desc(const tp_attn_desc* d) {
   if (!d) return TP_EINVAL;
   if (d->dtype != TP_BF16) return TP_EDTYPE;
   if (d->b < 0 || d->s < 0 || d->h < 0 || d->n_q < 1 || d->n_kv < 1 || d->d < 1 || d->t < 1 || d->rank < 0 ||
@@ -347,6 +348,16 @@ int tp_attn_shard_fwd(const tp_attn_desc* d, const void* X, const void* Wqkv_i, 
   if (d->n_q % d->t || d->n_kv % d->t || d->n_q % d->n_kv) return TP_ENOTDIV;
   if (d->d != 64 && d->d != 128) return TP_EUNSUPPORTED;
   if (!fits_int(d->b * d->s) || !fits_int(d->h)) return TP_EINVAL;
+  return TP_OK;
+}
+
+// Query heads per work-group of the attention kernels: four, two or one, so
+// that the heads of a work-group share one KV head.
+int heads_per_wg(int group) { return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1); }
+
+int tp_attn_shard_fwd(const tp_attn_desc* d, const void* X, const void* Wqkv_i, const void* Wo_i, void* QKV_i,
+                      void* O_i, float* lse_i, void* Z_i, void* stream) {
+  if (int rc = check_attn_desc(d)) return rc;
   {
     const int64_t T_ = d->b * d->s, nq = (int64_t)(d->n_q / d->t) * d->d, nkv = (int64_t)(d->n_kv / d->t) * d->d;
     if (!present(X, T_ * d->h) || !present(Wqkv_i, d->h * (nq + 2 * nkv)) || !present(Wo_i, nq * d->h) ||
@@ -378,8 +389,7 @@ int tp_attn_shard_fwd(const tp_attn_desc* d, const void* X, const void* Wqkv_i, 
   a.s = (int)d->s;
   a.q = q;
   a.kv = kv;
-  const int group = q / kv;
-  a.hg = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+  a.hg = heads_per_wg(q / kv);
   a.causal = d->causal ? 1 : 0;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
   hipError_t e;
@@ -391,6 +401,77 @@ int tp_attn_shard_fwd(const tp_attn_desc* d, const void* X, const void* Wqkv_i, 
   // Z_i = O_i Wo_i
   EpiStore<uint16_t> e2{static_cast<uint16_t*>(Z_i), h, T_, h};
   return hip_status(gemm_bf16<KMAJOR, MNMAJOR>(problem(T_, h, q * D, O_i, q * D, Wo_i, nullptr, h), e2, st));
+}
+
+int tp_attn_shard_bwd(const tp_attn_desc* d, const void* dZ, const void* X, const void* Wqkv_i, const void* Wo_i,
+                      const void* QKV_i, const void* O_i, const float* lse_i, void* dO_i, float* stats_i,
+                      void* dQKV_i, float* dWqkv_i, float* dWo_i, void* dX_i, void* stream) {
+  if (int rc = check_attn_desc(d)) return rc;
+  const int64_t T64 = d->b * d->s, nq64 = (int64_t)(d->n_q / d->t) * d->d;
+  const int64_t nqkv64 = (int64_t)(d->n_q + 2 * d->n_kv) / d->t * d->d, rows64 = d->b * (d->n_q / d->t) * d->s;
+  if (!present(dZ, T64 * d->h) || !present(X, T64 * d->h) || !present(Wqkv_i, d->h * nqkv64) ||
+      !present(Wo_i, nq64 * d->h) || !present(QKV_i, T64 * nqkv64) || !present(O_i, T64 * nq64) ||
+      !present(lse_i, rows64) || !present(dO_i, T64 * nq64) || !present(stats_i, 2 * rows64) ||
+      !present(dQKV_i, T64 * nqkv64) || !present(dWqkv_i, d->h * nqkv64) || !present(dWo_i, nq64 * d->h) ||
+      !present(dX_i, T64 * d->h))
+    return TP_EINVAL;
+  if (d->h % 8) return TP_EALIGN;
+  if (!ptrs_aligned({dZ, X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, dO_i, stats_i, dQKV_i, dWqkv_i, dWo_i, dX_i}))
+    return TP_EALIGN;
+  if (!buffer_ok(T64 * d->h, 2) || !buffer_ok(T64 * nqkv64, 2) || !buffer_ok(d->h * nqkv64, 2) ||
+      !buffer_ok(2 * rows64, 4))
+    return TP_EUNSUPPORTED;
+  const int q = d->n_q / d->t, kv = d->n_kv / d->t, D = d->d;
+  const int T_ = (int)T64, h = (int)d->h, nq = q * D, nqkv = (q + 2 * kv) * D;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // dO_i = dZ Wo_i^T (Wo_i [q d, h] is K-contiguous for this product)
+  EpiStore<uint16_t> e1{static_cast<uint16_t*>(dO_i), nq, T_, nq};
+  if (gemm_bf16<KMAJOR, KMAJOR>(problem(T_, nq, h, dZ, h, Wo_i, nullptr, h), e1, st) != hipSuccess) return TP_EHIP;
+  // dWo_i = O_i^T dZ
+  EpiStore<float> e2{dWo_i, h, nq, h};
+  if (gemm_bf16<MNMAJOR, MNMAJOR>(problem(nq, h, T_, O_i, nq, dZ, nullptr, h), e2, st) != hipSuccess)
+    return TP_EHIP;
+  // the core: row statistics, dK/dV, dQ
+  attnb::BwdArgs a{};
+  a.qkv = static_cast<const uint16_t*>(QKV_i);
+  a.o = static_cast<const uint16_t*>(O_i);
+  a.dO = static_cast<const uint16_t*>(dO_i);
+  a.lse = lse_i;
+  a.stats = stats_i;
+  a.dqkv = static_cast<uint16_t*>(dQKV_i);
+  a.ld_qkv = nqkv;
+  a.ld_o = nq;
+  a.b = (int)d->b;
+  a.s = (int)d->s;
+  a.q = q;
+  a.kv = kv;
+  a.causal = d->causal ? 1 : 0;
+  a.scale = (float)(1.0 / std::sqrt((double)D));
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  const int hg = heads_per_wg(q / kv);
+  hipError_t e;
+  {
+    Probe pr(st);
+    e = D == 128 ? launch_attn_bwd_stats<128>(a, st) : launch_attn_bwd_stats<64>(a, st);
+  }
+  if (e != hipSuccess) return TP_EHIP;
+  {
+    Probe pr(st);
+    e = D == 128 ? launch_attn_bwd_dkv<128>(a, st) : launch_attn_bwd_dkv<64>(a, st);
+  }
+  if (e != hipSuccess) return TP_EHIP;
+  {
+    Probe pr(st);
+    e = D == 128 ? launch_attn_bwd_dq<128>(a, hg, st) : launch_attn_bwd_dq<64>(a, hg, st);
+  }
+  if (e != hipSuccess) return TP_EHIP;
+  // dWqkv_i = X^T dQKV_i
+  EpiStore<float> e3{dWqkv_i, nqkv, h, nqkv};
+  if (gemm_bf16<MNMAJOR, MNMAJOR>(problem(h, nqkv, T_, X, h, dQKV_i, nullptr, nqkv), e3, st) != hipSuccess)
+    return TP_EHIP;
+  // dX_i = dQKV_i Wqkv_i^T (Wqkv_i [h, (q+2kv) d] is K-contiguous for this product)
+  EpiStore<uint16_t> e4{static_cast<uint16_t*>(dX_i), h, T_, h};
+  return hip_status(gemm_bf16<KMAJOR, KMAJOR>(problem(T_, h, nqkv, dQKV_i, nqkv, Wqkv_i, nullptr, nqkv), e4, st));
 }
 
 int tp_sum_partials(int64_t rows, int64_t cols, int32_t t, int32_t dtype, const void* const* partials,

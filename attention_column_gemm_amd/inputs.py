@@ -129,6 +129,10 @@ class AttnConfig:
         core = 4 * d * self.b * q * (self.s * (self.s + 1) // 2)
         return qkv + out + core
 
+    def flops_bwd_per_rank(self) -> int:
+        """Backward FLOPs of one rank: twice each forward term (input- and weight-gradient products)."""
+        return 2 * self.flops_per_rank()
+
 
 MLP_CONFIGS = {
     1: MLPConfig(1, 1, 64, 128, 512, 2, "gelu", "fp32", 0.0, True, None, None),
@@ -188,6 +192,11 @@ def mlp_full_weights(c: MLPConfig) -> dict:
 
 def attn_activation(c: AttnConfig) -> np.ndarray:
     return _draw(c.cfg, "X", 0, (c.tokens, c.h), 1.0, True)
+
+
+def attn_upstream_grad(c: AttnConfig) -> np.ndarray:
+    """dZ [T,h]: gradient of the attention sublayer's output, the same on every rank."""
+    return _draw(c.cfg, "dOut", 0, (c.tokens, c.h), 1.0, True)
 
 
 def attn_rank_weights(c: AttnConfig, rank: int) -> dict:

@@ -81,7 +81,7 @@ class MLPShard:
 
 
 class AttnShard:
-    """One rank's attention shard (forward)."""
+    """One rank's attention shard (forward and backward)."""
 
     def __init__(self, b, s, h, n_q, n_kv, d, t, rank, causal=True, device="cuda"):
         torch = _torch()
@@ -104,6 +104,27 @@ class AttnShard:
         B.tp_attn_shard_fwd(self.desc, self.X, self.Wqkv, self.Wo, self.QKV, self.O,
                             self.lse if want_lse else None, self.Z, stream)
         return self.Z
+
+    def alloc_backward(self):
+        """Buffers of the backward pass (allocated once, reused by every call)."""
+        torch = _torch()
+        if getattr(self, "dQKV", None) is None:
+            T, h, d = self.b * self.s, self.h, self.d
+            e = lambda *shape, dt=torch.bfloat16: torch.empty(*shape, dtype=dt, device=self.device)
+            self.dO = e(T, self.q * d)
+            self.stats = e(self.b, self.q, self.s, 2, dt=torch.float32)
+            self.dQKV = e(T, (self.q + 2 * self.kv) * d)
+            self.dWqkv = e(h, (self.q + 2 * self.kv) * d, dt=torch.float32)
+            self.dWo = e(self.q * d, h, dt=torch.float32)
+            self.dX = e(T, h)
+        return self
+
+    def backward(self, dZ, stream=None):
+        """Gradients for the upstream gradient ``dZ`` [T, h] (needs a forward with lse)."""
+        self.alloc_backward()
+        B.tp_attn_shard_bwd(self.desc, dZ, self.X, self.Wqkv, self.Wo, self.QKV, self.O, self.lse, self.dO,
+                            self.stats, self.dQKV, self.dWqkv, self.dWo, self.dX, stream)
+        return self.dX
 
 
 def sum_partials(partials, bias=None, p_drop=0.0, seed=0, out=None, stream=None):

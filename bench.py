@@ -3,9 +3,10 @@
 A step is one pass of the whole hot path for rank 0 of the chosen workload:
 attention shard forward (QKV GEMM, causal GQA attention, output projection),
 its emulated all-reduce, the MLP shard forward, its emulated all-reduce, the
-MLP shard backward and its emulated all-reduce, plus the host-side
-all-reduce accounting.  Inputs are seeded synthetic tensors already resident
-in HBM when timing starts.
+MLP shard backward and its emulated all-reduce, the attention shard backward
+(taking the reduced MLP input gradient as its upstream gradient) and its
+emulated all-reduce, plus the host-side all-reduce accounting.  Inputs are
+seeded synthetic tensors already resident in HBM when timing starts.
 
 The reported metric is the per-rank MLP forward+backward throughput
 (algorithmic FLOPs 18*T*h*f for SwiGLU, 12*T*h*f for GeLU, over the measured
@@ -103,6 +104,18 @@ def kernel_plan(mc, ac):
              ("mlp_bwd_dW1_gemm", "a6", 2 * T * h * f * n1, None),
              ("mlp_bwd_dX_gemm", "a6", 2 * T * f * h * n1, None),
              ("allreduce_bwd_sum", "a7", None, (mc.t + 1) * T * h * d)]
+    if ac is not None:
+        # attention backward: algorithmic FLOPs per kernel (the score and dP
+        # recomputations are not counted): dK/dV do dP, dV and dK, dQ does dQ
+        pairs = ac.b * q * (ac.s * (ac.s + 1) // 2)
+        plan += [("attn_bwd_dO_gemm", "f1", 2 * Ta * ha * q * dh, None),
+                 ("attn_bwd_dWo_gemm", "f1", 2 * Ta * ha * q * dh, None),
+                 ("attn_bwd_stats", "f1", None, 2 * Ta * q * dh * 2 + ac.b * q * ac.s * 12),
+                 ("attn_bwd_dkv", "f1", 6 * dh * pairs, None),
+                 ("attn_bwd_dq", "f1", 2 * dh * pairs, None),
+                 ("attn_bwd_dWqkv_gemm", "f1", 2 * Ta * ha * (q + 2 * kv) * dh, None),
+                 ("attn_bwd_dX_gemm", "f1", 2 * Ta * ha * (q + 2 * kv) * dh, None),
+                 ("allreduce_attn_bwd_sum", "a7", None, (ac.t + 1) * Ta * ha * 2)]
     return plan
 
 
@@ -200,9 +213,13 @@ def main():
     out = torch.empty_like(mlp.Z)
     dxsum = torch.empty_like(mlp.dX)
     if attn is not None:
-        attn.forward(want_lse=False)
+        assert ac.tokens == mc.tokens and ac.h == mc.h, "the attention backward takes the MLP's input gradient"
+        attn.forward(want_lse=True)
+        attn.backward(dxsum)
         za_others = others(attn.Z, ac.t)
         zasum = torch.empty_like(attn.Z)
+        dxa_others = others(attn.dX, ac.t)
+        dxasum = torch.empty_like(attn.dX)
     torch.cuda.synchronize()
 
     plan = kernel_plan(mc, ac)
@@ -220,7 +237,7 @@ def main():
         ev = lambda: torch.cuda.Event(enable_timing=True)
         if attn is not None:
             e0 = ev(); e0.record()
-            attn.forward(want_lse=False)
+            attn.forward(want_lse=True)
             sum_partials([attn.Z] + za_others, None, 0.0, 0, out=zasum)
             e1 = ev(); e1.record()
             marks.append(("attention_fwd_and_allreduce", e0, e1))
@@ -233,8 +250,14 @@ def main():
         e3 = ev(); e3.record()
         sum_partials([mlp.dX] + dx_others, None, 0.0, 0, out=dxsum)
         e4 = ev(); e4.record()
-        B.tp_comm_bytes(mc.tokens, mc.h, mc.t, 2 if mc.bf16 else 4)   # a9: host-only accounting
         marks += [("mlp_fwd", e0, e1), ("mlp_bwd", e2, e3), ("allreduce_fwd", e1, e2), ("allreduce_bwd", e3, e4)]
+        if attn is not None:
+            attn.backward(dxsum)
+            e5 = ev(); e5.record()
+            sum_partials([attn.dX] + dxa_others, None, 0.0, 0, out=dxasum)
+            e6 = ev(); e6.record()
+            marks += [("attention_bwd", e4, e5), ("allreduce_attn_bwd", e5, e6)]
+        B.tp_comm_bytes(mc.tokens, mc.h, mc.t, 2 if mc.bf16 else 4)   # a9: host-only accounting
         return marks
 
     log(f"[bench] warmup {args.warmup} steps")
@@ -310,8 +333,8 @@ def main():
         "data": "synthetic",
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "config": {
-            "workload": {"cfg5": "full per-rank layer shard (attention fwd + SwiGLU MLP fwd+bwd), rank 0 of t=8",
-                         "cfg3": "Llama SwiGLU MLP shard fwd+bwd + GQA attention shard fwd, rank 0 of t=8",
+            "workload": {"cfg5": "full per-rank layer shard (attention + SwiGLU MLP, fwd+bwd), rank 0 of t=8",
+                         "cfg3": "Llama SwiGLU MLP shard + GQA attention shard, fwd+bwd, rank 0 of t=8",
                          "cfg2": "GPT GeLU MLP shard fwd+bwd with dropout 0.1, rank 0 of t=4"}[args.workload],
             "tokens": mc.tokens, "b": mc.b, "s": mc.s, "h": mc.h, "h_ffn": mc.h_ffn, "t": mc.t, "f": mc.f,
             "act": mc.act, "p_drop": mc.p_drop, "bias": mc.bias,
@@ -331,6 +354,8 @@ def main():
     if attn is not None:
         af = I.ATTN_CONFIGS[acid].flops_per_rank()
         res["attention_fwd_tflops"] = round(af / (span["attention_fwd_and_allreduce"] * 1e-3) / 1e12, 2)
+        ab = I.ATTN_CONFIGS[acid].flops_bwd_per_rank()
+        res["attention_bwd_tflops"] = round(ab / (span["attention_bwd"] * 1e-3) / 1e12, 2)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 2
         src = torch.empty(n, dtype=torch.bfloat16, device="cuda").fill_(1.0)

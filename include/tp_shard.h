@@ -171,6 +171,39 @@ int tp_attn_shard_fwd(const tp_attn_desc* desc, const void* X, const void* Wqkv_
                       void* QKV_i, void* O_i, float* lse_i, void* Z_i, void* stream);
 
 /*
+ * tp_attn_shard_bwd -- backward of one rank's attention shard
+ * ([HJ] Attention, single-card backward; [LP] I.O on recomputing the scores;
+ * [TP1] operators f and g and the attention sublayer's communication).
+ *
+ *   dWo_i = O_i^T dZ;   dO_i = dZ Wo_i^T
+ *   per sequence and local query head j (KV head g = j / (q/kv)), c = 1/sqrt(d),
+ *   P = softmax(c Q K^T + mask) recomputed from lse_i:
+ *     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dO * O)),
+ *     dQ = c dS K,  dK = c dS^T Q   (dK, dV summed over the heads of the group)
+ *   dQKV_i = [dQ heads | dK heads | dV heads] (the layout of QKV_i)
+ *   dWqkv_i = X^T dQKV_i;   dX_i = dQKV_i Wqkv_i^T
+ * dZ is the gradient of the attention sublayer's output, the same on every
+ * rank; dX_i is this rank's partial input gradient, summed over ranks by
+ * tp_sum_partials (no bias, p = 0).
+ * Arguments:
+ *   dZ      [T, h]             gradient of the sublayer output (replicated), bf16
+ *   X, Wqkv_i, Wo_i            as in tp_attn_shard_fwd
+ *   QKV_i, O_i, lse_i          as written by tp_attn_shard_fwd (lse_i required)
+ *   dO_i    [T, q d]           out, bf16: gradient of O_i
+ *   stats_i [b, q, s, 2] fp32  scratch: per row {lse * log2(e), rowsum(dO * O)}
+ *   dQKV_i  [T, (q+2kv) d]     out, bf16
+ *   dWqkv_i [h, (q+2kv) d] fp32 out
+ *   dWo_i   [q d, h] fp32      out
+ *   dX_i    [T, h]             out, bf16 partial input gradient
+ * Same descriptor and conditions as tp_attn_shard_fwd.  The result does not
+ * depend on the order in which work-groups run (no atomics).
+ */
+int tp_attn_shard_bwd(const tp_attn_desc* desc, const void* dZ, const void* X, const void* Wqkv_i,
+                      const void* Wo_i, const void* QKV_i, const void* O_i, const float* lse_i,
+                      void* dO_i, float* stats_i, void* dQKV_i, float* dWqkv_i, float* dWo_i,
+                      void* dX_i, void* stream);
+
+/*
  * tp_sum_partials -- the all-reduce of operators g/f, emulated on one device
  * ([TP1] operators f and g; [L11] section 3 on the bias; [LP] I.III and [HJ] on dropout).
  *

@@ -11,8 +11,8 @@ from oracle import comm
 
 def test_library_exports_every_declared_function():
     names = B.declared_functions()
-    assert set(names) >= {"tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_attn_shard_fwd", "tp_sum_partials",
-                          "tp_comm_bytes", "tp_status_string"}
+    assert set(names) >= {"tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_attn_shard_fwd", "tp_attn_shard_bwd",
+                          "tp_sum_partials", "tp_comm_bytes", "tp_status_string"}
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -118,6 +118,33 @@ def test_attention_validation():
     assert call(rank=2) == B.TP_EINVAL
     assert call(h=100) == B.TP_EALIGN
     assert L.tp_attn_shard_fwd(None, A16, A16, A16, A16, A16, None, A16, None) == B.TP_EINVAL
+
+
+def test_attention_backward_validation():
+    """Every case is invalid, so nothing is launched."""
+    L = B.lib()
+
+    def call(ptrs=None, **kw):
+        d = dict(b=2, s=64, h=256, n_q=8, n_kv=2, d=128, t=2, rank=0, dtype=B.TP_BF16, causal=1)
+        d.update(kw)
+        desc = B.tp_attn_desc(**d)
+        p = [A16] * 13 if ptrs is None else ptrs
+        return L.tp_attn_shard_bwd(ctypes.byref(desc), *p, None)
+
+    assert call(dtype=B.TP_F32) == B.TP_EDTYPE
+    assert call(n_q=9) == B.TP_ENOTDIV
+    assert call(d=32) == B.TP_EUNSUPPORTED
+    assert call(rank=-1) == B.TP_EINVAL
+    assert call(h=100) == B.TP_EALIGN
+    for i in range(13):                      # each tensor is required
+        p = [A16] * 13
+        p[i] = None
+        assert call(ptrs=p) == B.TP_EINVAL, i
+    for i in range(13):                      # each tensor must be 16-byte aligned
+        p = [A16] * 13
+        p[i] = MIS
+        assert call(ptrs=p) == B.TP_EALIGN, i
+    assert L.tp_attn_shard_bwd(None, *([A16] * 13), None) == B.TP_EINVAL
 
 
 def test_sum_partials_validation():

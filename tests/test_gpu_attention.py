@@ -1,5 +1,6 @@
 """GPU parity of the attention shard forward (QKV GEMM, causal GQA flash
-attention, row-parallel output projection) against the float64 oracle."""
+attention, row-parallel output projection) and backward (dO and dWo GEMMs,
+flash backward, dWqkv and partial dX GEMMs) against the float64 oracle."""
 import numpy as np
 import pytest
 
@@ -106,3 +107,92 @@ def test_attention_cfg5_rank0_sampled():
     lse = _np(sh.lse).transpose(1, 0, 2).reshape(c.q, -1)[:, rows]
     check("lse_i rows", lse, ref["lse"], BF)
     check("Z_i rows", _np(sh.Z)[rows], ref["Z"], BF)
+
+
+# ------------------------------------------------------------------ backward
+
+BWD_SMALL = dict(SMALL)
+BWD_SMALL["s1_single_token"] = (I.custom_attn(205, 3, 1, 128, 4, 2, 64, 2), True)
+BWD_SMALL["s33_d128_gqa4"] = (I.custom_attn(206, 2, 33, 136, 8, 2, 128, 2), True)
+
+
+def _run_bwd(c, rank, causal=True):
+    from attention_column_gemm_amd.shard import to_device
+    sh, X, w = _run(c, rank, causal)
+    dZ = I.attn_upstream_grad(c)
+    sh.backward(to_device(dZ, "bf16"))
+    return sh, X, w, dZ
+
+
+def _check_bwd(tag, c, sh, X, w, dZ, causal):
+    ref = OA.shard_backward(dZ, X, w["Wqkv"], w["Wo"], b=c.b, s=c.s, q=c.q, kv=c.kv, d=c.d, causal=causal)
+    check(f"{tag}.dO_i", _np(sh.dO), ref["dO"], BF)
+    check(f"{tag}.dQKV_i", _np(sh.dQKV), ref["dQKV"], BF)
+    check(f"{tag}.dWqkv_i", _np(sh.dWqkv), ref["dWqkv"], BF)
+    check(f"{tag}.dWo_i", _np(sh.dWo), ref["dWo"], BF)
+    check(f"{tag}.dX_i", _np(sh.dX), ref["dX"], BF)
+    # the core alone, from the GPU's own bf16 QKV and dO (isolates the flash backward)
+    q, kv, d = c.q, c.kv, c.d
+    QKV = _np(sh.QKV)
+    dQ, dK, dV = OA.core_backward(QKV[:, :q * d], QKV[:, q * d:(q + kv) * d], QKV[:, (q + kv) * d:], _np(sh.dO),
+                                  b=c.b, s=c.s, n_q=q, n_kv=kv, d=d, causal=causal)
+    got = _np(sh.dQKV)
+    check(f"{tag}.core dQ", got[:, :q * d], dQ, 1e-2)
+    check(f"{tag}.core dK", got[:, q * d:(q + kv) * d], dK, 1e-2)
+    check(f"{tag}.core dV", got[:, (q + kv) * d:], dV, 1e-2)
+    return ref
+
+
+@pytest.mark.parametrize("name", list(BWD_SMALL))
+def test_attention_backward_all_ranks_full_parity(name):
+    torch = need_gpu()
+    c, causal = BWD_SMALL[name]
+    banner(f"attn bwd {name} b={c.b} s={c.s} h={c.h} n_q={c.n_q} n_kv={c.n_kv} d={c.d} t={c.t} causal={causal}")
+    from attention_column_gemm_amd.shard import sum_partials
+    gdX, rdX = [], []
+    for rank in range(c.t):
+        sh, X, w, dZ = _run_bwd(c, rank, causal)
+        torch.cuda.synchronize()
+        ref = _check_bwd(f"r{rank}", c, sh, X, w, dZ, causal)
+        gdX.append(sh.dX)
+        rdX.append(ref["dX"])
+    dX = sum_partials(gdX)
+    torch.cuda.synchronize()
+    check("dX = sum dX_i", _np(dX), O.sum_partials(rdX), BF)
+
+
+def test_attention_backward_is_deterministic():
+    torch = need_gpu()
+    c, causal = SMALL["gqa4_d128_ragged"]
+    banner("attn bwd determinism")
+    from attention_column_gemm_amd.shard import to_device
+    sh, X, w, dZ = _run_bwd(c, 1, causal)
+    first = [t.clone() for t in (sh.dQKV, sh.dWqkv, sh.dWo, sh.dX)]
+    sh.backward(to_device(dZ, "bf16"))
+    torch.cuda.synchronize()
+    for a, b in zip(first, (sh.dQKV, sh.dWqkv, sh.dWo, sh.dX)):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.slow
+def test_attention_backward_cfg4_first_and_last_rank():
+    """GQA attention shard backward, bf16: b=2 s=2048 h=4096 32q/8kv d=128 t=8."""
+    torch = need_gpu()
+    c = I.ATTN_CONFIGS[4]
+    for rank in (0, c.t - 1):
+        banner(f"attn bwd cfg4 full size, rank {rank}")
+        sh, X, w, dZ = _run_bwd(c, rank)
+        torch.cuda.synchronize()
+        _check_bwd(f"r{rank}", c, sh, X, w, dZ, True)
+        del sh
+
+
+@pytest.mark.slow
+def test_attention_backward_cfg5_rank0():
+    """Full-layer attention shard backward, bf16: b=4 s=2048 h=8192 64q/8kv d=128 t=8, rank 0."""
+    torch = need_gpu()
+    c = I.ATTN_CONFIGS[5]
+    banner("attn bwd cfg5 full size, rank 0")
+    sh, X, w, dZ = _run_bwd(c, 0)
+    torch.cuda.synchronize()
+    _check_bwd("r0", c, sh, X, w, dZ, True)
