@@ -15,6 +15,7 @@
 //  * stats: per (sequence, head, row) the pair {lse * log2(e), Delta}.
 //  * dK/dV: a work-group owns 32 keys of one KV head; its four waves take
 //    every fourth (query head, 32-row query tile) item of the causal range,
+//    last query tile first,
 //    each wave streaming its own Q and dO tiles into LDS with LDS-direct
 //    loads (double buffered), and the four waves' partial sums are added in a
 //    fixed order through LDS at the end (deterministic, no atomics).
@@ -30,6 +31,7 @@
 // in that same order, so no tile is ever stored transposed.
 #pragma once
 
+#include "attn_tiles.hpp"
 #include "common.hpp"
 #include "lds_dma.hpp"
 
@@ -38,6 +40,12 @@ namespace attnb {
 
 using lds::lds_u8;
 using lds::v4i16;
+using attnt::dma4;
+using attnt::dma_tile;
+using attnt::pack8;
+using attnt::row_frag;
+using attnt::tile_off;
+using attnt::tr_frag;
 
 constexpr int NTHREADS = 256;
 constexpr int KEY_BLOCK = 32;   // keys per dK/dV work-group
@@ -57,80 +65,6 @@ struct BwdArgs {
   float scale;       // 1 / sqrt(d)
   float scale_log2;  // log2(e) / sqrt(d)
 };
-
-// 16-byte chunk permutation of a row-major [rows][D] bf16 tile: logical chunk
-// c of row r sits at chunk c ^ swz(r).  Sixteen consecutive rows at one
-// logical chunk (a 128-bit fragment read) and four consecutive rows at one
-// aligned chunk pair (a transposing read) both land on distinct banks.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
-  return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);  // D = 64: row parity picks the bank half
-}
-template <int D>
-__device__ __forceinline__ uint32_t tile_off(int r, int c) {
-  return (uint32_t)(r * D * 2 + ((c ^ swz<D>(r)) << 4));
-}
-
-// 16-byte row fragment (rows r0 + lane%32, k step kk) of a row-major tile.
-template <int D>
-__device__ __forceinline__ bf16x8 row_frag(const lds_u8* tile, int r0, int kk) {
-  const int lane = threadIdx.x & 63;
-  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-      tile + tile_off<D>(r0 + (lane & 31), kk * 2 + (lane >> 5)));
-}
-
-// Transposed fragment of a row-major tile T[row][col]: lane l gets column
-// 32 dt + l % 32 at the eight rows that the registers 8 jj .. 8 jj + 7 of a
-// 32x32 accumulator hold for its half h = l / 32, i.e. rows
-// r0 + 16 jj + 4 h + {0..3} and r0 + 16 jj + 8 + 4 h + {0..3}.
-template <int D>
-__device__ __forceinline__ bf16x8 tr_frag(const lds_u8* tile, int r0, int dt, int jj) {
-  const int lane = threadIdx.x & 63;
-  const int g4 = lane >> 4, R = lane & 15, h = lane >> 5;
-  const int col = 32 * dt + 16 * (g4 & 1) + 4 * (R & 3);
-  v4i16 part[2];
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int row = r0 + 16 * jj + 4 * h + 8 * half + (R >> 2);
-    part[half] = lds::read_tr16(tile, tile_off<D>(row, col >> 3) + (col & 7) * 2);
-  }
-  typedef short v8i16 __attribute__((ext_vector_type(8)));
-  v8i16 v = {part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-// LDS-direct load of rows [row0, row0 + ROWS) x D bf16 columns starting at
-// byte column col_bytes of a row-major matrix (ld_bytes per row, nrows rows,
-// behind `rsrc`) into a swizzled [ROWS][D] tile at LDS byte address dst.
-// This wave issues the tile's 1 KiB instructions i0, i0 + step, ...
-template <int D, int ROWS>
-__device__ __forceinline__ void dma_tile(const u32x4& rsrc, uint32_t ld_bytes, int row0, int nrows,
-                                         uint32_t col_bytes, uint32_t dst, int i0, int step) {
-  constexpr int NI = ROWS * D * 2 / 1024;
-  const int lane = threadIdx.x & 63;
-  for (int i = i0; i < NI; i += step) {
-    const int o = i * 1024 + 16 * lane;
-    const int r = o / (2 * D), pos = (o % (2 * D)) >> 4;
-    const int c = pos ^ swz<D>(r);
-    const uint32_t voff =
-        row0 + r < nrows ? (uint32_t)(row0 + r) * ld_bytes + col_bytes + (uint32_t)c * 16u : kOOB;
-    lds::dma16(rsrc, voff, dst + (uint32_t)i * 1024u);
-  }
-}
-
-// One 4-byte load per lane from `rsrc` at `voff` into LDS at m0 + 4 * lane.
-__device__ __forceinline__ void dma4(const u32x4& rsrc, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc)
-               : "memory");
-}
-
-__device__ __forceinline__ bf16x8 pack8(const float* v) {
-  u32x4 w;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-  return __builtin_bit_cast(bf16x8, w);
-}
 
 // ---- stats -------------------------------------------------------------------
 // Row r = (beta q + j) s + i: stats[2r] = lse * log2(e), stats[2r+1] = Delta.
@@ -214,9 +148,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_bwd_dkv_kernel(BwdArgs a) {
   const u32x4 rst = lds::sgpr_rsrc(a.stats + (int64_t)beta * a.q * a.s * 2, (uint32_t)a.q * a.s * 8u);
   const uint32_t wl = lds_base + (uint32_t)wave * WAVE_LDS;
 
+  // items run from the last query tile backwards, so the work-groups of one
+  // KV head (all key blocks) read the same Q and dO tiles at about the same
+  // time and share them in L2
   auto item = [&](int n, int& j, int& i0) {
     j = g * group + n / ntile;
-    i0 = (qt0 + n % ntile) * Q_TILE;
+    i0 = (nqt - 1 - n % ntile) * Q_TILE;
   };
   auto issue = [&](int n, int st) {
     int j, i0;
@@ -325,7 +262,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_bwd_dkv_kernel(BwdArgs a) {
 
 // ---- dQ ----------------------------------------------------------------------
 template <int D>
-__global__ void __launch_bounds__(NTHREADS, 1) attn_bwd_dq_kernel(BwdArgs a, int hg) {
+__global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_kernel(BwdArgs a, int hg) {
   constexpr int DT = D / 32, KK = D / 16;
   constexpr int TILE = DQ_KEYS * D * 2;  // one 64-key K or V tile
   constexpr int TI = TILE / 1024;
