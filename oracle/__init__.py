@@ -16,8 +16,10 @@ Pages cited (by title and section):
          (tensor-parallel linear sharding and fwd/bwd communication volume),
          sections 1-6.
 * [LP]   cnblogs "ラブパラ" (a survey of parallelisms): O.I Notation,
-         O.II Collective Communication, I.III Tensor Parallelism,
-         II.II Communication Approaches, II.V Agnostic to Implementation.
+         O.II Collective Communication, I.O Activations, I.III Tensor
+         Parallelism, II.II Communication Approaches, II.III Computational
+         Details, II.V Agnostic to Implementation, III.III Block Layout
+         Contract.
 * [HJ]   hjcheng0602.cn "tensorparallel/tp": MLP (single-card forward and
          backward, TP forward and backward) and Attention sections.
 * [TP1]  "Tensor Parallelism张量并行（一）": row split, column split, MLP and
@@ -31,10 +33,12 @@ Modules:
                               and the emulated all-reduce (sum of partials).
 * :mod:`oracle.attention`   - causal GQA attention, unsharded and per shard,
                               forward and backward.
+* :mod:`oracle.sequence_parallel` - the closing all-reduce with a fused residual
+                              add, and its Megatron-SP reduce-scatter / all-gather split.
 * :mod:`oracle.comm`        - all-reduce count and bytes per layer.
 * :mod:`oracle.flops`       - algorithmic FLOP counts.
 
 Parity status: every function here is pinned by a test in
 ``tests/test_oracle_*.py`` except where its docstring says "parity unpinned".
 """
-from . import activations, dropout, mlp, attention, comm, flops  # noqa: F401
+from . import activations, dropout, mlp, attention, sequence_parallel, comm, flops  # noqa: F401

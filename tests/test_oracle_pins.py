@@ -17,6 +17,7 @@ import pytest
 from oracle import activations as A
 from oracle import attention as att
 from oracle import comm, dropout, flops, mlp
+from oracle import sequence_parallel as sp
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -488,6 +489,67 @@ def test_attention_backward_shards_match_unsharded():
         np.testing.assert_allclose(sh["dO"], full["dO"][:, cq], rtol=1e-12, atol=1e-12)
         dX += sh["dX"]
     np.testing.assert_allclose(dX, full["dX"], rtol=1e-11, atol=1e-12)
+
+
+# ------------------------------------------- fused residual and Megatron-SP
+
+def _partials(seed, t=4, T=12, h=16):
+    g = _rng(seed)
+    return [g.standard_normal((T, h)) for _ in range(t)], g.standard_normal(h), g.standard_normal((T, h))
+
+
+def test_residual_is_added_once_and_never_dropped():
+    """With all partials and the bias zero, the block output is exactly the
+    residual at any dropout rate and any t: the residual path is added once,
+    after dropout ([LP] II.III fused bias + dropout + residual add)."""
+    for t in (1, 3):
+        P, b, R = _partials(31, t=t)
+        Z = [np.zeros_like(p) for p in P]
+        for p in (0.0, 0.1, 0.5):
+            out = sp.sum_partials_residual(Z, np.zeros_like(b), p, 7, R)
+            assert np.array_equal(out, R)
+
+
+def test_residual_fusion_adds_the_residual_to_the_plain_all_reduce():
+    P, b, R = _partials(32)
+    for p in (0.0, 0.25):
+        plain = mlp.sum_partials(P, b, p, 11)
+        fused = sp.sum_partials_residual(P, b, p, 11, R)
+        np.testing.assert_array_equal(fused, plain + R)
+        np.testing.assert_array_equal(sp.sum_partials_residual(P, b, p, 11, None), plain)
+
+
+def test_reduce_scatter_then_all_gather_equals_the_all_reduce():
+    """[LP] III.III: the all-reduce split into reduce-scatter (token slices,
+    token-wise bias/dropout/residual on the slice) and all-gather gives the
+    same tensor, element for element, in rank order."""
+    for t in (1, 2, 4):
+        P, b, R = _partials(33 + t, t=t, T=4 * t + 8 * t, h=24)
+        T = P[0].shape[0]
+        for p in (0.0, 0.3):
+            full = sp.sum_partials_residual(P, b, p, 5, R)
+            slices = []
+            for r in range(t):
+                rows = sp.slice_rows(T, t, r)
+                assert rows[0] == r * (T // t) and len(rows) == T // t
+                slices.append(sp.reduce_scatter(P, t, r, b, p, 5, R[rows]))
+            np.testing.assert_array_equal(sp.all_gather(slices), full)
+    with pytest.raises(ValueError):
+        sp.slice_rows(10, 4, 0)
+
+
+def test_reduce_scatter_slices_partition_the_sum():
+    """p = 0, no bias, no residual: the slices are the rows of sum_i P_i, and a
+    slice does not depend on the other ranks' rows of the partials."""
+    P, _, _ = _partials(36, t=4, T=16, h=8)
+    for r in range(4):
+        rows = sp.slice_rows(16, 4, r)
+        got = sp.reduce_scatter(P, 4, r)
+        np.testing.assert_array_equal(got, sum(p[rows] for p in P))
+        Q = [p.copy() for p in P]
+        for q in Q:
+            q[np.setdiff1d(np.arange(16), rows)] = np.nan
+        np.testing.assert_array_equal(sp.reduce_scatter(Q, 4, r), got)
 
 
 # ---------------------------------------------------------------------- comm
