@@ -66,12 +66,21 @@ def lib() -> ctypes.CDLL:
         L.tp_attn_shard_bwd.argtypes = [ctypes.POINTER(tp_attn_desc)] + [_VP] * 13 + [_VP]
         L.tp_sum_partials.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.POINTER(_VP), _VP, ctypes.c_float, ctypes.c_uint64, _VP, _VP]
+        L.tp_sum_partials_residual.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.POINTER(_VP), _VP, ctypes.c_float, ctypes.c_uint64, _VP,
+                                               _VP, _VP]
+        L.tp_reduce_scatter.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.POINTER(_VP), _VP, ctypes.c_float, ctypes.c_uint64,
+                                        _VP, _VP, _VP]
+        L.tp_all_gather.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.POINTER(_VP), _VP, _VP]
         L.tp_comm_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.POINTER(tp_comm)]
         L.tp_status_string.argtypes = [ctypes.c_int]
         L.tp_status_string.restype = ctypes.c_char_p
         for name in ("tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_attn_shard_fwd", "tp_attn_shard_bwd",
-                     "tp_sum_partials", "tp_comm_bytes"):
+                     "tp_sum_partials", "tp_sum_partials_residual", "tp_reduce_scatter", "tp_all_gather",
+                     "tp_comm_bytes"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -144,6 +153,28 @@ def tp_sum_partials(rows: int, cols: int, t: int, dtype: int, partials, bias, p_
     arr = (_VP * max(1, len(partials)))(*[_ptr(p) for p in partials])
     _check(lib().tp_sum_partials(int(rows), int(cols), int(t), int(dtype), arr, _ptr(bias), float(p_drop),
                                  int(seed) & (2 ** 64 - 1), _ptr(out), _stream(stream)), "tp_sum_partials")
+
+
+def tp_sum_partials_residual(rows: int, cols: int, t: int, dtype: int, partials, bias, p_drop: float, seed: int,
+                             residual, out, stream=None):
+    arr = (_VP * max(1, len(partials)))(*[_ptr(p) for p in partials])
+    _check(lib().tp_sum_partials_residual(int(rows), int(cols), int(t), int(dtype), arr, _ptr(bias), float(p_drop),
+                                          int(seed) & (2 ** 64 - 1), _ptr(residual), _ptr(out), _stream(stream)),
+           "tp_sum_partials_residual")
+
+
+def tp_reduce_scatter(rows: int, cols: int, t: int, rank: int, dtype: int, partials, bias, p_drop: float, seed: int,
+                      residual_r, out_r, stream=None):
+    arr = (_VP * max(1, len(partials)))(*[_ptr(p) for p in partials])
+    _check(lib().tp_reduce_scatter(int(rows), int(cols), int(t), int(rank), int(dtype), arr, _ptr(bias),
+                                   float(p_drop), int(seed) & (2 ** 64 - 1), _ptr(residual_r), _ptr(out_r),
+                                   _stream(stream)), "tp_reduce_scatter")
+
+
+def tp_all_gather(rows_per_rank: int, cols: int, t: int, dtype: int, slices, out, stream=None):
+    arr = (_VP * max(1, len(slices)))(*[_ptr(p) for p in slices])
+    _check(lib().tp_all_gather(int(rows_per_rank), int(cols), int(t), int(dtype), arr, _ptr(out), _stream(stream)),
+           "tp_all_gather")
 
 
 def tp_comm_bytes(tokens: int, h: int, t: int, delta: int) -> tp_comm:

@@ -41,14 +41,18 @@ template <> struct Vec<float> {
   }
 };
 
-// out = Dropout(sum_{i<t} P_i + bias).  The partials are summed in rank order
-// in fp32; the bias is added once, after the sum; the dropout decision of flat
-// element idx comes from dropout_keep(seed, idx, thr).  cols is a multiple of
-// the vector width, so one vector lies in one row.
+// out = residual + Dropout(sum_{i<t} P_i + bias).  The partials are summed
+// in rank order in fp32; the bias is added once, after the sum; the dropout
+// decision of the element at flat index e of this call's range comes from
+// dropout_keep(seed, idx0 + e, thr), idx0 being the range's first index in
+// the full tensor (so a token slice keeps the full tensor's mask); the
+// residual (optional) is added last.  cols is a multiple of the vector width,
+// so one vector lies in one row.
 template <class T>
 __global__ void __launch_bounds__(256) sum_partials_kernel(int64_t n_vec, int64_t cols, int t, PartialPtrs P,
                                                            const T* __restrict__ bias, uint32_t thr, float scale,
-                                                           uint64_t seed, T* __restrict__ out) {
+                                                           uint64_t seed, uint64_t idx0,
+                                                           const T* __restrict__ residual, T* __restrict__ out) {
   constexpr int V = Vec<T>::N;
   for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < n_vec; v += (int64_t)gridDim.x * blockDim.x) {
     const int64_t e0 = v * V;
@@ -68,9 +72,26 @@ __global__ void __launch_bounds__(256) sum_partials_kernel(int64_t n_vec, int64_
     }
     if (thr) {
 #pragma unroll
-      for (int j = 0; j < V; ++j) acc[j] = dropout_keep(seed, (uint64_t)(e0 + j), thr) ? acc[j] * scale : 0.0f;
+      for (int j = 0; j < V; ++j)
+        acc[j] = dropout_keep(seed, idx0 + (uint64_t)(e0 + j), thr) ? acc[j] * scale : 0.0f;
+    }
+    if (residual) {
+      float r[V];
+      Vec<T>::load(residual + e0, r);
+#pragma unroll
+      for (int j = 0; j < V; ++j) acc[j] += r[j];
     }
     Vec<T>::store(out + e0, acc);
+  }
+}
+
+// out = [S_0; S_1; ...; S_{t-1}]: the t slices of n_vec_slice vectors each,
+// concatenated in rank order (16-byte vector copies).
+__global__ void __launch_bounds__(256) gather_kernel(int64_t n_vec_slice, int t, PartialPtrs S, u32x4* __restrict__ out) {
+  const int64_t n = n_vec_slice * t;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < n; v += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = v / n_vec_slice, e = v - r * n_vec_slice;
+    out[v] = reinterpret_cast<const u32x4*>(S.p[r])[e];
   }
 }
 

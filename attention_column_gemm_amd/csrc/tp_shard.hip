@@ -474,34 +474,102 @@ int tp_attn_shard_bwd(const tp_attn_desc* d, const void* dZ, const void* X, cons
   return hip_status(gemm_bf16<KMAJOR, KMAJOR>(problem(T_, h, nqkv, dQKV_i, nqkv, Wqkv_i, nullptr, nqkv), e4, st));
 }
 
-int tp_sum_partials(int64_t rows, int64_t cols, int32_t t, int32_t dtype, const void* const* partials,
-                    const void* bias, float p_drop, uint64_t seed, void* out, void* stream) {
-  if (dtype != TP_F32 && dtype != TP_BF16) return TP_EDTYPE;
-  if (rows < 0 || cols < 0 || t < 1 || !partials || !present(out, rows * cols)) return TP_EINVAL;
-  if (t > MAX_PARTIALS) return TP_EUNSUPPORTED;
+}  // extern "C"
+
+namespace {
+
+// Rows [row0, row0 + nrows) of residual + Dropout(sum_i P_i + bias) over full
+// [rows_total, cols] partials, written to out [nrows, cols]; the residual, if
+// any, is [nrows, cols].  Shared by the all-reduce and the reduce-scatter.
+int sum_rows(int64_t rows_total, int64_t row0, int64_t nrows, int64_t cols, int32_t t, int32_t dtype,
+             const void* const* partials, const void* bias, float p_drop, uint64_t seed, const void* residual,
+             void* out, void* stream) {
   uint32_t thr = 0;
   float scale = 1.0f;
   int rc = check_dropout(p_drop, &thr, &scale);
   if (rc) return rc;
   const int vec = dtype == TP_BF16 ? 8 : 4;
+  const int esz = dtype == TP_BF16 ? 2 : 4;
   if (cols % vec) return TP_EALIGN;
   PartialPtrs P{};
   for (int i = 0; i < t; ++i) {
-    if (!present(partials[i], rows * cols)) return TP_EINVAL;
+    if (!present(partials[i], rows_total * cols)) return TP_EINVAL;
     if (!aligned16(partials[i])) return TP_EALIGN;
-    P.p[i] = partials[i];
+    P.p[i] = partials[i] ? static_cast<const uint8_t*>(partials[i]) + row0 * cols * esz : nullptr;
   }
-  if (!ptrs_aligned({bias, out})) return TP_EALIGN;
-  const int64_t nv = rows * cols / vec;
+  if (!ptrs_aligned({bias, residual, out})) return TP_EALIGN;
+  const int64_t nv = nrows * cols / vec;
   if (nv == 0) return TP_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint64_t idx0 = (uint64_t)(row0 * cols);
   Probe pr(st);
   if (dtype == TP_BF16)
     hipLaunchKernelGGL(sum_partials_kernel<uint16_t>, dim3(grid_for(nv)), dim3(256), 0, st, nv, cols, t, P,
-                       static_cast<const uint16_t*>(bias), thr, scale, seed, static_cast<uint16_t*>(out));
+                       static_cast<const uint16_t*>(bias), thr, scale, seed, idx0,
+                       static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(out));
   else
     hipLaunchKernelGGL(sum_partials_kernel<float>, dim3(grid_for(nv)), dim3(256), 0, st, nv, cols, t, P,
-                       static_cast<const float*>(bias), thr, scale, seed, static_cast<float*>(out));
+                       static_cast<const float*>(bias), thr, scale, seed, idx0, static_cast<const float*>(residual),
+                       static_cast<float*>(out));
+  return hip_status(hipGetLastError());
+}
+
+int check_sum_args(int64_t rows, int64_t cols, int32_t t, int32_t dtype, const void* const* partials) {
+  if (dtype != TP_F32 && dtype != TP_BF16) return TP_EDTYPE;
+  if (rows < 0 || cols < 0 || t < 1 || !partials) return TP_EINVAL;
+  if (t > MAX_PARTIALS) return TP_EUNSUPPORTED;
+  return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_sum_partials(int64_t rows, int64_t cols, int32_t t, int32_t dtype, const void* const* partials,
+                    const void* bias, float p_drop, uint64_t seed, void* out, void* stream) {
+  return tp_sum_partials_residual(rows, cols, t, dtype, partials, bias, p_drop, seed, nullptr, out, stream);
+}
+
+int tp_sum_partials_residual(int64_t rows, int64_t cols, int32_t t, int32_t dtype, const void* const* partials,
+                             const void* bias, float p_drop, uint64_t seed, const void* residual, void* out,
+                             void* stream) {
+  if (int rc = check_sum_args(rows, cols, t, dtype, partials)) return rc;
+  if (!present(out, rows * cols)) return TP_EINVAL;
+  return sum_rows(rows, 0, rows, cols, t, dtype, partials, bias, p_drop, seed, residual, out, stream);
+}
+
+int tp_reduce_scatter(int64_t rows, int64_t cols, int32_t t, int32_t rank, int32_t dtype,
+                      const void* const* partials, const void* bias, float p_drop, uint64_t seed,
+                      const void* residual_r, void* out_r, void* stream) {
+  if (int rc = check_sum_args(rows, cols, t, dtype, partials)) return rc;
+  if (rank < 0 || rank >= t) return TP_EINVAL;
+  if (rows % t) return TP_ENOTDIV;
+  const int64_t n = rows / t;
+  if (!present(out_r, n * cols)) return TP_EINVAL;
+  return sum_rows(rows, rank * n, n, cols, t, dtype, partials, bias, p_drop, seed, residual_r, out_r, stream);
+}
+
+int tp_all_gather(int64_t rows_per_rank, int64_t cols, int32_t t, int32_t dtype, const void* const* slices,
+                  void* out, void* stream) {
+  if (dtype != TP_F32 && dtype != TP_BF16) return TP_EDTYPE;
+  if (rows_per_rank < 0 || cols < 0 || t < 1 || !slices) return TP_EINVAL;
+  if (t > MAX_PARTIALS) return TP_EUNSUPPORTED;
+  const int esz = dtype == TP_BF16 ? 2 : 4;
+  if ((cols * esz) % 16) return TP_EALIGN;
+  const int64_t n = rows_per_rank * cols;
+  if (!present(out, n * t)) return TP_EINVAL;
+  PartialPtrs S{};
+  for (int i = 0; i < t; ++i) {
+    if (!present(slices[i], n)) return TP_EINVAL;
+    if (!aligned16(slices[i])) return TP_EALIGN;
+    S.p[i] = slices[i];
+  }
+  if (!aligned16(out)) return TP_EALIGN;
+  const int64_t nv = n * esz / 16;
+  if (nv == 0) return TP_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Probe pr(st);
+  hipLaunchKernelGGL(gather_kernel, dim3(grid_for(nv * t)), dim3(256), 0, st, nv, t, S, static_cast<u32x4*>(out));
   return hip_status(hipGetLastError());
 }
 

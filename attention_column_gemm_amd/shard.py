@@ -127,13 +127,45 @@ class AttnShard:
         return self.dX
 
 
-def sum_partials(partials, bias=None, p_drop=0.0, seed=0, out=None, stream=None):
-    """Emulated all-reduce of same-shaped device tensors (rank order)."""
+def _shape_dtype(P0):
     torch = _torch()
-    P0 = partials[0]
     rows, cols = P0.shape[0], int(np.prod(P0.shape[1:]))
-    dtype = B.TP_BF16 if P0.dtype == torch.bfloat16 else B.TP_F32
+    return rows, cols, (B.TP_BF16 if P0.dtype == torch.bfloat16 else B.TP_F32)
+
+
+def sum_partials(partials, bias=None, p_drop=0.0, seed=0, out=None, stream=None, residual=None):
+    """Emulated all-reduce of same-shaped device tensors (rank order), with the
+    residual add fused when ``residual`` is given."""
+    torch = _torch()
+    rows, cols, dtype = _shape_dtype(partials[0])
     if out is None:
-        out = torch.empty_like(P0)
-    B.tp_sum_partials(rows, cols, len(partials), dtype, list(partials), bias, p_drop, seed, out, stream)
+        out = torch.empty_like(partials[0])
+    if residual is None:
+        B.tp_sum_partials(rows, cols, len(partials), dtype, list(partials), bias, p_drop, seed, out, stream)
+    else:
+        B.tp_sum_partials_residual(rows, cols, len(partials), dtype, list(partials), bias, p_drop, seed, residual,
+                                   out, stream)
+    return out
+
+
+def reduce_scatter(partials, rank, bias=None, p_drop=0.0, seed=0, residual_r=None, out=None, stream=None):
+    """Rank ``rank``'s token slice of the emulated all-reduce (Megatron-SP first half)."""
+    torch = _torch()
+    rows, cols, dtype = _shape_dtype(partials[0])
+    t = len(partials)
+    if out is None:
+        out = torch.empty((rows // t,) + tuple(partials[0].shape[1:]), dtype=partials[0].dtype,
+                          device=partials[0].device)
+    B.tp_reduce_scatter(rows, cols, t, rank, dtype, list(partials), bias, p_drop, seed, residual_r, out, stream)
+    return out
+
+
+def all_gather(slices, out=None, stream=None):
+    """The full tensor from the ranks' token slices (Megatron-SP second half)."""
+    torch = _torch()
+    rows, cols, dtype = _shape_dtype(slices[0])
+    if out is None:
+        out = torch.empty((rows * len(slices),) + tuple(slices[0].shape[1:]), dtype=slices[0].dtype,
+                          device=slices[0].device)
+    B.tp_all_gather(rows, cols, len(slices), dtype, list(slices), out, stream)
     return out

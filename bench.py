@@ -14,7 +14,11 @@ time of the MLP shard's forward and backward calls) and its fraction of the
 MI355X bf16 dense matrix-core peak; every kernel's time, the emulated
 all-reduces' HBM bandwidth and the attention shard are reported beside it.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg5|cfg3|cfg2] [--no-cpu]
+Beside it, outside the step, the block-closing all-reduce with the residual
+add fused and its Megatron-SP split (one rank's reduce-scatter, the
+all-gather) are timed at the same [T, h] shape.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg5|cfg3|cfg2] [--no-cpu] [--no-extras]
 """
 from __future__ import annotations
 
@@ -119,6 +123,45 @@ def kernel_plan(mc, ac):
     return plan
 
 
+def time_split_and_residual(torch, mc, partials, residual, bias, reps=10):
+    """The block-closing all-reduce with the residual fused, and its
+    Megatron-SP split (one rank's reduce-scatter, the all-gather), at the
+    workload's [T, h] shape; HBM bytes each call must move."""
+    from attention_column_gemm_amd.shard import all_gather, reduce_scatter, sum_partials
+    t, T, h = mc.t, mc.tokens, mc.h
+    d = 2 if mc.bf16 else 4
+    n = T // t
+    out = torch.empty_like(partials[0])
+    sl = torch.empty((n, h), dtype=partials[0].dtype, device="cuda")
+    slices = [sl] + [sl.clone() for _ in range(t - 1)]
+    full = torch.empty_like(partials[0])
+    calls = {
+        "allreduce_residual_fused": (lambda: sum_partials(partials, bias, mc.p_drop, mc.seed, out=out,
+                                                          residual=residual),
+                                     (t + 2) * T * h * d + (h * d if bias is not None else 0), "f3"),
+        "sp_reduce_scatter_rank0": (lambda: reduce_scatter(partials, 0, bias, mc.p_drop, mc.seed,
+                                                           residual_r=residual[:n], out=sl),
+                                    T * h * d + 2 * n * h * d + (h * d if bias is not None else 0), "f2"),
+        "sp_all_gather": (lambda: all_gather(slices, out=full), 2 * T * h * d, "f2"),
+    }
+    res = []
+    for name, (fn, nbytes, row) in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        res.append({"kernel": name, "row": row, "avg_ms": round(ms, 5), "bytes": nbytes,
+                    "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                    "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
+    return res
+
+
 def cpu_baseline(mc, X, dOut, w, budget_s=12.0):
     """The float64 oracle on a bounded token slice of the same rank-0 shard."""
     import numpy as np
@@ -167,6 +210,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="cfg5", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the separate timing of the fused-residual all-reduce and its reduce-scatter / "
+                         "all-gather split (profiling runs: keeps the step's kernels last)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (a known-size reference for "
                          "HBM traffic counters); not part of the timed region")
@@ -356,6 +402,8 @@ def main():
         res["attention_fwd_tflops"] = round(af / (span["attention_fwd_and_allreduce"] * 1e-3) / 1e12, 2)
         ab = I.ATTN_CONFIGS[acid].flops_bwd_per_rank()
         res["attention_bwd_tflops"] = round(ab / (span["attention_bwd"] * 1e-3) / 1e12, 2)
+    if mc.tokens % mc.t == 0 and not args.no_extras:
+        res["split_and_residual"] = time_split_and_residual(torch, mc, [mlp.Z] + z_others, mlp.X, b2)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 2
         src = torch.empty(n, dtype=torch.bfloat16, device="cuda").fill_(1.0)

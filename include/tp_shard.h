@@ -72,7 +72,7 @@ typedef struct {
   int32_t act;      /* tp_act */
 } tp_mlp_desc;
 
-/* One rank's attention shard (forward). */
+/* One rank's attention shard (forward and backward). */
 typedef struct {
   int64_t b, s, h;  /* sequences, sequence length, hidden size; T = b*s */
   int32_t n_q;      /* query heads of the whole layer */
@@ -224,6 +224,54 @@ int tp_attn_shard_bwd(const tp_attn_desc* desc, const void* dZ, const void* X, c
  */
 int tp_sum_partials(int64_t rows, int64_t cols, int32_t t, int32_t dtype, const void* const* partials,
                     const void* bias, float p_drop, uint64_t seed, void* out, void* stream);
+
+/*
+ * tp_sum_partials_residual -- the block-closing all-reduce with the residual
+ * add fused ([LP] II.III Computational Details: fused bias + dropout +
+ * residual add, fused all-reduce + residual add).
+ *
+ *   out = residual + Dropout_{p, seed}( sum_{i=0}^{t-1} partials[i] + bias )
+ * As tp_sum_partials, with the residual (the block's input, [rows, cols],
+ * same dtype, or NULL for none) added once, after dropout.  out may alias the
+ * residual (in-place residual stream) but none of the partials.
+ */
+int tp_sum_partials_residual(int64_t rows, int64_t cols, int32_t t, int32_t dtype, const void* const* partials,
+                             const void* bias, float p_drop, uint64_t seed, const void* residual, void* out,
+                             void* stream);
+
+/*
+ * tp_reduce_scatter -- Megatron-SP's split of the block-closing all-reduce,
+ * first half, emulated on one device ([LP] III.III Block Layout Contract).
+ *
+ * Rank `rank`'s token slice, rows [rank*rows/t, (rank+1)*rows/t), of
+ *   residual + Dropout_{p, seed}( sum_i partials[i] + bias )
+ * computed from those rows of the partials only.  The dropout mask of an
+ * element is that of its position in the full [rows, cols] tensor, so the t
+ * slices are exactly the rows of tp_sum_partials_residual's output.
+ * Arguments:
+ *   rows, cols   full tensor shape; rows % t != 0 gives TP_ENOTDIV
+ *   rank         0 <= rank < t
+ *   partials     HOST array of t device pointers, each the FULL [rows, cols] partial
+ *   bias, p_drop, seed  as tp_sum_partials
+ *   residual_r   [rows/t, cols] this rank's slice of the residual, or NULL
+ *   out_r        [rows/t, cols] out
+ */
+int tp_reduce_scatter(int64_t rows, int64_t cols, int32_t t, int32_t rank, int32_t dtype,
+                      const void* const* partials, const void* bias, float p_drop, uint64_t seed,
+                      const void* residual_r, void* out_r, void* stream);
+
+/*
+ * tp_all_gather -- Megatron-SP's second half, at the next block's entry,
+ * emulated on one device ([LP] III.III Block Layout Contract).
+ *
+ *   out = [slices[0]; slices[1]; ...; slices[t-1]]   (rank order, exact copy)
+ * Arguments:
+ *   rows_per_rank, cols  shape of each slice; cols * element size must be a multiple of 16 bytes
+ *   slices       HOST array of t device pointers, each [rows_per_rank, cols]
+ *   out          [t * rows_per_rank, cols]; may alias none of the slices
+ */
+int tp_all_gather(int64_t rows_per_rank, int64_t cols, int32_t t, int32_t dtype, const void* const* slices,
+                  void* out, void* stream);
 
 /*
  * tp_comm_bytes -- host-only all-reduce accounting of one layer per microbatch

@@ -12,7 +12,8 @@ from oracle import comm
 def test_library_exports_every_declared_function():
     names = B.declared_functions()
     assert set(names) >= {"tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_attn_shard_fwd", "tp_attn_shard_bwd",
-                          "tp_sum_partials", "tp_comm_bytes", "tp_status_string"}
+                          "tp_sum_partials", "tp_sum_partials_residual", "tp_reduce_scatter", "tp_all_gather",
+                          "tp_comm_bytes", "tp_status_string"}
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -162,6 +163,31 @@ def test_sum_partials_validation():
     # empty tensors need no storage and launch nothing
     empty = (ctypes.c_void_p * 2)(None, None)
     assert f(0, 8, 2, B.TP_BF16, empty, None, 0.0, 0, None, None) == B.TP_OK
+
+
+def test_residual_and_split_validation():
+    """Every case is invalid, so nothing is launched."""
+    L = B.lib()
+    arr = (ctypes.c_void_p * 2)(A16, A16)
+    R = L.tp_sum_partials_residual
+    assert R(4, 8, 2, 9, arr, None, 0.0, 0, A16, A16, None) == B.TP_EDTYPE
+    assert R(4, 8, 2, B.TP_BF16, arr, None, 0.0, 0, MIS, A16, None) == B.TP_EALIGN   # residual misaligned
+    assert R(4, 8, 2, B.TP_BF16, arr, None, 0.0, 0, A16, None, None) == B.TP_EINVAL  # out missing
+    assert R(4, 8, 2, B.TP_BF16, arr, None, 2.0, 0, A16, A16, None) == B.TP_EINVAL   # p outside [0, 1)
+    S = L.tp_reduce_scatter
+    arr4 = (ctypes.c_void_p * 4)(A16, A16, A16, A16)
+    assert S(6, 8, 4, 0, B.TP_BF16, arr4, None, 0.0, 0, None, A16, None) == B.TP_ENOTDIV  # 6 rows over 4 ranks
+    assert S(8, 8, 4, 4, B.TP_BF16, arr4, None, 0.0, 0, None, A16, None) == B.TP_EINVAL   # rank >= t
+    assert S(8, 12, 4, 0, B.TP_BF16, arr4, None, 0.0, 0, None, A16, None) == B.TP_EALIGN  # cols not a vector multiple
+    assert S(8, 8, 4, 1, B.TP_BF16, arr4, None, 0.0, 0, MIS, A16, None) == B.TP_EALIGN
+    G = L.tp_all_gather
+    assert G(4, 8, 2, 7, arr, A16, None) == B.TP_EDTYPE
+    assert G(4, 6, 2, B.TP_F32, arr, A16, None) == B.TP_EALIGN          # 24-byte rows
+    assert G(4, 8, 2, B.TP_BF16, arr, MIS, None) == B.TP_EALIGN
+    assert G(4, 8, 2, B.TP_BF16, (ctypes.c_void_p * 2)(A16, None), A16, None) == B.TP_EINVAL
+    assert G(4, 8, 65, B.TP_BF16, arr, A16, None) == B.TP_EUNSUPPORTED
+    empty = (ctypes.c_void_p * 2)(None, None)
+    assert G(0, 8, 2, B.TP_BF16, empty, None, None) == B.TP_OK
 
 
 def test_status_strings():
