@@ -27,6 +27,35 @@ from __future__ import annotations
 import numpy as np
 
 
+def shard_heads(n_q: int, n_kv: int, t: int, rank: int):
+    """The heads rank ``rank`` owns: ``(q, kv, q0, kv0)`` -- its number of query
+    and KV heads and the first of each.
+
+    A rank holds whole GQA groups, the query heads with their KV head ([L11]
+    section 4; [LP] I.III).  ``n_kv >= t``: the ``n_kv`` groups are dealt out in
+    rank order, the first ``n_kv % t`` ranks taking one more ([TP1], GQA
+    paragraph: a non-dividing count needs an uneven split).  ``n_kv < t``: each
+    KV head is replicated on ``t / n_kv`` consecutive ranks, which split its
+    query heads evenly ([LP] III.III: when the split is not complete several
+    cards share one KV projection, a parameter replica); this needs ``t`` to be
+    a multiple of ``n_kv`` and the group size a multiple of ``t / n_kv``.
+    """
+    if n_q % n_kv:
+        raise ValueError("n_q must divide by n_kv")
+    group = n_q // n_kv
+    if n_kv >= t:
+        base, extra = divmod(n_kv, t)
+        kv = base + (1 if rank < extra else 0)
+        kv0 = rank * base + min(rank, extra)
+        return kv * group, kv, kv0 * group, kv0
+    if t % n_kv or group % (t // n_kv):
+        raise ValueError("replicated KV heads need t % n_kv == 0 and (n_q/n_kv) % (t/n_kv) == 0")
+    r = t // n_kv
+    g, sub = divmod(rank, r)
+    q = group // r
+    return q, 1, g * group + sub * q, g
+
+
 def _f64(a):
     return np.asarray(a, dtype=np.float64)
 

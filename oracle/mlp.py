@@ -39,12 +39,22 @@ def _f64(a):
     return None if a is None else np.asarray(a, dtype=np.float64)
 
 
-def shard_cols(h_ffn: int, t: int, rank: int) -> slice:
-    """Intermediate columns owned by ``rank`` (an even split; [L11] section 2)."""
-    if h_ffn % t:
-        raise ValueError("h_ffn must divide by t")
-    f = h_ffn // t
-    return slice(rank * f, (rank + 1) * f)
+def shard_cols(h_ffn: int, t: int, rank: int, unit: int = 1) -> slice:
+    """Intermediate columns owned by ``rank``.
+
+    An even split when ``t`` divides ``h_ffn`` ([L11] section 2).  Otherwise
+    ([TP1], GQA paragraph: a non-dividing size needs an uneven split or
+    padding) the columns are cut into contiguous ranges, in rank order, as
+    even as whole ``unit``-column blocks allow: with ``u = h_ffn / unit``
+    blocks, every rank gets ``u // t`` blocks and the first ``u % t`` ranks one
+    more (a rank may get none).  ``unit`` must divide ``h_ffn``.
+    """
+    if h_ffn % unit:
+        raise ValueError("unit must divide h_ffn")
+    u = h_ffn // unit
+    base, extra = divmod(u, t)
+    start = unit * (rank * base + min(rank, extra))
+    return slice(start, start + unit * (base + (1 if rank < extra else 0)))
 
 
 # ----------------------------------------------------------------------------

@@ -491,6 +491,115 @@ def test_attention_backward_shards_match_unsharded():
     np.testing.assert_allclose(dX, full["dX"], rtol=1e-11, atol=1e-12)
 
 
+# ------------------------------------------------------------ uneven shards
+
+def test_uneven_column_split_is_a_partition():
+    for h_ffn, t, unit in [(512, 2, 1), (1000, 3, 8), (24, 2, 8), (40, 8, 8), (13, 4, 1), (12, 5, 4)]:
+        got = [mlp.shard_cols(h_ffn, t, r, unit) for r in range(t)]
+        assert got[0].start == 0 and got[-1].stop == h_ffn
+        for a, b in zip(got, got[1:]):
+            assert a.stop == b.start
+        sizes = [c.stop - c.start for c in got]
+        assert all(sz % unit == 0 for sz in sizes) and max(sizes) - min(sizes) <= unit
+        assert sizes == sorted(sizes, reverse=True)
+        if h_ffn % (t * unit) == 0:
+            assert sizes == [h_ffn // t] * t
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_uneven_mlp_shards_match_unsharded(act):
+    """Uneven (and empty) column shards: Sigma_i Z_i and Sigma_i dX_i equal the
+    unsharded layer, the column pieces of H and dW1 concatenate to it, the row
+    pieces of dW2 stack to it ([L11] sections 2-3 hold for any column split)."""
+    g = _rng(41)
+    T, h, hf = 5, 6, 13
+    X = g.standard_normal((T, h))
+    W1, Wu = g.standard_normal((h, hf)), g.standard_normal((h, hf))
+    W2, b1 = g.standard_normal((hf, h)), g.standard_normal(hf)
+    dOut = g.standard_normal((T, h))
+    wu = Wu if act == "swiglu" else None
+    bb = b1 if act == "gelu" else None
+    full = mlp.forward(X, W1, W2, act=act, Wu=wu, b1=bb)
+    fb = mlp.backward(dOut, X, W1, W2, act=act, Wu=wu, b1=bb)
+    for t in (2, 3, 5, 16):
+        Z = np.zeros((T, h))
+        dX = np.zeros((T, h))
+        Hs, dW1s, dW2s = [], [], []
+        for r in range(t):
+            c = mlp.shard_cols(hf, t, r)
+            fw, bw = mlp.shard_step(dOut, X, W1[:, c], W2[c], act=act, Wu_i=None if wu is None else wu[:, c],
+                                    b1_i=None if bb is None else bb[c])
+            Z += fw["Z"]
+            dX += bw["dX"]
+            Hs.append(fw["H"])
+            dW1s.append(bw["dW1"])
+            dW2s.append(bw["dW2"])
+        np.testing.assert_allclose(Z, full["Y"], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dX, fb["dX"], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(np.concatenate(Hs, 1), full["H"], rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(np.concatenate(dW1s, 1), fb["dW1"], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(np.concatenate(dW2s, 0), fb["dW2"], rtol=1e-12, atol=1e-12)
+
+
+def test_head_split_rules():
+    """Every query head on exactly one rank, with its KV head local; KV heads
+    either dealt out whole or replicated on t/n_kv ranks."""
+    for n_q, n_kv, t in [(8, 2, 2), (12, 3, 2), (10, 5, 4), (8, 2, 4), (16, 4, 8), (32, 8, 8), (6, 6, 4), (8, 1, 8)]:
+        group = n_q // n_kv
+        owner = {}
+        kv_owners = {}
+        for r in range(t):
+            q, kv, q0, kv0 = att.shard_heads(n_q, n_kv, t, r)
+            for j in range(q0, q0 + q):
+                assert j not in owner
+                owner[j] = r
+                assert kv0 <= j // group < kv0 + kv           # the head's KV head is local
+            for gh in range(kv0, kv0 + kv):
+                kv_owners.setdefault(gh, []).append(r)
+        assert sorted(owner) == list(range(n_q))
+        assert sorted(kv_owners) == list(range(n_kv))
+        reps = {len(v) for v in kv_owners.values()}
+        assert reps == ({1} if n_kv >= t else {t // n_kv})
+    for bad in [(8, 3, 2), (12, 4, 8), (8, 2, 6), (8, 4, 6)]:
+        with pytest.raises(ValueError):
+            att.shard_heads(*bad, 0)
+
+
+@pytest.mark.parametrize("n_q,n_kv,t", [(12, 3, 2), (8, 2, 4), (6, 2, 4)])
+def test_uneven_and_replicated_attention_shards_match_unsharded(n_q, n_kv, t):
+    """Sigma_i Z_i = Z and Sigma_i dX_i = dX; the Q column blocks of dWqkv_i
+    are the unsharded dWq columns of the rank's heads; the K/V blocks of the
+    ranks that hold the same (replicated) KV head add up to its unsharded dWk,
+    dWv (the gradient of a parameter replica is reduced over its replicas)."""
+    if n_kv < t and (t % n_kv or (n_q // n_kv) % (t // n_kv)):
+        pytest.skip("not a supported split")
+    g = _rng(42)
+    b, s, h, d = 2, 5, 12, 3
+    X = g.standard_normal((b * s, h))
+    Wq, Wk, Wv = (g.standard_normal((h, n * d)) / 3 for n in (n_q, n_kv, n_kv))
+    Wo = g.standard_normal((n_q * d, h)) / 3
+    dZ = g.standard_normal((b * s, h))
+    full = att.forward(X, Wq, Wk, Wv, Wo, b=b, s=s, n_q=n_q, n_kv=n_kv, d=d)
+    fb = att.backward(dZ, X, Wq, Wk, Wv, Wo, b=b, s=s, n_q=n_q, n_kv=n_kv, d=d)
+    Z, dX = np.zeros_like(full["Z"]), np.zeros_like(fb["dX"])
+    dWk, dWv = np.zeros_like(fb["dWk"]), np.zeros_like(fb["dWv"])
+    for r in range(t):
+        q, kv, q0, kv0 = att.shard_heads(n_q, n_kv, t, r)
+        cq, ck = slice(q0 * d, (q0 + q) * d), slice(kv0 * d, (kv0 + kv) * d)
+        Wqkv = np.concatenate([Wq[:, cq], Wk[:, ck], Wv[:, ck]], 1)
+        Z += att.shard_forward(X, Wqkv, Wo[cq], b=b, s=s, q=q, kv=kv, d=d)["Z"]
+        sh = att.shard_backward(dZ, X, Wqkv, Wo[cq], b=b, s=s, q=q, kv=kv, d=d)
+        dX += sh["dX"]
+        np.testing.assert_allclose(sh["dWqkv"][:, :q * d], fb["dWq"][:, cq], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(sh["dWo"], fb["dWo"][cq], rtol=1e-12, atol=1e-12)
+        dWk[:, ck] += sh["dWqkv"][:, q * d:(q + kv) * d]
+        dWv[:, ck] += sh["dWqkv"][:, (q + kv) * d:]
+    np.testing.assert_allclose(Z, full["Z"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dX, fb["dX"], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dWk, fb["dWk"], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dWv, fb["dWv"], rtol=1e-11, atol=1e-12)
+
+
 # ------------------------------------------- fused residual and Megatron-SP
 
 def _partials(seed, t=4, T=12, h=16):
