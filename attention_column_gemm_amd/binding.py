@@ -74,13 +74,16 @@ def lib() -> ctypes.CDLL:
                                         _VP, _VP, _VP]
         L.tp_all_gather.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.POINTER(_VP), _VP, _VP]
+        L.tp_mlp_shard_cols.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+        L.tp_attn_shard_heads.argtypes = [ctypes.c_int32] * 4 + [ctypes.POINTER(ctypes.c_int32)] * 4
         L.tp_comm_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.POINTER(tp_comm)]
         L.tp_status_string.argtypes = [ctypes.c_int]
         L.tp_status_string.restype = ctypes.c_char_p
         for name in ("tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_attn_shard_fwd", "tp_attn_shard_bwd",
                      "tp_sum_partials", "tp_sum_partials_residual", "tp_reduce_scatter", "tp_all_gather",
-                     "tp_comm_bytes"):
+                     "tp_mlp_shard_cols", "tp_attn_shard_heads", "tp_comm_bytes"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -175,6 +178,22 @@ def tp_all_gather(rows_per_rank: int, cols: int, t: int, dtype: int, slices, out
     arr = (_VP * max(1, len(slices)))(*[_ptr(p) for p in slices])
     _check(lib().tp_all_gather(int(rows_per_rank), int(cols), int(t), int(dtype), arr, _ptr(out), _stream(stream)),
            "tp_all_gather")
+
+
+def tp_mlp_shard_cols(h_ffn: int, t: int, rank: int, dtype: int):
+    """(f_i, col0): the intermediate columns rank ``rank`` owns."""
+    f, c0 = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().tp_mlp_shard_cols(int(h_ffn), int(t), int(rank), int(dtype), ctypes.byref(f), ctypes.byref(c0)),
+           "tp_mlp_shard_cols")
+    return f.value, c0.value
+
+
+def tp_attn_shard_heads(n_q: int, n_kv: int, t: int, rank: int):
+    """(q_i, kv_i, q0, kv0): the heads rank ``rank`` owns."""
+    v = [ctypes.c_int32() for _ in range(4)]
+    _check(lib().tp_attn_shard_heads(int(n_q), int(n_kv), int(t), int(rank), *[ctypes.byref(x) for x in v]),
+           "tp_attn_shard_heads")
+    return tuple(x.value for x in v)
 
 
 def tp_comm_bytes(tokens: int, h: int, t: int, delta: int) -> tp_comm:

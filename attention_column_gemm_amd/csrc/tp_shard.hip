@@ -148,9 +148,9 @@ hipError_t colsum(int64_t rows, int64_t cols, const void* X, float* out, hipStre
 }
 
 template <class T>
-int mlp_fwd_impl(const tp_mlp_desc& d, const void* X, const void* W1, const void* Wu, const void* b1,
+int mlp_fwd_impl(const tp_mlp_desc& d, int f, const void* X, const void* W1, const void* Wu, const void* b1,
                  const void* W2, void* saved, void* H, void* Z, hipStream_t st) {
-  const int T_ = (int)d.tokens, h = (int)d.h, f = (int)(d.h_ffn / d.t);
+  const int T_ = (int)d.tokens, h = (int)d.h;
   hipError_t e;
   if (d.act == TP_GELU) {
     EpiGeluFwd<T> epi{static_cast<T*>(saved), static_cast<T*>(H), static_cast<const T*>(b1), f, T_, f};
@@ -166,10 +166,10 @@ int mlp_fwd_impl(const tp_mlp_desc& d, const void* X, const void* W1, const void
 }
 
 template <class T>
-int mlp_bwd_impl(const tp_mlp_desc& d, const void* dOut, uint32_t thr, float scale, uint64_t seed,
+int mlp_bwd_impl(const tp_mlp_desc& d, int f, const void* dOut, uint32_t thr, float scale, uint64_t seed,
                  const void* X, const void* W1, const void* Wu, const void* W2, const void* saved, const void* H,
                  void* dY, float* db2, void* dA, float* dW1, float* db1, float* dW2, void* dX, hipStream_t st) {
-  const int T_ = (int)d.tokens, h = (int)d.h, f = (int)(d.h_ffn / d.t);
+  const int T_ = (int)d.tokens, h = (int)d.h;
   const int64_t Tf = (int64_t)T_ * f;
   hipError_t e = hipSuccess;
   // a4: dropout backward (or a copy when dY is requested with p = 0)
@@ -226,19 +226,53 @@ int mlp_bwd_impl(const tp_mlp_desc& d, const void* dOut, uint32_t thr, float sca
 // 32-bit byte offsets; every operand must stay below 2 GiB.
 bool buffer_ok(int64_t elems, int64_t elem_bytes) { return elems * elem_bytes < ((int64_t)1 << 31); }
 
-int validate_mlp(const tp_mlp_desc* d, bool* bf16) {
+// This rank's intermediate columns: contiguous blocks of `unit` columns,
+// dealt out in rank order as evenly as whole blocks allow (the first
+// (h_ffn/unit) % t ranks take one block more); an even split when t divides
+// h_ffn/unit.
+void mlp_cols(int64_t h_ffn, int t, int rank, int unit, int64_t* f, int64_t* col0) {
+  const int64_t u = h_ffn / unit, base = u / t, extra = u % t;
+  *f = unit * (base + (rank < extra ? 1 : 0));
+  *col0 = unit * (rank * base + (rank < extra ? rank : extra));
+}
+
+int validate_mlp(const tp_mlp_desc* d, bool* bf16, int64_t* f) {
   if (!d) return TP_EINVAL;
   if (d->dtype != TP_F32 && d->dtype != TP_BF16) return TP_EDTYPE;
   if (d->act != TP_GELU && d->act != TP_SWIGLU) return TP_EDTYPE;
   if (d->t < 1 || d->rank < 0 || d->rank >= d->t) return TP_EINVAL;
   if (!fits_int(d->tokens) || !fits_int(d->h) || !fits_int(d->h_ffn)) return TP_EINVAL;
-  if (d->h_ffn % d->t) return TP_ENOTDIV;
   *bf16 = d->dtype == TP_BF16;
   const int vec = *bf16 ? 8 : 4;
-  if (d->h % vec || (d->h_ffn / d->t) % vec) return TP_EALIGN;
-  const int64_t f = d->h_ffn / d->t;
-  if (*bf16 && (!buffer_ok(d->tokens * d->h, 2) || !buffer_ok(d->tokens * f, 2) || !buffer_ok(d->h * f, 2)))
+  if (d->h % vec || d->h_ffn % vec) return TP_EALIGN;
+  int64_t col0;
+  mlp_cols(d->h_ffn, d->t, d->rank, vec, f, &col0);
+  if (*bf16 && (!buffer_ok(d->tokens * d->h, 2) || !buffer_ok(d->tokens * *f, 2) || !buffer_ok(d->h * *f, 2)))
     return TP_EUNSUPPORTED;
+  return TP_OK;
+}
+
+// This rank's heads: q query heads from q0 and kv KV heads from kv0.  Whole
+// GQA groups are dealt out when n_kv >= t (the first n_kv % t ranks take one
+// more); when n_kv < t each KV head is replicated on t / n_kv consecutive
+// ranks that split its query heads evenly.
+int attn_heads(int n_q, int n_kv, int t, int rank, int* q, int* kv, int* q0, int* kv0) {
+  if (n_q % n_kv) return TP_ENOTDIV;
+  const int group = n_q / n_kv;
+  if (n_kv >= t) {
+    const int base = n_kv / t, extra = n_kv % t;
+    *kv = base + (rank < extra ? 1 : 0);
+    *kv0 = rank * base + (rank < extra ? rank : extra);
+    *q = *kv * group;
+    *q0 = *kv0 * group;
+    return TP_OK;
+  }
+  const int r = t / n_kv;
+  if (t % n_kv || group % r) return TP_ENOTDIV;
+  *kv = 1;
+  *kv0 = rank / r;
+  *q = group / r;
+  *q0 = *kv0 * group + (rank % r) * *q;
   return TP_OK;
 }
 
@@ -279,6 +313,27 @@ const char* tp_status_string(int s) {
   }
 }
 
+int tp_mlp_shard_cols(int64_t h_ffn, int32_t t, int32_t rank, int32_t dtype, int64_t* f_i, int64_t* col0) {
+  if (dtype != TP_F32 && dtype != TP_BF16) return TP_EDTYPE;
+  if (!f_i || !col0 || h_ffn < 0 || t < 1 || rank < 0 || rank >= t) return TP_EINVAL;
+  const int vec = dtype == TP_BF16 ? 8 : 4;
+  if (h_ffn % vec) return TP_EALIGN;
+  mlp_cols(h_ffn, t, rank, vec, f_i, col0);
+  return TP_OK;
+}
+
+int tp_attn_shard_heads(int32_t n_q, int32_t n_kv, int32_t t, int32_t rank, int32_t* q_i, int32_t* kv_i,
+                        int32_t* q0, int32_t* kv0) {
+  if (!q_i || !kv_i || !q0 || !kv0 || n_q < 1 || n_kv < 1 || t < 1 || rank < 0 || rank >= t) return TP_EINVAL;
+  int q, kv, a, b;
+  if (int rc = attn_heads(n_q, n_kv, t, rank, &q, &kv, &a, &b)) return rc;
+  *q_i = q;
+  *kv_i = kv;
+  *q0 = a;
+  *kv0 = b;
+  return TP_OK;
+}
+
 int tp_comm_bytes(int64_t tokens, int64_t h, int32_t t, int32_t delta, tp_comm* out) {
   if (!out || tokens < 0 || h < 0 || t < 1 || delta < 1) return TP_EINVAL;
   const uint64_t payload = (uint64_t)tokens * (uint64_t)h * (uint64_t)delta;
@@ -294,10 +349,11 @@ int tp_comm_bytes(int64_t tokens, int64_t h, int32_t t, int32_t delta, tp_comm* 
 int tp_mlp_shard_fwd(const tp_mlp_desc* desc, const void* X, const void* W1_i, const void* Wu_i, const void* b1_i,
                      const void* W2_i, void* saved_i, void* H_i, void* Z_i, void* stream) {
   bool bf16 = false;
-  int rc = validate_mlp(desc, &bf16);
+  int64_t f = 0;
+  int rc = validate_mlp(desc, &bf16, &f);
   if (rc) return rc;
   {
-    const int64_t T_ = desc->tokens, h = desc->h, f = desc->h_ffn / desc->t, ns = desc->act == TP_GELU ? 1 : 2;
+    const int64_t T_ = desc->tokens, h = desc->h, ns = desc->act == TP_GELU ? 1 : 2;
     if (!present(X, T_ * h) || !present(W1_i, h * f) || !present(W2_i, f * h) || !present(saved_i, ns * T_ * f) ||
         !present(H_i, T_ * f) || !present(Z_i, T_ * h) || (desc->act == TP_SWIGLU && !present(Wu_i, h * f)))
       return TP_EINVAL;
@@ -305,8 +361,8 @@ int tp_mlp_shard_fwd(const tp_mlp_desc* desc, const void* X, const void* W1_i, c
   if (desc->act == TP_GELU ? (Wu_i != nullptr) : (b1_i != nullptr)) return TP_EINVAL;
   if (!ptrs_aligned({X, W1_i, Wu_i, b1_i, W2_i, saved_i, H_i, Z_i})) return TP_EALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return bf16 ? mlp_fwd_impl<uint16_t>(*desc, X, W1_i, Wu_i, b1_i, W2_i, saved_i, H_i, Z_i, st)
-              : mlp_fwd_impl<float>(*desc, X, W1_i, Wu_i, b1_i, W2_i, saved_i, H_i, Z_i, st);
+  return bf16 ? mlp_fwd_impl<uint16_t>(*desc, (int)f, X, W1_i, Wu_i, b1_i, W2_i, saved_i, H_i, Z_i, st)
+              : mlp_fwd_impl<float>(*desc, (int)f, X, W1_i, Wu_i, b1_i, W2_i, saved_i, H_i, Z_i, st);
 }
 
 int tp_mlp_shard_bwd(const tp_mlp_desc* desc, const void* dOut, float p_drop, uint64_t seed, const void* X,
@@ -314,13 +370,14 @@ int tp_mlp_shard_bwd(const tp_mlp_desc* desc, const void* dOut, float p_drop, ui
                      void* dY, float* db2, void* dA_i, float* dW1_i, float* db1_i, float* dW2_i, void* dX_i,
                      void* stream) {
   bool bf16 = false;
-  int rc = validate_mlp(desc, &bf16);
+  int64_t f = 0;
+  int rc = validate_mlp(desc, &bf16, &f);
   if (rc) return rc;
   uint32_t thr = 0;
   float scale = 1.0f;
   if ((rc = check_dropout(p_drop, &thr, &scale))) return rc;
   {
-    const int64_t T_ = desc->tokens, h = desc->h, f = desc->h_ffn / desc->t, ns = desc->act == TP_GELU ? 1 : 2;
+    const int64_t T_ = desc->tokens, h = desc->h, ns = desc->act == TP_GELU ? 1 : 2;
     if (!present(dOut, T_ * h) || !present(X, T_ * h) || !present(W1_i, h * f) || !present(W2_i, f * h) ||
         !present(saved_i, ns * T_ * f) || !present(H_i, T_ * f) || !present(dA_i, ns * T_ * f) ||
         !present(dW1_i, ns * h * f) || !present(dW2_i, f * h) || !present(dX_i, T_ * h) ||
@@ -332,10 +389,10 @@ int tp_mlp_shard_bwd(const tp_mlp_desc* desc, const void* dOut, float p_drop, ui
   if (!ptrs_aligned({dOut, X, W1_i, Wu_i, W2_i, saved_i, H_i, dY, db2, dA_i, dW1_i, db1_i, dW2_i, dX_i}))
     return TP_EALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return bf16 ? mlp_bwd_impl<uint16_t>(*desc, dOut, thr, scale, seed, X, W1_i, Wu_i, W2_i, saved_i, H_i, dY,
-                                       db2, dA_i, dW1_i, db1_i, dW2_i, dX_i, st)
-              : mlp_bwd_impl<float>(*desc, dOut, thr, scale, seed, X, W1_i, Wu_i, W2_i, saved_i, H_i, dY, db2,
-                                    dA_i, dW1_i, db1_i, dW2_i, dX_i, st);
+  return bf16 ? mlp_bwd_impl<uint16_t>(*desc, (int)f, dOut, thr, scale, seed, X, W1_i, Wu_i, W2_i, saved_i, H_i,
+                                       dY, db2, dA_i, dW1_i, db1_i, dW2_i, dX_i, st)
+              : mlp_bwd_impl<float>(*desc, (int)f, dOut, thr, scale, seed, X, W1_i, Wu_i, W2_i, saved_i, H_i, dY,
+                                    db2, dA_i, dW1_i, db1_i, dW2_i, dX_i, st);
 }
 
 // Descriptor checks shared by the attention entry points.
@@ -345,10 +402,17 @@ int check_attn_desc(const tp_attn_desc* d) {
   if (d->b < 0 || d->s < 0 || d->h < 0 || d->n_q < 1 || d->n_kv < 1 || d->d < 1 || d->t < 1 || d->rank < 0 ||
       d->rank >= d->t)
     return TP_EINVAL;
-  if (d->n_q % d->t || d->n_kv % d->t || d->n_q % d->n_kv) return TP_ENOTDIV;
+  int q, kv, q0, kv0;
+  if (int rc = attn_heads(d->n_q, d->n_kv, d->t, d->rank, &q, &kv, &q0, &kv0)) return rc;
   if (d->d != 64 && d->d != 128) return TP_EUNSUPPORTED;
   if (!fits_int(d->b * d->s) || !fits_int(d->h)) return TP_EINVAL;
   return TP_OK;
+}
+
+// This rank's query and KV head counts (the descriptor has been checked).
+void local_heads(const tp_attn_desc* d, int* q, int* kv) {
+  int q0, kv0;
+  attn_heads(d->n_q, d->n_kv, d->t, d->rank, q, kv, &q0, &kv0);
 }
 
 // Query heads per work-group of the attention kernels: four, two or one, so
@@ -358,8 +422,10 @@ int heads_per_wg(int group) { return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 
 int tp_attn_shard_fwd(const tp_attn_desc* d, const void* X, const void* Wqkv_i, const void* Wo_i, void* QKV_i,
                       void* O_i, float* lse_i, void* Z_i, void* stream) {
   if (int rc = check_attn_desc(d)) return rc;
+  int q, kv;
+  local_heads(d, &q, &kv);
   {
-    const int64_t T_ = d->b * d->s, nq = (int64_t)(d->n_q / d->t) * d->d, nkv = (int64_t)(d->n_kv / d->t) * d->d;
+    const int64_t T_ = d->b * d->s, nq = (int64_t)q * d->d, nkv = (int64_t)kv * d->d;
     if (!present(X, T_ * d->h) || !present(Wqkv_i, d->h * (nq + 2 * nkv)) || !present(Wo_i, nq * d->h) ||
         !present(QKV_i, T_ * (nq + 2 * nkv)) || !present(O_i, T_ * nq) || !present(Z_i, T_ * d->h))
       return TP_EINVAL;
@@ -367,10 +433,10 @@ int tp_attn_shard_fwd(const tp_attn_desc* d, const void* X, const void* Wqkv_i, 
   if (d->h % 8) return TP_EALIGN;
   if (!ptrs_aligned({X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, Z_i})) return TP_EALIGN;
   {
-    const int64_t T_ = d->b * d->s, nqkv = (int64_t)(d->n_q + 2 * d->n_kv) / d->t * d->d;
+    const int64_t T_ = d->b * d->s, nqkv = (int64_t)(q + 2 * kv) * d->d;
     if (!buffer_ok(T_ * d->h, 2) || !buffer_ok(T_ * nqkv, 2) || !buffer_ok(d->h * nqkv, 2)) return TP_EUNSUPPORTED;
   }
-  const int q = d->n_q / d->t, kv = d->n_kv / d->t, D = d->d;
+  const int D = d->d;
   const int T_ = (int)(d->b * d->s), h = (int)d->h;
   const int nqkv = (q + 2 * kv) * D;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -407,8 +473,10 @@ int tp_attn_shard_bwd(const tp_attn_desc* d, const void* dZ, const void* X, cons
                       const void* QKV_i, const void* O_i, const float* lse_i, void* dO_i, float* stats_i,
                       void* dQKV_i, float* dWqkv_i, float* dWo_i, void* dX_i, void* stream) {
   if (int rc = check_attn_desc(d)) return rc;
-  const int64_t T64 = d->b * d->s, nq64 = (int64_t)(d->n_q / d->t) * d->d;
-  const int64_t nqkv64 = (int64_t)(d->n_q + 2 * d->n_kv) / d->t * d->d, rows64 = d->b * (d->n_q / d->t) * d->s;
+  int q, kv;
+  local_heads(d, &q, &kv);
+  const int64_t T64 = d->b * d->s, nq64 = (int64_t)q * d->d;
+  const int64_t nqkv64 = (int64_t)(q + 2 * kv) * d->d, rows64 = d->b * (int64_t)q * d->s;
   if (!present(dZ, T64 * d->h) || !present(X, T64 * d->h) || !present(Wqkv_i, d->h * nqkv64) ||
       !present(Wo_i, nq64 * d->h) || !present(QKV_i, T64 * nqkv64) || !present(O_i, T64 * nq64) ||
       !present(lse_i, rows64) || !present(dO_i, T64 * nq64) || !present(stats_i, 2 * rows64) ||
@@ -421,7 +489,7 @@ int tp_attn_shard_bwd(const tp_attn_desc* d, const void* dZ, const void* X, cons
   if (!buffer_ok(T64 * d->h, 2) || !buffer_ok(T64 * nqkv64, 2) || !buffer_ok(d->h * nqkv64, 2) ||
       !buffer_ok(2 * rows64, 4))
     return TP_EUNSUPPORTED;
-  const int q = d->n_q / d->t, kv = d->n_kv / d->t, D = d->d;
+  const int D = d->d;
   const int T_ = (int)T64, h = (int)d->h, nq = q * D, nqkv = (q + 2 * kv) * D;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // dO_i = dZ Wo_i^T (Wo_i [q d, h] is K-contiguous for this product)

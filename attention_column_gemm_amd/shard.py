@@ -39,7 +39,7 @@ class MLPShard:
         torch = _torch()
         self.torch = torch
         self.tokens, self.h, self.h_ffn, self.t, self.rank = tokens, h, h_ffn, t, rank
-        self.f = h_ffn // t
+        self.f, self.col0 = B.tp_mlp_shard_cols(h_ffn, t, rank, B.TP_BF16 if dtype == "bf16" else B.TP_F32)
         self.act, self.dtype = act, dtype
         self.tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.desc = B.mlp_desc(tokens, h, h_ffn, t, rank, B.TP_BF16 if dtype == "bf16" else B.TP_F32,
@@ -86,7 +86,7 @@ class AttnShard:
     def __init__(self, b, s, h, n_q, n_kv, d, t, rank, causal=True, device="cuda"):
         torch = _torch()
         self.b, self.s, self.h, self.n_q, self.n_kv, self.d, self.t, self.rank = b, s, h, n_q, n_kv, d, t, rank
-        self.q, self.kv = n_q // t, n_kv // t
+        self.q, self.kv, self.q0, self.kv0 = B.tp_attn_shard_heads(n_q, n_kv, t, rank)
         self.desc = B.attn_desc(b, s, h, n_q, n_kv, d, t, rank, B.TP_BF16, 1 if causal else 0)
         T = b * s
         e = lambda *shape, dt=torch.bfloat16: torch.empty(*shape, dtype=dt, device=device)

@@ -11,8 +11,9 @@
  *
  * Notation ([L11] section 1; [LP] O.I): T = b*s tokens of a microbatch, hidden
  * size h, MLP intermediate size h_ffn, TP degree t, bytes per element delta;
- * per-rank intermediate width f = h_ffn / t; q = n_q / t local query heads and
- * kv = n_kv / t local KV heads of width d.
+ * per-rank intermediate width f (= h_ffn / t when t divides it; in general
+ * tp_mlp_shard_cols), q local query heads and kv local KV heads of width d
+ * (= n_q / t and n_kv / t when t divides them; in general tp_attn_shard_heads).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -27,8 +28,8 @@
  *  - Storage type: TP_F32 means every activation, weight and bias is fp32;
  *    TP_BF16 means they are bf16 (products accumulate in fp32).  Weight and
  *    bias gradients (dW*, db*) are always fp32.
- *  - For TP_BF16 the sizes h, f, (q + 2 kv) d and q d must be multiples of 8;
- *    for TP_F32 multiples of 4 (vector width of 16 bytes).
+ *  - For TP_BF16 the sizes h, h_ffn, (q + 2 kv) d and q d must be multiples of
+ *    8; for TP_F32 multiples of 4 (vector width of 16 bytes).
  *  - Every launch is asynchronous on `stream` (a hipStream_t passed as void*;
  *    NULL is the default stream).  Arguments are validated before any launch:
  *    on a negative return nothing was enqueued.  Nothing is printed and no
@@ -54,7 +55,7 @@ typedef enum { TP_GELU = 0, TP_SWIGLU = 1 } tp_act;
 enum {
   TP_OK = 0,
   TP_EINVAL = -1,       /* NULL for a required non-empty tensor, size < 0, t < 1, rank >= t, p outside [0,1) */
-  TP_ENOTDIV = -2,      /* h_ffn % t, n_q % t, n_kv % t or n_q % n_kv is not 0 */
+  TP_ENOTDIV = -2,      /* a split the shard rules do not cover (see tp_attn_shard_heads; rows % t for the reduce-scatter) */
   TP_EDTYPE = -3,       /* unknown dtype/activation, or a combination not provided (attention in fp32) */
   TP_EALIGN = -4,       /* a pointer is not 16-byte aligned or a width is not a multiple of the vector width */
   TP_EHIP = -5,         /* the HIP runtime reported an error when enqueuing a kernel */
@@ -65,7 +66,7 @@ enum {
 typedef struct {
   int64_t tokens;   /* T = b*s */
   int64_t h;        /* hidden size */
-  int64_t h_ffn;    /* full intermediate size; this rank holds f = h_ffn / t columns */
+  int64_t h_ffn;    /* full intermediate size; this rank holds f columns (tp_mlp_shard_cols) */
   int32_t t;        /* TP degree (1 = unsharded layer) */
   int32_t rank;     /* which slice this shard is, 0 <= rank < t (informational for the MLP) */
   int32_t dtype;    /* tp_dtype */
@@ -95,6 +96,44 @@ typedef struct {
 } tp_comm;
 
 /*
+ * tp_mlp_shard_cols -- the intermediate columns a rank owns (host only).
+ * ([L11] section 2 for the even split; [TP1], GQA paragraph: a size that t
+ * does not divide needs an uneven split.)
+ * The h_ffn columns are cut into contiguous blocks of the storage vector (8
+ * bf16 or 4 fp32 columns) dealt out in rank order as evenly as whole blocks
+ * allow: with u = h_ffn / vec blocks, rank i gets u / t blocks, plus one if
+ * i < u % t (a rank may get none; its partials are then zero).  f_i and col0
+ * are this rank's width and first column; f_i = h_ffn / t when t * vec
+ * divides h_ffn.  Every MLP entry point uses this split for desc->rank.
+ * Errors: TP_EDTYPE, TP_EINVAL (NULL output, h_ffn < 0, rank outside
+ * [0, t)), TP_EALIGN (h_ffn not a multiple of the vector width).
+ */
+int tp_mlp_shard_cols(int64_t h_ffn, int32_t t, int32_t rank, int32_t dtype, int64_t* f_i, int64_t* col0);
+
+/*
+ * tp_attn_shard_heads -- the heads a rank owns (host only).
+ * ([L11] section 4 and [LP] I.III: a rank holds whole GQA groups; [TP1], GQA
+ * paragraph: uneven split when the count does not divide; [LP] III.III: when
+ * the split cannot be complete, several ranks share one KV projection, a
+ * parameter replica.)
+ *   n_kv >= t: the n_kv groups are dealt out in rank order, rank i taking
+ *              n_kv / t of them plus one if i < n_kv % t, with all their
+ *              n_q / n_kv query heads each;
+ *   n_kv <  t: KV head g is replicated on the r = t / n_kv ranks g*r ..
+ *              g*r + r - 1, which take (n_q / n_kv) / r of its query heads each
+ *              (needs t % n_kv == 0 and (n_q / n_kv) % r == 0).
+ * q_i, kv_i: this rank's query / KV head counts; q0, kv0: the first of each.
+ * With replicated KV heads the K and V column blocks of tp_attn_shard_bwd's
+ * dWqkv_i are this rank's share of that replica's gradient: the ranks that
+ * hold the same KV head add them.  Every attention entry point uses this
+ * split for desc->rank.
+ * Errors: TP_EINVAL (NULL output, counts < 1, rank outside [0, t)),
+ * TP_ENOTDIV (n_q % n_kv != 0, or a replication the rule above does not cover).
+ */
+int tp_attn_shard_heads(int32_t n_q, int32_t n_kv, int32_t t, int32_t rank, int32_t* q_i, int32_t* kv_i,
+                        int32_t* q0, int32_t* kv0);
+
+/*
  * tp_mlp_shard_fwd -- forward of one rank's MLP shard
  * ([L11] sections 2-3; [TP1] column split and "MLP and attention"; [HJ] TP forward).
  *
@@ -104,7 +143,7 @@ typedef struct {
  *   GeLU:   A_i = X W1_i + b1_i;  H_i = GeLU(A_i)
  *   SwiGLU: G_i = X W1_i;  U_i = X Wu_i;  H_i = SiLU(G_i) * U_i
  *   Z_i = H_i W2_i
- * Arguments (T = tokens, f = h_ffn / t):
+ * Arguments (T = tokens, f = this rank's width, tp_mlp_shard_cols):
  *   X     [T, h]   replicated input
  *   W1_i  [h, f]   first-layer columns of this rank (the gate for SwiGLU)
  *   Wu_i  [h, f]   SwiGLU up-projection columns; must be NULL for GeLU

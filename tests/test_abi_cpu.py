@@ -6,7 +6,9 @@ import ctypes
 import pytest
 
 from attention_column_gemm_amd import binding as B
+from oracle import attention as OA
 from oracle import comm
+from oracle import mlp as OM
 
 
 def test_library_exports_every_declared_function():
@@ -65,9 +67,9 @@ def _fwd(desc, **ptrs):
     (_mlp(rank=2), {}, B.TP_EINVAL),
     (_mlp(t=0), {}, B.TP_EINVAL),
     (_mlp(tokens=-1), {}, B.TP_EINVAL),
-    (_mlp(h_ffn=513), {}, B.TP_ENOTDIV),
+    (_mlp(h_ffn=513), {}, B.TP_EALIGN),
     (_mlp(h=100), {}, B.TP_EALIGN),
-    (_mlp(h_ffn=2 * 12), {}, B.TP_EALIGN),
+    (_mlp(h_ffn=20), {}, B.TP_EALIGN),
     (_mlp(), {"X": None}, B.TP_EINVAL),
     (_mlp(), {"Wu": A16}, B.TP_EINVAL),
     (_mlp(act=B.TP_SWIGLU), {"Wu": None}, B.TP_EINVAL),
@@ -163,6 +165,31 @@ def test_sum_partials_validation():
     # empty tensors need no storage and launch nothing
     empty = (ctypes.c_void_p * 2)(None, None)
     assert f(0, 8, 2, B.TP_BF16, empty, None, 0.0, 0, None, None) == B.TP_OK
+
+
+def test_shard_split_helpers_match_the_oracle_rules():
+    """The library's uneven-split rules (host only) against the oracle's."""
+    L = B.lib()
+    f, c0 = ctypes.c_int64(), ctypes.c_int64()
+    for h_ffn, t in [(512, 2), (1000, 3), (24, 2), (40, 8), (28672, 8), (11008, 8), (16, 5), (0, 3)]:
+        for dtype, unit in ((B.TP_BF16, 8), (B.TP_F32, 4)):
+            for r in range(t):
+                assert L.tp_mlp_shard_cols(h_ffn, t, r, dtype, ctypes.byref(f), ctypes.byref(c0)) == B.TP_OK
+                want = OM.shard_cols(h_ffn, t, r, unit)
+                assert (c0.value, c0.value + f.value) == (want.start, want.stop)
+    assert L.tp_mlp_shard_cols(100, 2, 0, B.TP_BF16, ctypes.byref(f), ctypes.byref(c0)) == B.TP_EALIGN
+    assert L.tp_mlp_shard_cols(64, 2, 2, B.TP_BF16, ctypes.byref(f), ctypes.byref(c0)) == B.TP_EINVAL
+    assert L.tp_mlp_shard_cols(64, 2, 0, 9, ctypes.byref(f), ctypes.byref(c0)) == B.TP_EDTYPE
+    assert L.tp_mlp_shard_cols(64, 2, 0, B.TP_BF16, None, ctypes.byref(c0)) == B.TP_EINVAL
+    q, kv, q0, kv0 = (ctypes.c_int32() for _ in range(4))
+    refs = [ctypes.byref(x) for x in (q, kv, q0, kv0)]
+    for n_q, n_kv, t in [(64, 8, 8), (32, 8, 8), (12, 3, 2), (10, 5, 3), (8, 2, 4), (16, 2, 8), (8, 1, 8), (6, 6, 4)]:
+        for r in range(t):
+            assert L.tp_attn_shard_heads(n_q, n_kv, t, r, *refs) == B.TP_OK
+            assert (q.value, kv.value, q0.value, kv0.value) == OA.shard_heads(n_q, n_kv, t, r)
+    for n_q, n_kv, t in [(8, 3, 2), (12, 4, 8), (8, 2, 6), (8, 4, 6)]:
+        assert L.tp_attn_shard_heads(n_q, n_kv, t, 0, *refs) == B.TP_ENOTDIV
+    assert L.tp_attn_shard_heads(8, 2, 2, 2, *refs) == B.TP_EINVAL
 
 
 def test_residual_and_split_validation():

@@ -565,7 +565,7 @@ def test_head_split_rules():
             att.shard_heads(*bad, 0)
 
 
-@pytest.mark.parametrize("n_q,n_kv,t", [(12, 3, 2), (8, 2, 4), (6, 2, 4)])
+@pytest.mark.parametrize("n_q,n_kv,t", [(12, 3, 2), (8, 2, 4), (16, 2, 8), (10, 5, 3)])
 def test_uneven_and_replicated_attention_shards_match_unsharded(n_q, n_kv, t):
     """Sigma_i Z_i = Z and Sigma_i dX_i = dX; the Q column blocks of dWqkv_i
     are the unsharded dWq columns of the rank's heads; the K/V blocks of the
