@@ -16,7 +16,8 @@ all-reduces' HBM bandwidth and the attention shard are reported beside it.
 
 Beside it, outside the step, the block-closing all-reduce with the residual
 add fused and its Megatron-SP split (one rank's reduce-scatter, the
-all-gather) are timed at the same [T, h] shape.
+all-gather) are timed at the same [T, h] shape, and rank 0 of two uneven
+splits (an FFN width t does not divide, KV heads replicated over ranks).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg5|cfg3|cfg2] [--no-cpu] [--no-extras]
 """
@@ -160,6 +161,52 @@ def time_split_and_residual(torch, mc, partials, residual, bias, reps=10):
                     "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
                     "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
     return res
+
+
+def time_uneven_shards(torch, reps=5):
+    """Uneven splits run the same kernels on the rank's own share: the Llama
+    SwiGLU MLP (T=4096, h=4096, h_ffn=11008) over t=3 ranks (widths 3672,
+    3672, 3664) and the full-layer attention (64 q / 8 kv heads, d=128) over
+    t=16 ranks (each KV head replicated on two ranks), rank 0, fwd+bwd."""
+    import numpy as np
+    from attention_column_gemm_amd import inputs as I
+    from attention_column_gemm_amd.shard import AttnShard, MLPShard, to_device
+    out = []
+    rng = np.random.default_rng(0)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    T, h, hf, t = 4096, 4096, 11008, 3
+    sh = MLPShard(T, h, hf, t, 0, act="swiglu", dtype="bf16")
+    g = lambda *shape, std=0.02: I.round_to_bf16(rng.standard_normal(shape).astype(np.float32) * std)
+    sh.load(g(T, h, std=1.0), g(h, sh.f), g(h, sh.f), None, g(sh.f, h), g(T, h, std=1.0))
+    ms = timed(lambda: (sh.forward(), sh.backward(0.0, 0, want_db2=False, want_db1=False)))
+    fl = 18 * T * h * sh.f
+    out.append({"case": f"SwiGLU MLP h_ffn={hf} over t={t}, rank 0 (f={sh.f})", "row": "f4", "avg_ms": round(ms, 4),
+                "tflops": round(fl / (ms * 1e-3) / 1e12, 2)})
+    del sh
+    b, s, h, n_q, n_kv, d, t = 4, 2048, 8192, 64, 8, 128, 16
+    ash = AttnShard(b, s, h, n_q, n_kv, d, t, 0)
+    ash.load(g(b * s, h, std=1.0), g(h, (ash.q + 2 * ash.kv) * d), g(ash.q * d, h))
+    dZ = to_device(g(b * s, h, std=1.0), "bf16")
+    ms = timed(lambda: (ash.forward(), ash.backward(dZ)))
+    ac = I.custom_attn(0, b, s, h, n_q, n_kv, d, t)
+    fl = 3 * (2 * b * s * h * (ash.q + 2 * ash.kv) * d + 2 * b * s * ash.q * d * h
+              + 4 * d * b * ash.q * (s * (s + 1) // 2))
+    out.append({"case": f"attention {n_q}q/{n_kv}kv d={d} over t={t} (KV replicated on 2 ranks), rank 0 "
+                        f"(q={ash.q}, kv={ash.kv})", "row": "f4", "avg_ms": round(ms, 4),
+                "tflops": round(fl / (ms * 1e-3) / 1e12, 2)})
+    return out
 
 
 def cpu_baseline(mc, X, dOut, w, budget_s=12.0):
@@ -404,6 +451,10 @@ def main():
         res["attention_bwd_tflops"] = round(ab / (span["attention_bwd"] * 1e-3) / 1e12, 2)
     if mc.tokens % mc.t == 0 and not args.no_extras:
         res["split_and_residual"] = time_split_and_residual(torch, mc, [mlp.Z] + z_others, mlp.X, b2)
+    if args.workload == "cfg5" and not args.no_extras:
+        del attn, mlp, z_others, dx_others, za_others, dxa_others
+        torch.cuda.empty_cache()
+        res["uneven_shards"] = time_uneven_shards(torch)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 2
         src = torch.empty(n, dtype=torch.bfloat16, device="cuda").fill_(1.0)
