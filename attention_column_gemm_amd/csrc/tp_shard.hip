@@ -76,10 +76,11 @@ GemmProblem problem(int M, int N, int K, const void* A, int64_t lda, const void*
   return p;
 }
 
-// Tile choice: the large tile unless it leaves most of the 256 CUs idle, in
-// which case the quarter-size tile (more work-groups) is used.  Cost model:
-// waves of work-groups x tile area, with the small tile charged 1.3x per
-// element for its lower operand reuse.
+// Tile choice: the large tile (one work-group per CU) unless it would leave
+// more than ~44% of the 256 CUs without a tile; then the quarter-size tile,
+// of which two work-groups share a CU.  Measured on gfx950: with 160 or more
+// large tiles the large tile wins even though some CUs idle (a partly idle
+// chip clocks higher), with 128 or fewer the small tile wins.
 // TPSHARD_TILE=large|small overrides the choice (used by the tests to cover
 // both tile shapes at small sizes).
 bool use_small_tile(int M, int N, int bm, int bn) {
@@ -87,12 +88,8 @@ bool use_small_tile(int M, int N, int bm, int bn) {
     if (!std::strcmp(force, "large")) return false;
     if (!std::strcmp(force, "small")) return true;
   }
-  auto waves = [](int64_t tiles) { return (tiles + kNumCUs - 1) / kNumCUs; };
   const int64_t big = (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-  const int64_t small = (int64_t)((M + bm / 2 - 1) / (bm / 2)) * ((N + bn / 2 - 1) / (bn / 2));
-  const double cost_big = (double)waves(big) * bm * bn;
-  const double cost_small = 1.3 * (double)waves(small) * (bm / 2) * (bn / 2);
-  return cost_small < cost_big;
+  return big < (int64_t)kNumCUs * 9 / 16;
 }
 
 template <int AL, int BL, class Epi>
