@@ -171,7 +171,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem
   constexpr int STAGE = A_BYTES + NB * B_BYTES;
   constexpr int NSTAGE = 2, KK = BK / 16;
   static_assert(KK >= 3 && NW % 2 == 0, "staggered issue needs at least three k steps and paired waves");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
+  constexpr int STAGING = WGM * WGN * NB * 32 * ((BN / WGN) * 4 + 16);  // epilogue staging (see below)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE > STAGING ? NSTAGE * STAGE : STAGING];
 
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   int tm, tn;
@@ -274,30 +275,55 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem
     }
   }
 
-  // Epilogue: lane holds, for tile (i, j), row m = .. + (lane & 31) and columns
-  // n = .. + 8*q4 + 4*(lane >> 5) + e, e = 0..3, in accumulator slots 4*q4 + e.
-  // The saved inputs an epilogue reads are loaded for a whole 32-row block
-  // before any of it is consumed.
+  // Epilogue, one 32-row block of the wave's sub-tile at a time, through LDS
+  // (idle once every wave is past the K loop): the wave writes its
+  // accumulators to its own padded region, where lane l holds row l % 32 and
+  // columns 8*q4 + 4*(l / 32) + e of each 32-column tile, and reads them back
+  // so that WN/4 consecutive lanes cover one row, four columns each.  The
+  // epilogue's loads of saved tensors and its stores then move whole
+  // contiguous row segments per instruction, and its saved-tensor loads for
+  // the block are issued before any of them is consumed.
+  constexpr int LPR = WN / 4;           // lanes per staged row
+  constexpr int RPP = 64 / LPR;         // rows per pass
+  constexpr int PASSES = 32 / RPP;
+  constexpr int PITCH = WN * 4 + 16;    // bytes per staged row (16-byte pad: conflict-free writes)
+  static_assert(64 % LPR == 0 && 32 % RPP == 0, "staging layout");
+  static_assert(NW * NB * 32 * PITCH <= sizeof(smem), "staging space");
+  lds::wait_lgkm0();
+  barrier();
+  const uint32_t stage = (uint32_t)(wave * NB * 32 * PITCH);
+  const int srow = lane / LPR, scol = (lane % LPR) * 4;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int m = m0 + wm * WM + i * 32 + (lane & 31);
-    typename Epi::Aux aux[TN][4];
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) epi.load(m, n0 + wn * WN + j * 32 + q4 * 8 + (lane >> 5) * 4, aux[j][q4]);
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 v = {acc[b][i][j][4 * q4], acc[b][i][j][4 * q4 + 1], acc[b][i][j][4 * q4 + 2],
+                           acc[b][i][j][4 * q4 + 3]};
+          const uint32_t off = stage + (uint32_t)(b * 32 * PITCH + (lane & 31) * PITCH +
+                                                  (j * 32 + q4 * 8 + (lane >> 5) * 4) * 4);
+          *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(const_cast<lds_u8*>(lds) + off) = v;
+        }
+    typename Epi::Aux aux[PASSES];
+    const int mb = m0 + wm * WM + i * 32, n = n0 + wn * WN + scol;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int n = n0 + wn * WN + j * 32 + q4 * 8 + (lane >> 5) * 4;
-        float v[NB][4];
+    for (int ps = 0; ps < PASSES; ++ps) epi.load(mb + ps * RPP + srow, n, aux[ps]);
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+    for (int ps = 0; ps < PASSES; ++ps) {
+      float v[NB][4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[b][e] = acc[b][i][j][q4 * 4 + e];
-        epi(m, n, v, aux[j][q4]);
+      for (int b = 0; b < NB; ++b) {
+        const uint32_t off = stage + (uint32_t)(b * 32 * PITCH + (ps * RPP + srow) * PITCH + scol * 4);
+        const f32x4 x = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(lds + off);
+        v[b][0] = x[0];
+        v[b][1] = x[1];
+        v[b][2] = x[2];
+        v[b][3] = x[3];
       }
+      epi(mb + ps * RPP + srow, n, v, aux[ps]);
     }
   }
 }
