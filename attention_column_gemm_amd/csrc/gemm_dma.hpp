@@ -17,9 +17,10 @@
 //    help: the loop is limited by the CU's LDS and vector-memory pipelines,
 //    not by load latency.
 //  * The waves split into two halves, one wave of each on every SIMD; the
-//    halves issue their share of a tile's loads one k step apart, so that on
-//    every SIMD one wave can issue MFMAs while the other is handing loads to
-//    the memory pipeline (measured 3-4% over issuing all loads at once).
+//    halves issue their share of a tile's loads one or two k steps apart, so
+//    that on every SIMD one wave can issue MFMAs while the other is handing
+//    loads to the memory pipeline (measured 3-7% over issuing all loads at
+//    once).
 //  * K-contiguous operands live in LDS as [rows][BK] with the 16-byte chunks
 //    of a row XOR-swizzled by the row index (conflict-free 128-bit fragment
 //    reads).  M/N-contiguous operands (weights stored [K,N], the
@@ -243,8 +244,13 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem
   // Waves 0 .. NW/2-1 form half 0, the rest half 1; wave w runs on SIMD w % 4,
   // so with eight waves every SIMD holds one wave of each half.  Half 0
   // issues its share of tile t+1 right after the barrier that frees the
-  // stage (one k step before tile t starts), half 1 one k step into tile t.
-  // Each wave waits for its own loads (vmcnt 0) before the next barrier.
+  // stage (one k step before tile t starts), half 1 at k step STAGGER of tile
+  // t: step 0 when A is K-contiguous, step 1 when it is M-contiguous (the
+  // weight gradients, whose transposing fragment reads keep the LDS busier);
+  // both measured best on gfx950, later points leave the loads too little
+  // time to land.  Each wave waits for its own loads (vmcnt 0) before the next
+  // barrier.
+  constexpr int STAGGER = AL == KMAJOR ? 0 : 1;
   const int half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / (NW / 2);
   auto sync_next = [&]() {
     wait_vmcnt<0>();
@@ -262,7 +268,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       if (kk + 1 < KK) {
-        if (kk == 1 && half == 1 && kt + 1 < nk) issue(kt + 1);
+        if (kk == STAGGER && half == 1 && kt + 1 < nk) issue(kt + 1);
         load_frags(F[(kk + 1) & 1], kt, kk + 1);
       } else if (kt + 1 < nk) {
         // tile kt+1 has landed and every read of tile kt's stage is done, so
