@@ -13,12 +13,12 @@
 //
 // Three kernels:
 //  * stats: per (sequence, head, row) the pair {lse * log2(e), Delta}.
-//  * dK/dV: a work-group owns 32 keys of one KV head; its four waves take
-//    every fourth (query head, 32-row query tile) item of the causal range,
-//    last query tile first,
-//    each wave streaming its own Q and dO tiles into LDS with LDS-direct
-//    loads (double buffered), and the four waves' partial sums are added in a
-//    fixed order through LDS at the end (deterministic, no atomics).
+//  * dK/dV: a work-group owns 32 keys of one KV head, staged once in LDS; its
+//    eight waves (two per SIMD) take every eighth (query head, 32-row query
+//    tile) item of the causal range, last query tile first, each wave
+//    streaming its own Q and dO tiles into LDS with LDS-direct loads, and
+//    the eight waves' partial sums are added in a fixed order through LDS at
+//    the end (deterministic, no atomics).
 //  * dQ: the forward's layout (waves own 32 query rows; the work-group shares
 //    64-key K and V blocks in LDS).
 // Operand layouts: with v_mfma_f32_32x32x16_bf16 computing C[i][j] += sum_k
@@ -98,15 +98,22 @@ __global__ void __launch_bounds__(NTHREADS) attn_bwd_stats_kernel(BwdArgs a, int
 }
 
 // ---- dK, dV ----------------------------------------------------------------
+// Eight waves (two per SIMD, so one wave's exponentials and loads overlap the
+// other's MFMAs) share one 32-key block: its K and V rows sit in LDS once,
+// and each wave streams the Q and dO tiles of every eighth item into its own
+// LDS slot.
+constexpr int DKV_WAVES = 8;
 template <int D>
-__global__ void __launch_bounds__(NTHREADS, 1) attn_bwd_dkv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(64 * DKV_WAVES, 1) attn_bwd_dkv_kernel(BwdArgs a) {
   constexpr int DT = D / 32, KK = D / 16;
   constexpr int TILE = Q_TILE * D * 2;   // one 32-row tile
   constexpr int TI = TILE / 1024;        // its LDS-direct instructions
-  constexpr int STAGE = 2 * TILE + 256;  // Q tile, dO tile, 32 x {lse2, Delta}
-  constexpr int WAVE_LDS = 2 * STAGE;
-  static_assert(4 * 2 * DT * 16 * 64 * 4 <= 4 * WAVE_LDS, "reduction space");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * WAVE_LDS];
+  constexpr int SLOT = 2 * TILE + 256;   // a wave's Q tile, dO tile, 32 x {lse2, Delta}
+  constexpr int KV_BYTES = 2 * TILE;     // the block's K and V rows
+  constexpr int LDS_BYTES = KV_BYTES + DKV_WAVES * SLOT;
+  constexpr int PART = 2 * DT * 16 * 64 * 4;  // one wave's dK and dV partial sums
+  static_assert(4 * PART <= LDS_BYTES, "reduction space");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   const lds_u8* lds = (const lds_u8*)smem;
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
@@ -117,21 +124,17 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_bwd_dkv_kernel(BwdArgs a) {
   const int group = a.q / a.kv;
   const int64_t tok0 = (int64_t)beta * a.s;
   const uint32_t ldq = (uint32_t)a.ld_qkv * 2u, ldo = (uint32_t)a.ld_o * 2u;
+  const u32x4 rq = lds::sgpr_rsrc(a.qkv + tok0 * a.ld_qkv, (uint32_t)a.s * ldq);
+  const u32x4 rdo = lds::sgpr_rsrc(a.dO + tok0 * a.ld_o, (uint32_t)a.s * ldo);
+  const u32x4 rst = lds::sgpr_rsrc(a.stats + (int64_t)beta * a.q * a.s * 2, (uint32_t)a.q * a.s * 8u);
 
-  // this block's keys and values as MFMA operands (zeros past the sequence)
-  bf16x8 kf[KK], vf[KK];
-  {
-    const rsrc_t seq = make_rsrc(a.qkv + tok0 * a.ld_qkv, (uint32_t)a.s * ldq);
-    const int key = k0 + l32;
-    const uint32_t kc = (uint32_t)(a.q + g) * D * 2u, vc = (uint32_t)(a.q + a.kv + g) * D * 2u;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const uint32_t base = (uint32_t)key * ldq + (uint32_t)(16 * kk + 8 * h) * 2u;
-      kf[kk] = __builtin_bit_cast(bf16x8, buf_load16(seq, key < a.s ? base + kc : kOOB));
-      vf[kk] = __builtin_bit_cast(bf16x8, buf_load16(seq, key < a.s ? base + vc : kOOB));
-    }
-  }
-  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): keep these out of the tile pipeline's counts
+  // the block's K and V rows (zeros past the sequence), loaded once
+  dma_tile<D, KEY_BLOCK>(rq, ldq, k0, a.s, (uint32_t)(a.q + g) * D * 2u, lds_base, wave, DKV_WAVES);
+  dma_tile<D, KEY_BLOCK>(rq, ldq, k0, a.s, (uint32_t)(a.q + a.kv + g) * D * 2u, lds_base + TILE, wave, DKV_WAVES);
+  lds::wait_vmcnt<0>();
+  lds::barrier();
+  const lds_u8* tkey = lds;
+  const lds_u8* tval = lds + TILE;
 
   f32x16 dk[DT], dv[DT];
 #pragma unroll
@@ -143,45 +146,25 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_bwd_dkv_kernel(BwdArgs a) {
   const int qt0 = a.causal ? (k0 / Q_TILE) : 0;
   const int ntile = nqt - qt0;
   const int nitems = group * ntile;
-  const u32x4 rq = lds::sgpr_rsrc(a.qkv + tok0 * a.ld_qkv, (uint32_t)a.s * ldq);
-  const u32x4 rdo = lds::sgpr_rsrc(a.dO + tok0 * a.ld_o, (uint32_t)a.s * ldo);
-  const u32x4 rst = lds::sgpr_rsrc(a.stats + (int64_t)beta * a.q * a.s * 2, (uint32_t)a.q * a.s * 8u);
-  const uint32_t wl = lds_base + (uint32_t)wave * WAVE_LDS;
+  const uint32_t slot = lds_base + (uint32_t)(KV_BYTES + wave * SLOT);
+  const lds_u8* tq = lds + (KV_BYTES + wave * SLOT);
+  const lds_u8* tdo = tq + TILE;
+  const lds_u8* tst = tq + 2 * TILE;
 
   // items run from the last query tile backwards, so the work-groups of one
   // KV head (all key blocks) read the same Q and dO tiles at about the same
   // time and share them in L2
-  auto item = [&](int n, int& j, int& i0) {
-    j = g * group + n / ntile;
-    i0 = (nqt - 1 - n % ntile) * Q_TILE;
-  };
-  auto issue = [&](int n, int st) {
-    int j, i0;
-    item(n, j, i0);
-    const uint32_t dst = wl + (uint32_t)st * STAGE;
-    dma_tile<D, Q_TILE>(rq, ldq, i0, a.s, (uint32_t)j * D * 2u, dst, 0, 1);
-    dma_tile<D, Q_TILE>(rdo, ldo, i0, a.s, (uint32_t)j * D * 2u, dst + TILE, 0, 1);
-    // lanes 2i, 2i+1: the {lse2, Delta} pair of row i0 + i
-    const int row = i0 + (lane >> 1);
-    dma4(rst, row < a.s ? ((uint32_t)j * a.s + row) * 8u + (lane & 1) * 4u : kOOB, dst + 2 * TILE);
-  };
-
-  if (wave < nitems) issue(wave, 0);
-  int it = 0;
-  for (int n = wave; n < nitems; n += 4, ++it) {
-    const int st = it & 1;
-    lds::wait_lgkm0();  // this wave's reads of the other stage are done
-    if (n + 4 < nitems) {
-      issue(n + 4, st ^ 1);
-      lds::wait_vmcnt<2 * TI + 1>();
-    } else {
-      lds::wait_vmcnt<0>();
+  for (int n = wave; n < nitems; n += DKV_WAVES) {
+    const int j = g * group + n / ntile;
+    const int i0 = (nqt - 1 - n % ntile) * Q_TILE;
+    lds::wait_lgkm0();  // this wave's reads of its slot are done
+    dma_tile<D, Q_TILE>(rq, ldq, i0, a.s, (uint32_t)j * D * 2u, slot, 0, 1);
+    dma_tile<D, Q_TILE>(rdo, ldo, i0, a.s, (uint32_t)j * D * 2u, slot + TILE, 0, 1);
+    {  // lanes 2i, 2i+1: the {lse2, Delta} pair of row i0 + i
+      const int row = i0 + (lane >> 1);
+      dma4(rst, row < a.s ? ((uint32_t)j * a.s + row) * 8u + (lane & 1) * 4u : kOOB, slot + 2 * TILE);
     }
-    int j, i0;
-    item(n, j, i0);
-    const lds_u8* tq = lds + (wave * WAVE_LDS + st * STAGE);
-    const lds_u8* tdo = tq + TILE;
-    const lds_u8* tst = tq + 2 * TILE;
+    lds::wait_vmcnt<0>();
 
     // S = Q K^T and dP = dO V^T for 32 queries x 32 keys: lane = key, registers = queries
     f32x16 sacc, pacc;
@@ -189,8 +172,9 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_bwd_dkv_kernel(BwdArgs a) {
     for (int e = 0; e < 16; ++e) sacc[e] = pacc[e] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(tq, 0, kk), kf[kk], sacc, 0, 0, 0);
-      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(tdo, 0, kk), vf[kk], pacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(tq, 0, kk), row_frag<D>(tkey, 0, kk), sacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(tdo, 0, kk), row_frag<D>(tval, 0, kk), pacc, 0, 0,
+                                                     0);
     }
     // P = exp2(S c log2e - lse2), dS = P (dP - Delta); register r holds query 8(r/4) + 4h + r%4
     const int key = k0 + l32;
@@ -225,28 +209,52 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_bwd_dkv_kernel(BwdArgs a) {
       }
   }
 
-  // add the four waves' partial sums in wave order and store
-  lds::wait_vmcnt<0>();
+  // add the eight waves' partial sums in a fixed order, (w0+w4) + (w1+w5) +
+  // (w2+w6) + (w3+w7), through LDS in two rounds, and store
+  float* red = reinterpret_cast<float*>(smem);  // [4][2 DT][16][64]
+  auto slot_of = [&](int w, int u, int e) { return ((w * 2 * DT + u) * 16 + e) * 64 + lane; };
+  lds::wait_lgkm0();
   __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);  // [wave][2 DT][16][64]
+  if (wave >= 4) {
 #pragma unroll
-  for (int t = 0; t < DT; ++t)
+    for (int t = 0; t < DT; ++t)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      red[((wave * 2 * DT + t) * 16 + e) * 64 + lane] = dk[t][e];
-      red[((wave * 2 * DT + DT + t) * 16 + e) * 64 + lane] = dv[t][e];
-    }
+      for (int e = 0; e < 16; ++e) {
+        red[slot_of(wave - 4, t, e)] = dk[t][e];
+        red[slot_of(wave - 4, DT + t, e)] = dv[t][e];
+      }
+  }
+  __syncthreads();
+  if (wave < 4) {
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        dk[t][e] += red[slot_of(wave, t, e)];
+        dv[t][e] += red[slot_of(wave, DT + t, e)];
+      }
+  }
+  __syncthreads();
+  if (wave < 4) {
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        red[slot_of(wave, t, e)] = dk[t][e];
+        red[slot_of(wave, DT + t, e)] = dv[t][e];
+      }
+  }
   __syncthreads();
   const int key = k0 + l32;
-  for (int u = wave; u < 2 * DT; u += 4) {
+  for (int u = wave; u < 2 * DT; u += DKV_WAVES) {
     const bool is_k = u < DT;
     const int dt = is_k ? u : u - DT;
     float v[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      float x = red[((0 * 2 * DT + u) * 16 + e) * 64 + lane];
+      float x = red[slot_of(0, u, e)];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) x += red[((w * 2 * DT + u) * 16 + e) * 64 + lane];
+      for (int w = 1; w < 4; ++w) x += red[slot_of(w, u, e)];
       v[e] = is_k ? x * a.scale : x;
     }
     if (key < a.s) {
@@ -393,7 +401,8 @@ template <int D>
 hipError_t launch_attn_bwd_dkv(const attnb::BwdArgs& a, hipStream_t stream) {
   const int nkb = (a.s + attnb::KEY_BLOCK - 1) / attnb::KEY_BLOCK;
   if (nkb == 0 || a.b * a.kv == 0) return hipSuccess;
-  hipLaunchKernelGGL((attnb::attn_bwd_dkv_kernel<D>), dim3(nkb, a.b * a.kv), dim3(attnb::NTHREADS), 0, stream, a);
+  hipLaunchKernelGGL((attnb::attn_bwd_dkv_kernel<D>), dim3(nkb, a.b * a.kv), dim3(64 * attnb::DKV_WAVES), 0, stream,
+                     a);
   return hipGetLastError();
 }
 
