@@ -25,7 +25,10 @@
 //    matching V^T operand is read from the row-major V tile with
 //    ds_read_b64_tr_b16 in that same order, so P never goes through LDS and V
 //    is never stored transposed.
-//  * Online softmax in base 2 (scores pre-multiplied by log2(e)/sqrt(d)).
+//  * Online softmax in base 2 (scores pre-multiplied by log2(e)/sqrt(d)),
+//    exponentials on v_exp_f32 directly; the running output is rescaled only
+//    when some row's maximum moved, and blocks wholly inside the causal
+//    triangle skip the mask.
 //  * Work-groups are issued heaviest-first (latest query rows) to even out the
 //    causal triangle.
 #pragma once
@@ -146,7 +149,7 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(AttnArgs a) {
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
     const float m_new = fmaxf(m_run, bmax);
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_new;
     float psum = 0.0f;
     bf16x8 pf[2][2];
@@ -155,17 +158,20 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(AttnArgs a) {
       float p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[r] = exp2f(sacc[kt][r] - m_use);
+        p[r] = __builtin_amdgcn_exp2f(sacc[kt][r] - m_use);
         psum += p[r];
       }
       pf[kt][0] = attnt::pack8(p);
       pf[kt][1] = attnt::pack8(p + 8);
     }
     l_run = l_run * alpha + psum;
+    // rescale only when some row's maximum moved (alpha == 1 exactly otherwise)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+      for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[t][e] *= alpha;
+        for (int e = 0; e < 16; ++e) oacc[t][e] *= alpha;
+    }
     // O^T += V^T P^T
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)

@@ -31,6 +31,8 @@
 // in that same order, so no tile is ever stored transposed.
 #pragma once
 
+#include <type_traits>
+
 #include "attn_tiles.hpp"
 #include "common.hpp"
 #include "lds_dma.hpp"
@@ -176,23 +178,33 @@ __global__ void __launch_bounds__(64 * DKV_WAVES, 1) attn_bwd_dkv_kernel(BwdArgs
       pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(tdo, 0, kk), row_frag<D>(tval, 0, kk), pacc, 0, 0,
                                                      0);
     }
-    // P = exp2(S c log2e - lse2), dS = P (dP - Delta); register r holds query 8(r/4) + 4h + r%4
+    // P = exp2(S c log2e - lse2), dS = P (dP - Delta); register r holds query 8(r/4) + 4h + r%4.
+    // Items wholly inside the sequence and below the causal diagonal skip the mask.
     const int key = k0 + l32;
+    const bool full = i0 + Q_TILE <= a.s && (!a.causal || k0 + KEY_BLOCK - 1 <= i0);
     float p[16], ds[16];
+    auto probs = [&](auto masked) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int ir = 8 * q4 + 4 * h;  // first of this group's four queries within the tile
-      const f32x4 s0 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(tst + ir * 8);
-      const f32x4 s1 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(tst + ir * 8 + 16);
-      const float lse2[4] = {s0.x, s0.z, s1.x, s1.z}, dlt[4] = {s0.y, s0.w, s1.y, s1.w};
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int ir = 8 * q4 + 4 * h;  // first of this group's four queries within the tile
+        const f32x4 s0 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(tst + ir * 8);
+        const f32x4 s1 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(tst + ir * 8 + 16);
+        const float lse2[4] = {s0.x, s0.z, s1.x, s1.z}, dlt[4] = {s0.y, s0.w, s1.y, s1.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * q4 + e, qi = i0 + ir + e;
-        const bool ok = qi < a.s && (!a.causal || key <= qi);
-        p[r] = ok ? exp2f(sacc[r] * a.scale_log2 - lse2[e]) : 0.0f;
-        ds[r] = p[r] * (pacc[r] - dlt[e]);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e, qi = i0 + ir + e;
+          p[r] = __builtin_amdgcn_exp2f(sacc[r] * a.scale_log2 - lse2[e]);
+          if constexpr (decltype(masked)::value) {
+            if (!(qi < a.s && (!a.causal || key <= qi))) p[r] = 0.0f;
+          }
+          ds[r] = p[r] * (pacc[r] - dlt[e]);
+        }
       }
-    }
+    };
+    if (full)
+      probs(std::false_type{});
+    else
+      probs(std::true_type{});
     bf16x8 pf[2], df[2];
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
@@ -343,6 +355,8 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_kernel(BwdArgs a, int
     if (a.causal && key0 > rp0 + 31) continue;
     const lds_u8* tk = lds + st * STAGE;
     const lds_u8* tv = tk + TILE;
+    // blocks wholly inside the sequence and below the causal diagonal skip the mask
+    const bool full = key0 + DQ_KEYS <= a.s && (!a.causal || key0 + DQ_KEYS - 1 <= rp0);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       // S^T = K Q^T and dP^T = V dO^T: lane = query, registers = keys
@@ -355,13 +369,21 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_kernel(BwdArgs a, int
         pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(tv, 32 * kt, kk), of[kk], pacc, 0, 0, 0);
       }
       float ds[16];
+      auto grads = [&](auto masked) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * h + (r & 3);
-        const bool ok = key < a.s && (!a.causal || key <= my_row);
-        const float p = ok ? exp2f(sacc[r] * a.scale_log2 - lse2) : 0.0f;
-        ds[r] = p * (pacc[r] - dlt);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * h + (r & 3);
+          float p = __builtin_amdgcn_exp2f(sacc[r] * a.scale_log2 - lse2);
+          if constexpr (decltype(masked)::value) {
+            if (!(key < a.s && (!a.causal || key <= my_row))) p = 0.0f;
+          }
+          ds[r] = p * (pacc[r] - dlt);
+        }
+      };
+      if (full)
+        grads(std::false_type{});
+      else
+        grads(std::true_type{});
       const bf16x8 df0 = pack8(ds), df1 = pack8(ds + 8);
       // dQ^T += K^T dS^T: lane = query, registers = head dims
 #pragma unroll

@@ -59,6 +59,8 @@ __device__ __forceinline__ bf16x8 tr_frag(const lds_u8* tile, int r0, int dt, in
 // byte column col_bytes of a row-major matrix (ld_bytes per row, nrows rows,
 // behind `rsrc`) into a swizzled [ROWS][D] tile at LDS byte address dst.
 // This wave issues the tile's 1 KiB instructions i0, i0 + step, ...
+// Row offsets use the full-rate 24-bit multiply: row indices and ld_bytes
+// stay below 2^24 (the host rejects larger attention shapes).
 template <int D, int ROWS>
 __device__ __forceinline__ void dma_tile(const u32x4& rsrc, uint32_t ld_bytes, int row0, int nrows,
                                          uint32_t col_bytes, uint32_t dst, int i0, int step) {
@@ -69,7 +71,7 @@ __device__ __forceinline__ void dma_tile(const u32x4& rsrc, uint32_t ld_bytes, i
     const int r = o / (2 * D), pos = (o % (2 * D)) >> 4;
     const int c = pos ^ swz<D>(r);
     const uint32_t voff =
-        row0 + r < nrows ? (uint32_t)(row0 + r) * ld_bytes + col_bytes + (uint32_t)c * 16u : kOOB;
+        row0 + r < nrows ? __umul24((uint32_t)(row0 + r), ld_bytes) + col_bytes + (uint32_t)c * 16u : kOOB;
     lds::dma16(rsrc, voff, dst + (uint32_t)i * 1024u);
   }
 }

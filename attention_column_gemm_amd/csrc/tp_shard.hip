@@ -403,6 +403,8 @@ int check_attn_desc(const tp_attn_desc* d) {
   if (int rc = attn_heads(d->n_q, d->n_kv, d->t, d->rank, &q, &kv, &q0, &kv0)) return rc;
   if (d->d != 64 && d->d != 128) return TP_EUNSUPPORTED;
   if (!fits_int(d->b * d->s) || !fits_int(d->h)) return TP_EINVAL;
+  // the attention kernels' tile loads form row offsets with 24-bit multiplies
+  if (d->s >= (1 << 24) || (int64_t)(q + 2 * kv) * d->d * 2 >= (1 << 24)) return TP_EUNSUPPORTED;
   return TP_OK;
 }
 

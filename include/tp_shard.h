@@ -59,7 +59,8 @@ enum {
   TP_EDTYPE = -3,       /* unknown dtype/activation, or a combination not provided (attention in fp32) */
   TP_EALIGN = -4,       /* a pointer is not 16-byte aligned or a width is not a multiple of the vector width */
   TP_EHIP = -5,         /* the HIP runtime reported an error when enqueuing a kernel */
-  TP_EUNSUPPORTED = -6  /* a size the kernels do not implement (head width other than 64 or 128, t > 64) */
+  TP_EUNSUPPORTED = -6  /* a size the kernels do not implement (head width other than 64 or 128, t > 64,
+                           an attention shard with s >= 2^24 or a QKV row of 2^24 bytes or more) */
 };
 
 /* One rank's MLP shard. */
