@@ -118,6 +118,9 @@ def test_attention_validation():
     assert call(n_q=9) == B.TP_ENOTDIV
     assert call(n_kv=3) == B.TP_ENOTDIV
     assert call(d=96) == B.TP_EUNSUPPORTED
+    # tile-load row offsets are 24-bit products: s and the QKV row bytes stay below 2^24
+    assert call(b=1, s=1 << 24) == B.TP_EUNSUPPORTED
+    assert call(b=1, s=1, n_q=1 << 16, n_kv=2, t=1) == B.TP_EUNSUPPORTED
     assert call(rank=2) == B.TP_EINVAL
     assert call(h=100) == B.TP_EALIGN
     assert L.tp_attn_shard_fwd(None, A16, A16, A16, A16, A16, None, A16, None) == B.TP_EINVAL
@@ -137,6 +140,7 @@ def test_attention_backward_validation():
     assert call(dtype=B.TP_F32) == B.TP_EDTYPE
     assert call(n_q=9) == B.TP_ENOTDIV
     assert call(d=32) == B.TP_EUNSUPPORTED
+    assert call(b=1, s=1 << 24) == B.TP_EUNSUPPORTED
     assert call(rank=-1) == B.TP_EINVAL
     assert call(h=100) == B.TP_EALIGN
     for i in range(13):                      # each tensor is required
