@@ -67,6 +67,10 @@ SMALL = {
     "ragged_gelu_bias_dropout_t4": I.custom_mlp(101, 2, 164, 264, 544, 4, "gelu", "bf16", p_drop=0.15, bias=True),
     "ragged_swiglu_t2": I.custom_mlp(102, 1, 328, 264, 688, 2, "swiglu", "bf16"),
     "ragged_gelu_fp32_t3": I.custom_mlp(103, 3, 45, 132, 3 * 76, 3, "gelu", "fp32", p_drop=0.3, bias=True),
+    # K loops of one and two 64-deep tiles: the loop body never runs, or runs once with the
+    # refill past the last tile (h = 40: dH has one K tile; f = 48 per rank: dX has one per segment)
+    "tinyK_swiglu_t4": I.custom_mlp(104, 2, 50, 40, 192, 4, "swiglu", "bf16"),
+    "tinyK_gelu_bias_dropout_t2": I.custom_mlp(105, 1, 70, 128, 144, 2, "gelu", "bf16", p_drop=0.1, bias=True),
 }
 
 
