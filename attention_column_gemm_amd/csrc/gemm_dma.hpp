@@ -14,13 +14,16 @@
 //    fragments are read from LDS while that step's MFMAs execute.  BK = 64
 //    with two stages measured faster than BK = 32 with three or four (fewer
 //    barriers), and an explicit L2 warm-up of the tile after next did not
-//    help: the loop is limited by the CU's LDS and vector-memory pipelines,
-//    not by load latency.
+//    help.
 //  * The waves split into two halves, one wave of each on every SIMD; the
 //    halves issue their share of a tile's loads one or two k steps apart, so
 //    that on every SIMD one wave can issue MFMAs while the other is handing
 //    loads to the memory pipeline (measured 3-7% over issuing all loads at
-//    once).
+//    once).  The last K tile is peeled off the loop, scheduling groups
+//    spread each k step's fragment reads over its MFMAs, and with both
+//    operands K-contiguous each half runs its own copy of the loop (see the
+//    loop).  Taking the LDS-direct loads out of the loop (a measurement
+//    switch) speeds it up by about a quarter; they are what limits it.
 //  * K-contiguous operands live in LDS as [rows][BK] with the 16-byte chunks
 //    of a row XOR-swizzled by the row index (conflict-free 128-bit fragment
 //    reads).  M/N-contiguous operands (weights stored [K,N], the
