@@ -365,12 +365,19 @@ def main():
     t_end = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record()
-    all_marks = [step(kevs[i]) for i in range(args.steps)]
+    all_marks = [step() for _ in range(args.steps)]
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+    # per-kernel durations: the same number of steps again, right after, with
+    # the library's events armed around every kernel (kept out of the steps
+    # above, whose spans give the headline value)
+    log(f"[bench] per-kernel timing over {args.steps} more steps")
+    for i in range(args.steps):
+        step(kevs[i])
+    torch.cuda.synchronize()
 
     kern_ms = np.zeros(nk)
     for kev in kevs:
