@@ -119,7 +119,7 @@ hipError_t gemm_any(const GemmProblem& p, const Epi& epi, hipStream_t st) {
 
 unsigned grid_for(int64_t n_vec) {
   int64_t blocks = (n_vec + 255) / 256;
-  if (blocks > 16 * kNumCUs) blocks = 16 * kNumCUs;
+  if (blocks > 64 * kNumCUs) blocks = 64 * kNumCUs;
   return (unsigned)(blocks < 1 ? 1 : blocks);
 }
 
