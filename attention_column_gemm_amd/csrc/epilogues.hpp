@@ -117,7 +117,7 @@ struct EpiGeluBwd {
   int64_t ld;
   int M, N;
   __device__ __forceinline__ void load(int m, int n, Aux& x) const {
-    if (m < M && n < N) x.a = Elem<T>::load_raw(A + (int64_t)m * ld + n);
+    if (m < M && n < N) x.a = Elem<T>::load_once(A, (int64_t)m * ld + n, (int64_t)M * ld);
   }
   __device__ __forceinline__ void operator()(int m, int n, const float (&v)[NB][4], const Aux& x) const {
     if (m >= M || n >= N) return;
@@ -147,8 +147,8 @@ struct EpiSwigluBwd {
   __device__ __forceinline__ void load(int m, int n, Aux& x) const {
     if (m < M && n < N) {
       const int64_t o = (int64_t)m * ld + n;
-      x.g = Elem<T>::load_raw(G + o);
-      x.u = Elem<T>::load_raw(U + o);
+      x.g = Elem<T>::load_once(G, o, (int64_t)M * ld);
+      x.u = Elem<T>::load_once(U, o, (int64_t)M * ld);
     }
   }
   __device__ __forceinline__ void operator()(int m, int n, const float (&v)[NB][4], const Aux& x) const {
