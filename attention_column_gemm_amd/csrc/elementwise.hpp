@@ -140,15 +140,16 @@ __global__ void __launch_bounds__(256) dropout_bwd_kernel(int64_t n_vec, const T
 }
 
 // out[c] = sum over rows of X[r, c] in fp32, in a fixed order (so repeated
-// runs agree bit for bit).  A work-group owns COLS_PER_WG columns: its threads
-// are (COLS_PER_WG / V) column vectors x ROW_LANES row lanes; lane l sums rows
-// l, l + ROW_LANES, ... and the lanes are then folded pairwise through LDS.
-template <class T>
+// runs agree bit for bit).  A work-group owns CV column vectors (CV * V
+// columns): its 256 threads are CV column vectors x 256/CV row lanes; lane l
+// sums rows l, l + ROW_LANES, ... in that order (four loads in flight), and
+// the lanes are then folded pairwise through LDS.  The launcher picks CV so
+// that narrow tensors still spread over the CUs.
+template <class T, int CV>
 __global__ void __launch_bounds__(256) colsum_kernel(int64_t rows, int64_t cols, int64_t ld, const T* __restrict__ X,
                                                      float* __restrict__ out) {
   constexpr int V = Vec<T>::N;
-  constexpr int CV = 8;                      // column vectors per work-group
-  constexpr int ROW_LANES = 256 / CV;        // 32
+  constexpr int ROW_LANES = 256 / CV;
   __shared__ float red[ROW_LANES][CV * V + 1];
   const int cv = threadIdx.x % CV, rl = threadIdx.x / CV;
   const int64_t c0 = (int64_t)blockIdx.x * CV * V + cv * V;
@@ -156,7 +157,17 @@ __global__ void __launch_bounds__(256) colsum_kernel(int64_t rows, int64_t cols,
 #pragma unroll
   for (int j = 0; j < V; ++j) acc[j] = 0.0f;
   if (c0 < cols) {
-    for (int64_t r = rl; r < rows; r += ROW_LANES) {
+    int64_t r = rl;
+    for (; r + 3 * ROW_LANES < rows; r += 4 * ROW_LANES) {
+      float x[4][V];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Vec<T>::load(X + (r + u * ROW_LANES) * ld + c0, x[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < V; ++j) acc[j] += x[u][j];
+    }
+    for (; r < rows; r += ROW_LANES) {
       float x[V];
       Vec<T>::load(X + r * ld + c0, x);
 #pragma unroll

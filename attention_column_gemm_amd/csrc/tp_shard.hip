@@ -135,12 +135,20 @@ hipError_t dropout_bwd(int64_t n, const void* dOut, uint32_t thr, float scale, u
 
 template <class T>
 hipError_t colsum(int64_t rows, int64_t cols, const void* X, float* out, hipStream_t st) {
-  const int64_t per_wg = 8 * Vec<T>::N;
-  const int64_t blocks = (cols + per_wg - 1) / per_wg;
-  if (blocks == 0) return hipSuccess;
+  // column vectors per work-group: the most (up to 8) that still gives every CU one
+  const int64_t nvec = cols / Vec<T>::N;
+  if (nvec == 0) return hipSuccess;
+  int cv = 8;
+  while (cv > 1 && (nvec + cv - 1) / cv < kNumCUs) cv /= 2;
+  const unsigned blocks = (unsigned)((nvec + cv - 1) / cv);
   Probe pr(st);
-  hipLaunchKernelGGL(colsum_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st, rows, cols, cols,
-                     static_cast<const T*>(X), out);
+  const T* x = static_cast<const T*>(X);
+  switch (cv) {
+    case 8: hipLaunchKernelGGL((colsum_kernel<T, 8>), dim3(blocks), dim3(256), 0, st, rows, cols, cols, x, out); break;
+    case 4: hipLaunchKernelGGL((colsum_kernel<T, 4>), dim3(blocks), dim3(256), 0, st, rows, cols, cols, x, out); break;
+    case 2: hipLaunchKernelGGL((colsum_kernel<T, 2>), dim3(blocks), dim3(256), 0, st, rows, cols, cols, x, out); break;
+    default: hipLaunchKernelGGL((colsum_kernel<T, 1>), dim3(blocks), dim3(256), 0, st, rows, cols, cols, x, out);
+  }
   return hipGetLastError();
 }
 
