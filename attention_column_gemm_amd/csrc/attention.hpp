@@ -33,6 +33,8 @@
 //    causal triangle.
 #pragma once
 
+#include <type_traits>
+
 #include "attn_tiles.hpp"
 #include "common.hpp"
 #include "lds_dma.hpp"
@@ -131,21 +133,27 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(AttnArgs a) {
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(attnt::row_frag<D>(tk, 32 * kt, kk), qf[kk], sacc[kt],
                                                            0, 0, 0);
     }
-    // scale, mask, block max
+    // scale, mask (only blocks that reach past the diagonal or the sequence), block max
     const bool need_mask = (a.causal && key0 + BKV - 1 > rp0) || key0 + BKV > a.s;
     float bmax = -INFINITY;
+    auto scale_max = [&](auto masked) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sacc[kt][r] * a.scale_log2;
-        if (need_mask) {
-          const int key = key0 + kt * 32 + 8 * (r >> 2) + 4 * hgrp + (r & 3);
-          if (key >= a.s || (a.causal && key > my_row)) x = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          float x = sacc[kt][r] * a.scale_log2;
+          if constexpr (decltype(masked)::value) {
+            const int key = key0 + kt * 32 + 8 * (r >> 2) + 4 * hgrp + (r & 3);
+            if (key >= a.s || (a.causal && key > my_row)) x = -INFINITY;
+          }
+          sacc[kt][r] = x;
+          bmax = fmaxf(bmax, x);
         }
-        sacc[kt][r] = x;
-        bmax = fmaxf(bmax, x);
-      }
+    };
+    if (need_mask)
+      scale_max(std::true_type{});
+    else
+      scale_max(std::false_type{});
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
     const float m_new = fmaxf(m_run, bmax);
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
