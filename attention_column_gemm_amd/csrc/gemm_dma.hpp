@@ -266,12 +266,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem
   // so with eight waves every SIMD holds one wave of each half.  Half 0
   // issues its share of tile t+1 right after the barrier that frees the
   // stage (one k step before tile t starts), half 1 at k step STAGGER of tile
-  // t: step 0 when A is K-contiguous, step 1 when it is M-contiguous (the
-  // weight gradients, whose transposing fragment reads keep the LDS busier);
-  // both measured best on gfx950, later points leave the loads too little
-  // time to land.  Each wave waits for its own loads (vmcnt 0) before the next
+  // t: step 0, except step 1 for the large single-B tile with M-contiguous A
+  // (the weight gradients' transposing fragment reads keep its LDS busier);
+  // measured on gfx950, later points leave the loads too little time to
+  // land.  Each wave waits for its own loads (vmcnt 0) before the next
   // barrier.
-  constexpr int STAGGER = AL == KMAJOR ? 0 : 1;
+  constexpr int STAGGER = (AL != KMAJOR && NB == 1 && BM == 256) ? 1 : 0;
   const int half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / (NW / 2);
   auto sync_next = [&]() {
     wait_vmcnt<0>();
@@ -285,7 +285,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem
   // on gfx950).  With an M-contiguous B and a K-contiguous A the hint makes
   // the compiler spill and is left out.
   auto interleave = [&]() {
-    if constexpr (!(AL == KMAJOR && BL != KMAJOR)) {
+    if constexpr (!(AL == KMAJOR && BL != KMAJOR && NB == 1)) {
       constexpr int NMF = NB * TM * TN;
       constexpr int NDS = TM * (AL == KMAJOR ? 1 : 2) + NB * TN * (BL == KMAJOR ? 1 : 2);
       interleave_reads<0, NMF, NDS>();
@@ -327,7 +327,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem
       }
     }
   };
-  if constexpr (AL == KMAJOR && BL == KMAJOR) {
+  if constexpr (AL == KMAJOR && (BL == KMAJOR || NB == 1)) {
     if (half == 0)
       kloop(std::integral_constant<int, 0>{});
     else
