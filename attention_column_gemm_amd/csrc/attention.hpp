@@ -29,8 +29,10 @@
 //    exponentials on v_exp_f32 directly; the running output is rescaled only
 //    when some row's maximum moved, and blocks wholly inside the causal
 //    triangle skip the mask.
-//  * Work-groups are issued heaviest-first (latest query rows) to even out the
-//    causal triangle.
+//  * Work-groups are ranked by work (later query rows see more keys); the
+//    first half of the dispatch order runs heaviest-first and the second half
+//    lightest-first, so each CU's two work-groups add up to about the same
+//    work.
 #pragma once
 
 #include <type_traits>
@@ -69,11 +71,12 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rows_per_wg = 32 * (4 / a.hg);
   const int npb = (a.s + rows_per_wg - 1) / rows_per_wg;
-  const int pb = npb - 1 - (int)blockIdx.x;
   const int group = a.q / a.kv;
   const int sub_per_kv = group / a.hg;
-  const int beta = blockIdx.y / (a.kv * sub_per_kv);
-  const int rem = blockIdx.y % (a.kv * sub_per_kv);
+  int pb, y;
+  attnt::causal_block_order(npb, a.b * a.kv * sub_per_kv, pb, y);
+  const int beta = y / (a.kv * sub_per_kv);
+  const int rem = y % (a.kv * sub_per_kv);
   const int g = rem / sub_per_kv;
   const int j = g * group + (rem % sub_per_kv) * a.hg + (wave % a.hg);
   const int pos0 = pb * rows_per_wg;

@@ -295,11 +295,12 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_kernel(BwdArgs a, int
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rows_per_wg = 32 * (4 / hg);
   const int npb = (a.s + rows_per_wg - 1) / rows_per_wg;
-  const int pb = npb - 1 - (int)blockIdx.x;  // latest rows (most keys) first
   const int group = a.q / a.kv;
   const int sub_per_kv = group / hg;
-  const int beta = blockIdx.y / (a.kv * sub_per_kv);
-  const int rem = blockIdx.y % (a.kv * sub_per_kv);
+  int pb, y;
+  attnt::causal_block_order(npb, a.b * a.kv * sub_per_kv, pb, y);
+  const int beta = y / (a.kv * sub_per_kv);
+  const int rem = y % (a.kv * sub_per_kv);
   const int g = rem / sub_per_kv;
   const int j = g * group + (rem % sub_per_kv) * hg + (wave % hg);
   const int pos0 = pb * rows_per_wg;

@@ -13,6 +13,22 @@ namespace attnt {
 using lds::lds_u8;
 using lds::v4i16;
 
+// Query block and head-group index of this work-group in a causal launch of
+// an npb x ny grid (query blocks x head groups) whose work-groups are all
+// resident at once, two per CU.  A later query block sees more keys, so the
+// blocks are ranked by work, heaviest first; the first half of the dispatch
+// order takes ranks 0, 1, 2, ... and the second half takes them from the
+// lightest back up, so that the work-group that fills a CU's second slot is
+// light where the first was heavy.  Dispatch order is blockIdx.x fastest.
+__device__ __forceinline__ void causal_block_order(int npb, int ny, int& pb, int& y) {
+  const int total = npb * ny;
+  const int L = (int)blockIdx.x + (int)blockIdx.y * npb;
+  const int half = (total + 1) / 2;
+  const int r = L < half ? L : total - 1 - (L - half);
+  pb = npb - 1 - r / ny;
+  y = r % ny;
+}
+
 // 16-byte chunk permutation of a row-major [rows][D] bf16 tile: logical chunk
 // c of row r sits at chunk c ^ swz(r).  Sixteen consecutive rows at one
 // logical chunk (a 128-bit fragment read) and four consecutive rows at one
