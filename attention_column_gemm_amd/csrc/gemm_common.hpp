@@ -32,10 +32,10 @@ namespace gemm {
 
 constexpr int GROUP_M = 4;
 
-// Tile coordinates of this work-group (see the file comment).
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+// Tile coordinates of work-group w of the problem's launch (see the file
+// comment).
+__device__ __forceinline__ void tile_coords(int w, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
-  const int w = blockIdx.x;
   const int q = total >> 3, r = total & 7, x = w & 7;
   const int L = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + (w >> 3);
   const int per_group = GROUP_M * tiles_n;

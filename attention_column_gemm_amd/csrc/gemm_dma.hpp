@@ -180,8 +180,19 @@ __device__ __forceinline__ void interleave_reads() {
   }
 }
 
+// LDS bytes of one work-group: two operand stages, reused by the epilogue's
+// staging area once the K loop is done.
+template <int BM, int BN, int WGM, int WGN, int BK, int NB>
+constexpr int smem_bytes() {
+  constexpr int STAGE = BM * BK * 2 + NB * BN * BK * 2;
+  constexpr int STAGING = WGM * WGN * NB * 32 * ((BN / WGN) * 4 + 16);  // epilogue staging (see below)
+  return 2 * STAGE > STAGING ? 2 * STAGE : STAGING;
+}
+
+// One output tile: tile w of problem p's launch, computed by the whole
+// work-group with `smem` (smem_bytes() bytes, 1 KiB aligned) as its LDS.
 template <int BM, int BN, int WGM, int WGN, int BK, int AL, int BL, class Epi>
-__global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem p, Epi epi) {
+__device__ __forceinline__ void gemm_dma_tile(const GemmProblem& p, const Epi& epi, int w, uint8_t* smem) {
   constexpr int NW = WGM * WGN;
   constexpr int NB = Epi::NB;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -191,12 +202,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem
   constexpr int STAGE = A_BYTES + NB * B_BYTES;
   constexpr int NSTAGE = 2, KK = BK / 16;
   static_assert(KK >= 3 && NW % 2 == 0, "staggered issue needs at least three k steps and paired waves");
-  constexpr int STAGING = WGM * WGN * NB * 32 * ((BN / WGN) * 4 + 16);  // epilogue staging (see below)
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE > STAGING ? NSTAGE * STAGE : STAGING];
 
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   int tm, tn;
-  gemm::tile_coords(tiles_m, tiles_n, tm, tn);
+  gemm::tile_coords(w, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -357,7 +366,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem
   constexpr int PASSES = 32 / RPP;
   constexpr int PITCH = WN * 4 + 16;    // bytes per staged row (16-byte pad: conflict-free writes)
   static_assert(64 % LPR == 0 && 32 % RPP == 0, "staging layout");
-  static_assert(NW * NB * 32 * PITCH <= sizeof(smem), "staging space");
+  static_assert(NW * NB * 32 * PITCH <= smem_bytes<BM, BN, WGM, WGN, BK, NB>(), "staging space");
   wait_vmcnt<0>();  // no LDS-direct load (the zero refill included) may land in the staging area
   lds::wait_lgkm0();
   barrier();
@@ -398,6 +407,37 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem
   }
 }
 
+template <int BM, int BN, int WGM, int WGN, int BK, int AL, int BL, class Epi>
+__global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem p, Epi epi) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[smem_bytes<BM, BN, WGM, WGN, BK, Epi::NB>()];
+  gemm_dma_tile<BM, BN, WGM, WGN, BK, AL, BL, Epi>(p, epi, blockIdx.x, smem);
+}
+
+// Tile shape and operand layouts of one problem of a paired launch.
+template <int BM_, int BN_, int WGM_, int WGN_, int BK_, int AL_, int BL_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, BK = BK_, AL = AL_, BL = BL_;
+  static constexpr int THREADS = 64 * WGM_ * WGN_;
+};
+
+// Two independent problems in one launch: work-groups 0 .. tiles1-1 take the
+// tiles of problem 1, the rest those of problem 2.  When each problem alone
+// would leave part of the chip idle in its last round of tiles, the other's
+// tiles fill it.
+template <class C1, class E1, class C2, class E2>
+__global__ void __launch_bounds__(C1::THREADS, 1)
+    gemm_dma_pair_kernel(GemmProblem p1, E1 e1, GemmProblem p2, E2 e2, int tiles1) {
+  static_assert(C1::THREADS == C2::THREADS, "both problems run on work-groups of one size");
+  constexpr int S1 = smem_bytes<C1::BM, C1::BN, C1::WGM, C1::WGN, C1::BK, E1::NB>();
+  constexpr int S2 = smem_bytes<C2::BM, C2::BN, C2::WGM, C2::WGN, C2::BK, E2::NB>();
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S1 > S2 ? S1 : S2];
+  const int w = blockIdx.x;
+  if (w < tiles1)
+    gemm_dma_tile<C1::BM, C1::BN, C1::WGM, C1::WGN, C1::BK, C1::AL, C1::BL, E1>(p1, e1, w, smem);
+  else
+    gemm_dma_tile<C2::BM, C2::BN, C2::WGM, C2::WGN, C2::BK, C2::AL, C2::BL, E2>(p2, e2, w - tiles1, smem);
+}
+
 }  // namespace gemm3
 
 // Host-side launcher: grid of ceil(M/BM) * ceil(N/BN) work-groups of 64 * WGM * WGN threads.
@@ -407,6 +447,18 @@ hipError_t launch_gemm_dma(const GemmProblem& p, const Epi& epi, hipStream_t str
   if (tiles == 0) return hipSuccess;
   hipLaunchKernelGGL((gemm3::gemm_dma_kernel<BM, BN, WGM, WGN, BK, AL, BL, Epi>), dim3(tiles),
                      dim3(64 * WGM * WGN), 0, stream, p, epi);
+  return hipGetLastError();
+}
+
+// Paired launcher: problem 1's tiles (dispatched first) then problem 2's.
+template <class C1, class C2, class E1, class E2>
+hipError_t launch_gemm_dma_pair(const GemmProblem& p1, const E1& e1, const GemmProblem& p2, const E2& e2,
+                                hipStream_t stream) {
+  const int t1 = ((p1.M + C1::BM - 1) / C1::BM) * ((p1.N + C1::BN - 1) / C1::BN);
+  const int t2 = ((p2.M + C2::BM - 1) / C2::BM) * ((p2.N + C2::BN - 1) / C2::BN);
+  if (t1 + t2 == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm3::gemm_dma_pair_kernel<C1, E1, C2, E2>), dim3(t1 + t2), dim3(C1::THREADS), 0, stream,
+                     p1, e1, p2, e2, t1);
   return hipGetLastError();
 }
 

@@ -83,12 +83,14 @@ GemmProblem problem(int M, int N, int K, const void* A, int64_t lda, const void*
 // chip clocks higher), with 128 or fewer the small tile wins.
 // TPSHARD_TILE=large|small overrides the choice (used by the tests to cover
 // both tile shapes at small sizes).
-bool use_small_tile(int M, int N, int bm, int bn) {
+int64_t tile_count(const GemmProblem& p, int bm, int bn) {
+  return (int64_t)((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
+}
+bool use_small_tile(int64_t big) {
   if (const char* force = std::getenv("TPSHARD_TILE")) {
     if (!std::strcmp(force, "large")) return false;
     if (!std::strcmp(force, "small")) return true;
   }
-  const int64_t big = (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   return big < (int64_t)kNumCUs * 9 / 16;
 }
 
@@ -96,13 +98,32 @@ template <int AL, int BL, class Epi>
 hipError_t gemm_bf16(const GemmProblem& p, const Epi& epi, hipStream_t st) {
   if constexpr (Epi::NB == 1) {
     Probe pr(st);
-    if (use_small_tile(p.M, p.N, 256, 256)) return launch_gemm_dma<128, 128, 2, 2, 64, AL, BL>(p, epi, st);
+    if (use_small_tile(tile_count(p, 256, 256))) return launch_gemm_dma<128, 128, 2, 2, 64, AL, BL>(p, epi, st);
     return launch_gemm_dma<256, 256, 4, 2, 64, AL, BL>(p, epi, st);
   } else {
     Probe pr(st);
-    if (use_small_tile(p.M, p.N, 256, 128)) return launch_gemm_dma<128, 64, 2, 2, 64, AL, BL>(p, epi, st);
+    if (use_small_tile(tile_count(p, 256, 128))) return launch_gemm_dma<128, 64, 2, 2, 64, AL, BL>(p, epi, st);
     return launch_gemm_dma<256, 128, 4, 2, 64, AL, BL>(p, epi, st);
   }
+}
+
+// Two independent bf16 GEMMs in one launch, p1's tiles dispatched first (the
+// longer K first, so the shorter tiles fill the last round).  Both take the
+// large tile unless their combined count of large tiles is below the
+// crossover above, then both the small one.  A GEMM whose last round of tiles
+// leaves CUs idle costs about a full round on its own (a power-limited chip
+// clocks only a little higher when partly idle); in a pair the other
+// problem's tiles take those CUs.
+template <int AL1, int BL1, int AL2, int BL2, class E1, class E2>
+hipError_t gemm_bf16_pair(const GemmProblem& p1, const E1& e1, const GemmProblem& p2, const E2& e2,
+                          hipStream_t st) {
+  constexpr int BN1 = E1::NB == 1 ? 256 : 128, BN2 = E2::NB == 1 ? 256 : 128;
+  Probe pr(st);
+  if (use_small_tile(tile_count(p1, 256, BN1) + tile_count(p2, 256, BN2)))
+    return launch_gemm_dma_pair<gemm3::TileCfg<128, BN1 / 2, 2, 2, 64, AL1, BL1>,
+                                gemm3::TileCfg<128, BN2 / 2, 2, 2, 64, AL2, BL2>>(p1, e1, p2, e2, st);
+  return launch_gemm_dma_pair<gemm3::TileCfg<256, BN1, 4, 2, 64, AL1, BL1>,
+                              gemm3::TileCfg<256, BN2, 4, 2, 64, AL2, BL2>>(p1, e1, p2, e2, st);
 }
 
 // Operands stored in bf16 run on the matrix cores, operands stored in fp32 on
@@ -202,27 +223,35 @@ int mlp_bwd_impl(const tp_mlp_desc& d, int f, const void* dOut, uint32_t thr, fl
     if ((e = gemm_any<T, MNMAJOR, MNMAJOR>(problem(f, h, T_, H, f, dYp, nullptr, h), epi, st)) != hipSuccess)
       return TP_EHIP;
   }
-  // a6: dW1_i = X^T dA_i  ([h, f], K = tokens); SwiGLU: dWg_i and dWu_i share the X^T tile
-  if (d.act == TP_GELU) {
-    EpiStore<float> epi{dW1, f, h, f};
-    e = gemm_any<T, MNMAJOR, MNMAJOR>(problem(h, f, T_, X, h, dA, nullptr, f), epi, st);
-  } else {
-    const T* dG = static_cast<const T*>(dA);
-    EpiStore2<float> epi{dW1, dW1 + (int64_t)h * f, f, h, f};
-    e = gemm_any<T, MNMAJOR, MNMAJOR>(problem(h, f, T_, X, h, dG, dG + Tf, f), epi, st);
+  // a6: dW1_i = X^T dA_i  ([h, f], K = tokens); SwiGLU: dWg_i and dWu_i share the X^T tile.
+  // a6: dX_i = dA_i W1_i^T  (SwiGLU: dG_i Wg_i^T + dU_i Wu_i^T, two K segments into one accumulator).
+  // The two are independent; bf16 shards run them as one paired launch.
+  GemmProblem pw = d.act == TP_GELU ? problem(h, f, T_, X, h, dA, nullptr, f)
+                                    : problem(h, f, T_, X, h, dA, static_cast<const T*>(dA) + Tf, f);
+  GemmProblem px = problem(T_, h, f, dA, f, W1, nullptr, f);
+  if (d.act == TP_SWIGLU) {
+    px.nseg = 2;
+    px.K[1] = f;
+    px.A[1] = reinterpret_cast<const uint16_t*>(static_cast<const T*>(dA) + Tf);
+    px.B[1][0] = static_cast<const uint16_t*>(Wu);
   }
-  if (e != hipSuccess) return TP_EHIP;
-  // a6: dX_i = dA_i W1_i^T  (SwiGLU: dG_i Wg_i^T + dU_i Wu_i^T, two K segments into one accumulator)
-  {
-    EpiStore<T> epi{static_cast<T*>(dX), h, T_, h};
-    GemmProblem p = problem(T_, h, f, dA, f, W1, nullptr, f);
-    if (d.act == TP_SWIGLU) {
-      p.nseg = 2;
-      p.K[1] = f;
-      p.A[1] = reinterpret_cast<const uint16_t*>(static_cast<const T*>(dA) + Tf);
-      p.B[1][0] = static_cast<const uint16_t*>(Wu);
+  EpiStore<T> ex{static_cast<T*>(dX), h, T_, h};
+  if (d.act == TP_GELU) {
+    EpiStore<float> ew{dW1, f, h, f};
+    if constexpr (std::is_same_v<T, float>) {
+      if ((e = gemm_any<T, MNMAJOR, MNMAJOR>(pw, ew, st)) != hipSuccess) return TP_EHIP;
+      e = gemm_any<T, KMAJOR, KMAJOR>(px, ex, st);
+    } else {
+      e = gemm_bf16_pair<MNMAJOR, MNMAJOR, KMAJOR, KMAJOR>(pw, ew, px, ex, st);
     }
-    e = gemm_any<T, KMAJOR, KMAJOR>(p, epi, st);
+  } else {
+    EpiStore2<float> ew{dW1, dW1 + (int64_t)h * f, f, h, f};
+    if constexpr (std::is_same_v<T, float>) {
+      if ((e = gemm_any<T, MNMAJOR, MNMAJOR>(pw, ew, st)) != hipSuccess) return TP_EHIP;
+      e = gemm_any<T, KMAJOR, KMAJOR>(px, ex, st);
+    } else {
+      e = gemm_bf16_pair<MNMAJOR, MNMAJOR, KMAJOR, KMAJOR>(pw, ew, px, ex, st);
+    }
   }
   return hip_status(e);
 }
@@ -499,12 +528,13 @@ int tp_attn_shard_bwd(const tp_attn_desc* d, const void* dZ, const void* X, cons
   const int D = d->d;
   const int T_ = (int)T64, h = (int)d->h, nq = q * D, nqkv = (q + 2 * kv) * D;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // dO_i = dZ Wo_i^T (Wo_i [q d, h] is K-contiguous for this product)
+  // dO_i = dZ Wo_i^T (Wo_i [q d, h] is K-contiguous for this product) and,
+  // independent of it, dWo_i = O_i^T dZ: one paired launch
   EpiStore<uint16_t> e1{static_cast<uint16_t*>(dO_i), nq, T_, nq};
-  if (gemm_bf16<KMAJOR, KMAJOR>(problem(T_, nq, h, dZ, h, Wo_i, nullptr, h), e1, st) != hipSuccess) return TP_EHIP;
-  // dWo_i = O_i^T dZ
   EpiStore<float> e2{dWo_i, h, nq, h};
-  if (gemm_bf16<MNMAJOR, MNMAJOR>(problem(nq, h, T_, O_i, nq, dZ, nullptr, h), e2, st) != hipSuccess)
+  if (gemm_bf16_pair<KMAJOR, KMAJOR, MNMAJOR, MNMAJOR>(problem(T_, nq, h, dZ, h, Wo_i, nullptr, h), e1,
+                                                       problem(nq, h, T_, O_i, nq, dZ, nullptr, h), e2,
+                                                       st) != hipSuccess)
     return TP_EHIP;
   // the core: row statistics, dK/dV, dQ
   attnb::BwdArgs a{};
@@ -540,13 +570,13 @@ int tp_attn_shard_bwd(const tp_attn_desc* d, const void* dZ, const void* X, cons
     e = D == 128 ? launch_attn_bwd_dq<128>(a, hg, st) : launch_attn_bwd_dq<64>(a, hg, st);
   }
   if (e != hipSuccess) return TP_EHIP;
-  // dWqkv_i = X^T dQKV_i
+  // dWqkv_i = X^T dQKV_i (K = tokens) and dX_i = dQKV_i Wqkv_i^T (Wqkv_i [h, (q+2kv) d]
+  // is K-contiguous for this product; K = (q+2kv) d): one paired launch, longer K first
   EpiStore<float> e3{dWqkv_i, nqkv, h, nqkv};
-  if (gemm_bf16<MNMAJOR, MNMAJOR>(problem(h, nqkv, T_, X, h, dQKV_i, nullptr, nqkv), e3, st) != hipSuccess)
-    return TP_EHIP;
-  // dX_i = dQKV_i Wqkv_i^T (Wqkv_i [h, (q+2kv) d] is K-contiguous for this product)
   EpiStore<uint16_t> e4{static_cast<uint16_t*>(dX_i), h, T_, h};
-  return hip_status(gemm_bf16<KMAJOR, KMAJOR>(problem(T_, h, nqkv, dQKV_i, nqkv, Wqkv_i, nullptr, nqkv), e4, st));
+  return hip_status(gemm_bf16_pair<MNMAJOR, MNMAJOR, KMAJOR, KMAJOR>(
+      problem(h, nqkv, T_, X, h, dQKV_i, nullptr, nqkv), e3,
+      problem(T_, h, nqkv, dQKV_i, nqkv, Wqkv_i, nullptr, nqkv), e4, st));
 }
 
 }  // extern "C"

@@ -105,21 +105,24 @@ def kernel_plan(mc, ac):
     plan.append(("mlp_bwd_dH_gemm_act", "a5", 2 * T * h * f, None))
     if mc.bias and mc.act == "gelu":
         plan.append(("mlp_bwd_db1_colsum", "a5", None, T * f * d + 4 * f))
-    plan += [("mlp_bwd_dW2_gemm", "a5", 2 * T * f * h, None),
-             ("mlp_bwd_dW1_gemm", "a6", 2 * T * h * f * n1, None),
-             ("mlp_bwd_dX_gemm", "a6", 2 * T * f * h * n1, None),
-             ("allreduce_bwd_sum", "a7", None, (mc.t + 1) * T * h * d)]
+    plan.append(("mlp_bwd_dW2_gemm", "a5", 2 * T * f * h, None))
+    if mc.bf16:
+        # dW1 (dWg, dWu) and dX are independent and share one paired launch
+        plan.append(("mlp_bwd_dW1_dX_gemm", "a6", 2 * T * h * f * n1 * 2, None))
+    else:
+        plan += [("mlp_bwd_dW1_gemm", "a6", 2 * T * h * f * n1, None),
+                 ("mlp_bwd_dX_gemm", "a6", 2 * T * f * h * n1, None)]
+    plan.append(("allreduce_bwd_sum", "a7", None, (mc.t + 1) * T * h * d))
     if ac is not None:
         # attention backward: algorithmic FLOPs per kernel (the score and dP
         # recomputations are not counted): dK/dV do dP, dV and dK, dQ does dQ
         pairs = ac.b * q * (ac.s * (ac.s + 1) // 2)
-        plan += [("attn_bwd_dO_gemm", "f1", 2 * Ta * ha * q * dh, None),
-                 ("attn_bwd_dWo_gemm", "f1", 2 * Ta * ha * q * dh, None),
+        # dO with dWo, and dWqkv with dX, run as paired launches
+        plan += [("attn_bwd_dO_dWo_gemm", "f1", 2 * 2 * Ta * ha * q * dh, None),
                  ("attn_bwd_stats", "f1", None, 2 * Ta * q * dh * 2 + ac.b * q * ac.s * 12),
                  ("attn_bwd_dkv", "f1", 6 * dh * pairs, None),
                  ("attn_bwd_dq", "f1", 2 * dh * pairs, None),
-                 ("attn_bwd_dWqkv_gemm", "f1", 2 * Ta * ha * (q + 2 * kv) * dh, None),
-                 ("attn_bwd_dX_gemm", "f1", 2 * Ta * ha * (q + 2 * kv) * dh, None),
+                 ("attn_bwd_dWqkv_dX_gemm", "f1", 2 * 2 * Ta * ha * (q + 2 * kv) * dh, None),
                  ("allreduce_attn_bwd_sum", "a7", None, (ac.t + 1) * Ta * ha * 2)]
     return plan
 
