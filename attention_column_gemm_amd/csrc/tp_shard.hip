@@ -205,24 +205,30 @@ int mlp_bwd_impl(const tp_mlp_desc& d, int f, const void* dOut, uint32_t thr, fl
     dYp = dY;
   }
   if (db2 && (e = colsum<T>(T_, h, dYp, db2, st)) != hipSuccess) return TP_EHIP;
-  // a5: dH = dY W2^T with the activation backward fused
-  if (d.act == TP_GELU) {
-    EpiGeluBwd<T> epi{static_cast<const T*>(saved), static_cast<T*>(dA), f, T_, f};
-    e = gemm_any<T, KMAJOR, KMAJOR>(problem(T_, f, h, dYp, h, W2, nullptr, h), epi, st);
-  } else {
-    const T* G = static_cast<const T*>(saved);
-    T* dG = static_cast<T*>(dA);
-    EpiSwigluBwd<T> epi{G, G + Tf, dG, dG + Tf, f, T_, f};
-    e = gemm_any<T, KMAJOR, KMAJOR>(problem(T_, f, h, dYp, h, W2, nullptr, h), epi, st);
+  // a5: dH = dY W2^T with the activation backward fused, and dW2_i = H_i^T dY
+  // ([f, h], K = tokens), independent of it: one paired launch for bf16 shards
+  {
+    const GemmProblem ph = problem(T_, f, h, dYp, h, W2, nullptr, h);
+    const GemmProblem pw = problem(f, h, T_, H, f, dYp, nullptr, h);
+    EpiStore<float> ew{dW2, h, f, h};
+    auto run = [&](const auto& eh) -> hipError_t {
+      if constexpr (std::is_same_v<T, float>) {
+        hipError_t r = gemm_any<T, KMAJOR, KMAJOR>(ph, eh, st);
+        return r != hipSuccess ? r : gemm_any<T, MNMAJOR, MNMAJOR>(pw, ew, st);
+      } else {
+        return gemm_bf16_pair<KMAJOR, KMAJOR, MNMAJOR, MNMAJOR>(ph, eh, pw, ew, st);
+      }
+    };
+    if (d.act == TP_GELU) {
+      e = run(EpiGeluBwd<T>{static_cast<const T*>(saved), static_cast<T*>(dA), f, T_, f});
+    } else {
+      const T* G = static_cast<const T*>(saved);
+      T* dG = static_cast<T*>(dA);
+      e = run(EpiSwigluBwd<T>{G, G + Tf, dG, dG + Tf, f, T_, f});
+    }
   }
   if (e != hipSuccess) return TP_EHIP;
   if (db1 && (e = colsum<T>(T_, f, dA, db1, st)) != hipSuccess) return TP_EHIP;
-  // a5: dW2_i = H_i^T dY   ([f, h], K = tokens)
-  {
-    EpiStore<float> epi{dW2, h, f, h};
-    if ((e = gemm_any<T, MNMAJOR, MNMAJOR>(problem(f, h, T_, H, f, dYp, nullptr, h), epi, st)) != hipSuccess)
-      return TP_EHIP;
-  }
   // a6: dW1_i = X^T dA_i  ([h, f], K = tokens); SwiGLU: dWg_i and dWu_i share the X^T tile.
   // a6: dX_i = dA_i W1_i^T  (SwiGLU: dG_i Wg_i^T + dU_i Wu_i^T, two K segments into one accumulator).
   // The two are independent; bf16 shards run them as one paired launch.

@@ -102,10 +102,14 @@ def kernel_plan(mc, ac):
         plan.append(("mlp_bwd_dropout", "a4", None, 2 * T * h * d))
     if mc.bias:
         plan.append(("mlp_bwd_db2_colsum", "a4", None, T * h * d + 4 * h))
-    plan.append(("mlp_bwd_dH_gemm_act", "a5", 2 * T * h * f, None))
+    if mc.bf16:
+        # dH (with the activation backward) and dW2 are independent: one paired launch
+        plan.append(("mlp_bwd_dH_dW2_gemm_act", "a5", 2 * 2 * T * h * f, None))
+    else:
+        plan += [("mlp_bwd_dH_gemm_act", "a5", 2 * T * h * f, None),
+                 ("mlp_bwd_dW2_gemm", "a5", 2 * T * f * h, None)]
     if mc.bias and mc.act == "gelu":
         plan.append(("mlp_bwd_db1_colsum", "a5", None, T * f * d + 4 * f))
-    plan.append(("mlp_bwd_dW2_gemm", "a5", 2 * T * f * h, None))
     if mc.bf16:
         # dW1 (dWg, dWu) and dX are independent and share one paired launch
         plan.append(("mlp_bwd_dW1_dX_gemm", "a6", 2 * T * h * f * n1 * 2, None))
