@@ -191,8 +191,11 @@ constexpr int smem_bytes() {
 
 // One output tile: tile w of problem p's launch, computed by the whole
 // work-group with `smem` (smem_bytes() bytes, 1 KiB aligned) as its LDS.
-template <int BM, int BN, int WGM, int WGN, int BK, int AL, int BL, class Epi>
-__device__ __forceinline__ void gemm_dma_tile(const GemmProblem& p, const Epi& epi, int w, uint8_t* smem) {
+// With KRANGE the K tiles kt_begin .. kt_begin + n_kt - 1 are accumulated
+// (the K tiles of the segments numbered consecutively), otherwise all of them.
+template <int BM, int BN, int WGM, int WGN, int BK, int AL, int BL, class Epi, bool KRANGE = false>
+__device__ __forceinline__ void gemm_dma_tile(const GemmProblem& p, const Epi& epi, int w, uint8_t* smem,
+                                              int kt_begin = 0, int n_kt = 0) {
   constexpr int NW = WGM * WGN;
   constexpr int NB = Epi::NB;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -229,7 +232,8 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmProblem& p, const Epi& e
   lb.init(n0, (uint32_t)p.ldb[0] * 2u, p.N);
 
   const int nk0 = (p.K[0] + BK - 1) / BK;
-  const int nk = nk0 + (p.nseg > 1 ? (p.K[1] + BK - 1) / BK : 0);
+  const int nk_all = nk0 + (p.nseg > 1 ? (p.K[1] + BK - 1) / BK : 0);
+  const int nk = KRANGE ? n_kt : nk_all;  // K tiles of this work-group, counted from kt_begin
   DOperand opa[2], opb[2][NB];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -238,11 +242,13 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmProblem& p, const Epi& e
     for (int b = 0; b < NB; ++b) opb[s][b] = make_doperand(p.B[s][b], p.ldb[s], p.N, p.K[s], BL);
   }
 
-  // kt may be nk (one past the last tile): every offset then lies past K and
-  // the loads only write zeros into LDS
+  // kt (local) may be nk (one past the last tile): it is then sent past the
+  // end of K, where every offset is out of range and the loads only write
+  // zeros into LDS
   auto issue = [&](int kt) {
-    const int s = (kt < nk0 || p.nseg == 1) ? 0 : 1;
-    const int k0 = (kt - (s ? nk0 : 0)) * BK;
+    const int gk = KRANGE ? (kt < nk ? kt_begin + kt : nk_all) : kt;
+    const int s = (gk < nk0 || p.nseg == 1) ? 0 : 1;
+    const int k0 = (gk - (s ? nk0 : 0)) * BK;
     const uint32_t st = lds_base + (uint32_t)(kt % NSTAGE) * STAGE;
     la.issue(opa[s], k0, st);
 #pragma unroll
@@ -407,10 +413,97 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmProblem& p, const Epi& e
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int AL, int BL, class Epi>
-__global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem p, Epi epi) {
+// Split tail.  When a launch's tile count leaves its last round of 256 CUs
+// at most half full, that round costs about as long as a full one.  The
+// last `tail` tiles of the dispatch order are then each computed by two
+// work-groups over the two halves of K, so the round takes half as long:
+// the halves write fp32 partial tiles to `scratch` ([tail][2][NB][BM][BN]),
+// and split_tail_finish_kernel adds them (first half + second half) and runs
+// the epilogue.  Requires a tile count that is a multiple of 8 (one equal run
+// of tiles per XCD) with tail <= 128.
+struct SplitTail {
+  float* scratch;  // null: no split
+  int full;        // work-groups 0 .. full-1 compute whole tiles
+  int tail;        // tiles split in two
+};
+
+// fp32 partial tile of a split: v for row m, columns n .. n+3 of tile (m0, n0).
+template <int BM, int BN, int NB_>
+struct EpiPartial {
+  static constexpr int NB = NB_;
+  struct Aux {};
+  float* base;  // this half's [NB][BM][BN] block
+  int m0, n0;
+  __device__ __forceinline__ void load(int, int, Aux&) const {}
+  __device__ __forceinline__ void operator()(int m, int n, const float (&v)[NB][4], const Aux& = Aux()) const {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const f32x4 x = {v[b][0], v[b][1], v[b][2], v[b][3]};
+      __builtin_nontemporal_store(
+          x, reinterpret_cast<f32x4*>(base + ((int64_t)b * BM + (m - m0)) * BN + (n - n0)));
+    }
+  }
+};
+
+// Tile coordinates of split slot `slot` (0 .. tail-1), half of XCD run
+// position full/8 + slot/8 on XCD slot%8: the tile that work-group
+// (position * 8 + XCD) of an unsplit launch computes.
+__device__ __forceinline__ void split_tile(const SplitTail& sp, int slot, int tiles_m, int tiles_n, int& tm, int& tn) {
+  gemm::tile_coords((sp.full / 8 + slot / 8) * 8 + slot % 8, tiles_m, tiles_n, tm, tn);
+}
+
+// SPLIT: the launch may carry a split tail (instantiated only where a caller
+// asks for it, so the plain kernel keeps its register budget).
+template <int BM, int BN, int WGM, int WGN, int BK, int AL, int BL, class Epi, bool SPLIT = false>
+__global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_dma_kernel(GemmProblem p, Epi epi, SplitTail sp) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[smem_bytes<BM, BN, WGM, WGN, BK, Epi::NB>()];
-  gemm_dma_tile<BM, BN, WGM, WGN, BK, AL, BL, Epi>(p, epi, blockIdx.x, smem);
+  const int w = blockIdx.x;
+  if (!SPLIT || w < sp.full) {
+    gemm_dma_tile<BM, BN, WGM, WGN, BK, AL, BL, Epi>(p, epi, w, smem);
+    return;
+  }
+  // split work-group s = w - full runs on XCD s % 8 and takes half (s/8) % 2
+  // of slot (s/8)/2 * 8 + s % 8
+  const int s = w - sp.full, x = s & 7, j = s >> 3;
+  const int slot = (j >> 1) * 8 + x, part = j & 1;
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  int tm, tn;
+  split_tile(sp, slot, tiles_m, tiles_n, tm, tn);
+  const int nk = (p.K[0] + BK - 1) / BK + (p.nseg > 1 ? (p.K[1] + BK - 1) / BK : 0);
+  const int h0 = nk / 2;
+  EpiPartial<BM, BN, Epi::NB> ep{sp.scratch + (int64_t)(slot * 2 + part) * Epi::NB * BM * BN, tm * BM, tn * BN};
+  gemm_dma_tile<BM, BN, WGM, WGN, BK, AL, BL, EpiPartial<BM, BN, Epi::NB>, true>(
+      p, ep, (sp.full / 8 + slot / 8) * 8 + slot % 8, smem, part ? h0 : 0, part ? nk - h0 : h0);
+}
+
+// Sum of the two halves of every split tile, in a fixed order, handed to the
+// epilogue: one thread per row and four columns.
+template <int BM, int BN, class Epi>
+__global__ void __launch_bounds__(256) split_tail_finish_kernel(GemmProblem p, Epi epi, SplitTail sp) {
+  constexpr int NB = Epi::NB, Q = BN / 4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)sp.tail * BM * Q) return;
+  const int slot = (int)(i / (BM * Q)), r = (int)(i / Q % BM), c = (int)(i % Q) * 4;
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  int tm, tn;
+  split_tile(sp, slot, tiles_m, tiles_n, tm, tn);
+  const int m = tm * BM + r, n = tn * BN + c;
+  if (m >= p.M || n >= p.N) return;
+  const float* h0 = sp.scratch + (int64_t)slot * 2 * NB * BM * BN;
+  const float* h1 = h0 + NB * BM * BN;
+  float v[NB][4];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(h0 + ((int64_t)b * BM + r) * BN + c);
+    const f32x4 bb = *reinterpret_cast<const f32x4*>(h1 + ((int64_t)b * BM + r) * BN + c);
+    v[b][0] = a[0] + bb[0];
+    v[b][1] = a[1] + bb[1];
+    v[b][2] = a[2] + bb[2];
+    v[b][3] = a[3] + bb[3];
+  }
+  typename Epi::Aux aux;
+  epi.load(m, n, aux);
+  epi(m, n, v, aux);
 }
 
 // Tile shape and operand layouts of one problem of a paired launch.
@@ -446,7 +539,36 @@ hipError_t launch_gemm_dma(const GemmProblem& p, const Epi& epi, hipStream_t str
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   if (tiles == 0) return hipSuccess;
   hipLaunchKernelGGL((gemm3::gemm_dma_kernel<BM, BN, WGM, WGN, BK, AL, BL, Epi>), dim3(tiles),
-                     dim3(64 * WGM * WGN), 0, stream, p, epi);
+                     dim3(64 * WGM * WGN), 0, stream, p, epi, gemm3::SplitTail{nullptr, tiles, 0});
+  return hipGetLastError();
+}
+
+// Scratch floats a split-tail launch of this tile shape needs, or 0 when the
+// split does not apply (tile count not a multiple of 8, last round more than
+// half full or already full, fewer than two K tiles per half).
+template <int BM, int BN, int BK, int NB>
+int64_t split_tail_floats(const GemmProblem& p) {
+  const int64_t tiles = (int64_t)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  const int64_t tail = tiles % 256;
+  const int nk = (p.K[0] + BK - 1) / BK + (p.nseg > 1 ? (p.K[1] + BK - 1) / BK : 0);
+  if (tiles < 256 || tiles % 8 || tail == 0 || tail > 128 || nk < 4) return 0;
+  return tail * 2 * NB * BM * BN;
+}
+
+// Split-tail launch: the GEMM (whole tiles, then the split halves of the
+// last `tail` tiles) and the kernel that finishes those tiles.
+template <int BM, int BN, int WGM, int WGN, int BK, int AL, int BL, class Epi>
+hipError_t launch_gemm_dma_split(const GemmProblem& p, const Epi& epi, float* scratch, hipStream_t stream) {
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  const int tail = tiles % 256;
+  const gemm3::SplitTail sp{scratch, tiles - tail, tail};
+  hipLaunchKernelGGL((gemm3::gemm_dma_kernel<BM, BN, WGM, WGN, BK, AL, BL, Epi, true>), dim3(tiles + tail),
+                     dim3(64 * WGM * WGN), 0, stream, p, epi, sp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)tail * BM * (BN / 4);
+  hipLaunchKernelGGL((gemm3::split_tail_finish_kernel<BM, BN, Epi>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     stream, p, epi, sp);
   return hipGetLastError();
 }
 

@@ -83,6 +83,13 @@ GemmProblem problem(int M, int N, int K, const void* A, int64_t lda, const void*
 // chip clocks higher), with 128 or fewer the small tile wins.
 // TPSHARD_TILE=large|small overrides the choice (used by the tests to cover
 // both tile shapes at small sizes).
+// TPSHARD_SPLIT_TAIL=0 turns the split of a GEMM's last round off (the
+// tests compare both ways).
+bool split_tail_enabled() {
+  const char* v = std::getenv("TPSHARD_SPLIT_TAIL");
+  return !(v && !std::strcmp(v, "0"));
+}
+
 int64_t tile_count(const GemmProblem& p, int bm, int bn) {
   return (int64_t)((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
 }
@@ -96,15 +103,24 @@ bool use_small_tile(int64_t big) {
 
 template <int AL, int BL, class Epi>
 hipError_t gemm_bf16(const GemmProblem& p, const Epi& epi, hipStream_t st) {
-  if constexpr (Epi::NB == 1) {
-    Probe pr(st);
-    if (use_small_tile(tile_count(p, 256, 256))) return launch_gemm_dma<128, 128, 2, 2, 64, AL, BL>(p, epi, st);
-    return launch_gemm_dma<256, 256, 4, 2, 64, AL, BL>(p, epi, st);
-  } else {
-    Probe pr(st);
-    if (use_small_tile(tile_count(p, 256, 128))) return launch_gemm_dma<128, 64, 2, 2, 64, AL, BL>(p, epi, st);
-    return launch_gemm_dma<256, 128, 4, 2, 64, AL, BL>(p, epi, st);
-  }
+  constexpr int BN = Epi::NB == 1 ? 256 : 128;
+  Probe pr(st);
+  if (use_small_tile(tile_count(p, 256, BN))) return launch_gemm_dma<128, BN / 2, 2, 2, 64, AL, BL>(p, epi, st);
+  return launch_gemm_dma<256, BN, 4, 2, 64, AL, BL>(p, epi, st);
+}
+
+// gemm_bf16 with device memory `scratch` (scratch_bytes bytes, 16-byte
+// aligned) that the call may overwrite: when it is large enough and the large
+// tile's last round would be at most half full, that round is split over K
+// (SplitTail in gemm_dma.hpp).
+template <int AL, int BL, class Epi>
+hipError_t gemm_bf16_split(const GemmProblem& p, const Epi& epi, hipStream_t st, void* scratch, int64_t scratch_bytes) {
+  constexpr int BN = Epi::NB == 1 ? 256 : 128;
+  const int64_t need = split_tail_floats<256, BN, 64, Epi::NB>(p) * 4;
+  if (!scratch || need == 0 || need > scratch_bytes || !split_tail_enabled() || use_small_tile(tile_count(p, 256, BN)))
+    return gemm_bf16<AL, BL>(p, epi, st);
+  Probe pr(st);
+  return launch_gemm_dma_split<256, BN, 4, 2, 64, AL, BL>(p, epi, static_cast<float*>(scratch), st);
 }
 
 // Two independent bf16 GEMMs in one launch, p1's tiles dispatched first (the
@@ -184,7 +200,10 @@ int mlp_fwd_impl(const tp_mlp_desc& d, int f, const void* X, const void* W1, con
   } else {
     T* G = static_cast<T*>(saved);
     EpiSwigluFwd<T> epi{G, G + (int64_t)T_ * f, static_cast<T*>(H), f, T_, f};
-    e = gemm_any<T, KMAJOR, MNMAJOR>(problem(T_, f, h, X, h, W1, Wu, f), epi, st);
+    if constexpr (std::is_same_v<T, float>)
+      e = gemm_any<T, KMAJOR, MNMAJOR>(problem(T_, f, h, X, h, W1, Wu, f), epi, st);
+    else  // Z_i is written only by the row GEMM below: until then it serves as scratch
+      e = gemm_bf16_split<KMAJOR, MNMAJOR>(problem(T_, f, h, X, h, W1, Wu, f), epi, st, Z, (int64_t)T_ * h * 2);
   }
   if (e != hipSuccess) return TP_EHIP;
   EpiStore<T> epi2{static_cast<T*>(Z), h, T_, h};

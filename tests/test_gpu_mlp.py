@@ -197,3 +197,23 @@ def test_mlp_cfg5_rank0_sampled():
     rows = edge_indices(c.tokens, extra=8, seed=5)
     cols = edge_indices(c.f, tiles=(64, 128, 256), extra=4, seed=6)
     _sampled_rank(c, 0, X, dOut, w, rows, cols)
+
+
+def test_mlp_split_tail_parity(monkeypatch):
+    """SwiGLU column GEMM whose last round of large tiles is split over K:
+    T=4000, h=256, f=2104 gives 16 x 17 = 272 tiles of 256 x 128 (ragged in
+    rows and columns), the last 16 computed as two K halves and finished by
+    a separate kernel.  Compared with the oracle with the split on and off."""
+    torch = need_gpu()
+    c = I.custom_mlp(106, 2, 2000, 256, 2104, 1, "swiglu", "bf16")
+    X, dOut = I.mlp_activation(c)
+    w = I.mlp_rank_weights(c, 0)
+    fw, bw = O.shard_step(dOut, X, w["W1"], w["W2"], act=c.act, Wu_i=w["Wu"], p=0.0, seed=c.seed)
+    for split in ("1", "0"):
+        monkeypatch.setenv("TPSHARD_SPLIT_TAIL", split)
+        banner(f"mlp split tail={split} T={c.tokens} h={c.h} f={c.f}")
+        sh = _gpu_rank(c, 0, X, dOut, w)
+        torch.cuda.synchronize()
+        _compare_rank(c, sh, fw, bw, tag=f"split{split}.")
+        _compare_rank_grads(c, sh, bw, tag=f"split{split}.")
+        del sh
