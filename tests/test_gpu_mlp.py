@@ -199,13 +199,22 @@ def test_mlp_cfg5_rank0_sampled():
     _sampled_rank(c, 0, X, dOut, w, rows, cols)
 
 
-def test_mlp_split_tail_parity(monkeypatch):
-    """SwiGLU column GEMM whose last round of large tiles is split over K:
-    T=4000, h=256, f=2104 gives 16 x 17 = 272 tiles of 256 x 128 (ragged in
-    rows and columns), the last 16 computed as two K halves and finished by
-    a separate kernel.  Compared with the oracle with the split on and off."""
+SPLIT_CASES = {
+    # column GEMM: 16 x 17 = 272 tiles of 256 x 128, ragged in rows and columns; the last 16 split
+    "col_T4000_h256_f2104": (106, 2, 2000, 256, 2104),
+    # column GEMM: one ragged row of 272 tiles, K = h = 200 in four 64-deep tiles (two per half)
+    "col_T250_h200_f34800": (107, 1, 250, 200, 34800),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT_CASES))
+def test_mlp_split_tail_parity(name, monkeypatch):
+    """GEMMs whose last round of large tiles is at most half full run it as
+    two K halves per tile, finished by a separate kernel that adds the halves
+    and runs the epilogue.  Compared with the oracle with the split on and off."""
     torch = need_gpu()
-    c = I.custom_mlp(106, 2, 2000, 256, 2104, 1, "swiglu", "bf16")
+    cfg, b, s, h, h_ffn = SPLIT_CASES[name]
+    c = I.custom_mlp(cfg, b, s, h, h_ffn, 1, "swiglu", "bf16")
     X, dOut = I.mlp_activation(c)
     w = I.mlp_rank_weights(c, 0)
     fw, bw = O.shard_step(dOut, X, w["W1"], w["W2"], act=c.act, Wu_i=w["Wu"], p=0.0, seed=c.seed)
