@@ -200,29 +200,43 @@ def test_mlp_cfg5_rank0_sampled():
 
 
 SPLIT_CASES = {
-    # column GEMM: 16 x 17 = 272 tiles of 256 x 128, ragged in rows and columns; the last 16 split
-    "col_T4000_h256_f2104": (106, 2, 2000, 256, 2104),
-    # column GEMM: one ragged row of 272 tiles, K = h = 200 in four 64-deep tiles (two per half)
-    "col_T250_h200_f34800": (107, 1, 250, 200, 34800),
+    # column GEMM: 16 x 17 = 272 tiles of 256 x 128, ragged in rows and columns; the last 16 are
+    # split, their partial tiles (8.4 MB) fitting in Z_i's memory (T h bf16 = 8.4 MB)
+    "col_T4000_h1056_f2104": (106, 2, 2000, 1056, 2104),
+    # one ragged row of 272 column tiles: K = h = 200 in four 64-deep tiles (two per half); Z_i's
+    # memory (0.1 MB) is too small for the partials, so this runs unsplit both ways
+    "col_T250_h200_f34800_no_room": (107, 1, 250, 200, 34800),
 }
 
 
 @pytest.mark.parametrize("name", list(SPLIT_CASES))
 def test_mlp_split_tail_parity(name, monkeypatch):
-    """GEMMs whose last round of large tiles is at most half full run it as
-    two K halves per tile, finished by a separate kernel that adds the halves
-    and runs the epilogue.  Compared with the oracle with the split on and off."""
+    """A column GEMM whose last round of large tiles is at most half full runs
+    it as two K halves per tile (fp32 partial tiles in Z_i's memory), finished
+    by a kernel that adds the halves and runs the SwiGLU epilogue.  Forward
+    outputs against the oracle with the split on and off; where the split
+    applies, the two runs differ in rounding (proof that it ran)."""
     torch = need_gpu()
+    from attention_column_gemm_amd.shard import MLPShard
     cfg, b, s, h, h_ffn = SPLIT_CASES[name]
     c = I.custom_mlp(cfg, b, s, h, h_ffn, 1, "swiglu", "bf16")
     X, dOut = I.mlp_activation(c)
     w = I.mlp_rank_weights(c, 0)
-    fw, bw = O.shard_step(dOut, X, w["W1"], w["W2"], act=c.act, Wu_i=w["Wu"], p=0.0, seed=c.seed)
+    fw = O.shard_forward(X, w["W1"], w["W2"], act=c.act, Wu_i=w["Wu"])
+    outs = {}
     for split in ("1", "0"):
         monkeypatch.setenv("TPSHARD_SPLIT_TAIL", split)
         banner(f"mlp split tail={split} T={c.tokens} h={c.h} f={c.f}")
-        sh = _gpu_rank(c, 0, X, dOut, w)
+        sh = MLPShard(c.tokens, c.h, c.h_ffn, c.t, 0, act=c.act, dtype=c.dtype)
+        sh.load(X, w["W1"], w["Wu"], w["b1"], w["W2"], dOut)
+        sh.forward()
         torch.cuda.synchronize()
-        _compare_rank(c, sh, fw, bw, tag=f"split{split}.")
-        _compare_rank_grads(c, sh, bw, tag=f"split{split}.")
+        tol = TOL[c.dtype]
+        check(f"split{split}.G_i", _np(sh.saved[0]), fw["G"], tol)
+        check(f"split{split}.U_i", _np(sh.saved[1]), fw["U"], tol)
+        check(f"split{split}.H_i", _np(sh.H), fw["H"], tol)
+        check(f"split{split}.Z_i", _np(sh.Z), fw["Z"], tol)
+        outs[split] = sh.saved[0].clone()
         del sh
+    ran = not torch.equal(outs["1"], outs["0"])
+    assert ran == ("no_room" not in name), "the split ran where it should not, or did not run where it should"
