@@ -152,7 +152,10 @@ int tp_attn_shard_heads(int32_t n_q, int32_t n_kv, int32_t t, int32_t rank, int3
  *   W2_i  [f, h]   second-layer rows of this rank
  *   saved_i        out: GeLU A_i [T, f]; SwiGLU G_i then U_i, two [T, f] blocks
  *   H_i   [T, f]   out: activation
- *   Z_i   [T, h]   out: partial output of this rank
+ *   Z_i   [T, h]   out: partial output of this rank.  Its memory is also
+ *                  scratch for the column GEMM (fp32 partial tiles when that
+ *                  GEMM's last round of tiles is split over K) before the row
+ *                  GEMM writes it, so it must not overlap any other argument.
  */
 int tp_mlp_shard_fwd(const tp_mlp_desc* desc, const void* X, const void* W1_i, const void* Wu_i,
                      const void* b1_i, const void* W2_i, void* saved_i, void* H_i, void* Z_i,
