@@ -242,8 +242,9 @@ def cpu_baseline(mc, X, dOut, w, budget_s=12.0):
                       f"(all weights; {flops / 1e9:.1f} GFLOP in float64 numpy/BLAS, {elapsed:.1f} s)"}
 
 
-def load_traffic(kernel_label):
-    """HBM bytes per launch from the rocprofv3 PMC summary, if taken on the current sources."""
+def load_traffic(kernel_label, workload):
+    """HBM bytes per launch from the rocprofv3 PMC summary, if taken on the current sources
+    and on this workload."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -251,7 +252,7 @@ def load_traffic(kernel_label):
         rec = json.load(open(path))
     except Exception:
         return None
-    if rec.get("source_hash") != source_hash():
+    if rec.get("source_hash") != source_hash() or rec.get("workload") != workload:
         return None
     ent = rec.get("kernels", {}).get(kernel_label)
     return None if ent is None else ent.get("bytes_per_launch")
@@ -418,12 +419,12 @@ def main():
         ach = dflops / (kern_ms[di] * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": dl, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "flops_per_launch": dflops,
-                "avg_ms": round(float(kern_ms[di]), 5), "traffic": load_traffic(dl)}
+                "avg_ms": round(float(kern_ms[di]), 5), "traffic": load_traffic(dl, args.workload)}
     else:
         ach = dbytes / (kern_ms[di] * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": dl, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "bytes_per_launch": dbytes,
-                "avg_ms": round(float(kern_ms[di]), 5), "traffic": load_traffic(dl)}
+                "avg_ms": round(float(kern_ms[di]), 5), "traffic": load_traffic(dl, args.workload)}
 
     res = {
         "metric": METRIC,

@@ -20,3 +20,38 @@ def test_more_than_one_gpu_exits_with_a_message():
 def test_unknown_workload_is_rejected():
     r = _run("--workload", "cfg9")
     assert r.returncode != 0
+
+
+def _bench_module():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_traffic_figures_apply_only_to_their_workload_and_sources():
+    import json
+    bench = _bench_module()
+    rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+    label, ent = next(iter(rec["kernels"].items()))
+    current = rec["source_hash"] == bench.source_hash()
+    got = bench.load_traffic(label, rec["workload"])
+    assert got == (ent["bytes_per_launch"] if current else None)
+    other = "cfg2" if rec["workload"] != "cfg2" else "cfg3"
+    assert bench.load_traffic(label, other) is None
+
+
+def test_kernel_plan_matches_the_paired_launches():
+    """bf16 backward GEMM pairs are one launch each; fp32 shards keep them apart."""
+    from attention_column_gemm_amd import inputs as I
+    bench = _bench_module()
+    plan = [p[0] for p in bench.kernel_plan(I.MLP_CONFIGS[5], I.ATTN_CONFIGS[5])]
+    assert "mlp_bwd_dH_dW2_gemm_act" in plan and "mlp_bwd_dW1_dX_gemm" in plan
+    assert "attn_bwd_dO_dWo_gemm" in plan and "attn_bwd_dWqkv_dX_gemm" in plan
+    fp32 = [p[0] for p in bench.kernel_plan(I.MLP_CONFIGS[1], None)]
+    assert "mlp_bwd_dH_gemm_act" in fp32 and "mlp_bwd_dX_gemm" in fp32
+    # the paired entries carry both problems' FLOPs
+    c = I.MLP_CONFIGS[5]
+    total = sum(p[2] or 0 for p in bench.kernel_plan(c, None) if p[0].startswith("mlp_"))
+    assert total == c.flops_per_rank()
