@@ -66,6 +66,12 @@ struct BwdArgs {
   int causal;
   float scale;       // 1 / sqrt(d)
   float scale_log2;  // log2(e) / sqrt(d)
+  // dK/dV load balance: key blocks 0 .. split-1 of every (sequence, KV head),
+  // the ones that see the most queries, are each taken by two work-groups
+  // over the two halves of their items; the halves' fp32 sums go to dkv_part
+  // ([b kv split][2][2 D/32][16][64]) and attn_bwd_dkv_combine_kernel adds them.
+  float* dkv_part;
+  int split;
 };
 
 // ---- stats -------------------------------------------------------------------
@@ -121,8 +127,26 @@ __global__ void __launch_bounds__(64 * DKV_WAVES, 1) attn_bwd_dkv_kernel(BwdArgs
 
   const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kb = blockIdx.x, k0 = kb * KEY_BLOCK;
-  const int beta = blockIdx.y / a.kv, g = blockIdx.y % a.kv;
+  // Job J of the 1-D grid, heaviest first: for i < split, three jobs per
+  // (sequence, KV head): both halves of key block i, then whole block
+  // split + i; the remaining whole blocks 2 split .. nkb-1 follow in order.
+  const int nkb = (a.s + KEY_BLOCK - 1) / KEY_BLOCK;
+  const int BG = a.b * a.kv, J = blockIdx.x;
+  int kb, bg, part;  // part: -1 whole, else the half
+  if (J < 3 * BG * a.split) {
+    const int i = J / (3 * BG), r = J % (3 * BG);
+    if (r < 2 * BG) {
+      kb = i; part = r / BG; bg = r % BG;
+    } else {
+      kb = a.split + i; part = -1; bg = r - 2 * BG;
+    }
+  } else {
+    const int r = J - 3 * BG * a.split;
+    kb = 2 * a.split + r / BG; part = -1; bg = r % BG;
+  }
+  (void)nkb;
+  const int k0 = kb * KEY_BLOCK;
+  const int beta = bg / a.kv, g = bg % a.kv;
   const int group = a.q / a.kv;
   const int64_t tok0 = (int64_t)beta * a.s;
   const uint32_t ldq = (uint32_t)a.ld_qkv * 2u, ldo = (uint32_t)a.ld_o * 2u;
@@ -155,8 +179,9 @@ __global__ void __launch_bounds__(64 * DKV_WAVES, 1) attn_bwd_dkv_kernel(BwdArgs
 
   // items run from the last query tile backwards, so the work-groups of one
   // KV head (all key blocks) read the same Q and dO tiles at about the same
-  // time and share them in L2
-  for (int n = wave; n < nitems; n += DKV_WAVES) {
+  // time and share them in L2; a half takes one half of the items
+  const int n_begin = part == 1 ? nitems / 2 : 0, n_end = part == 0 ? nitems / 2 : nitems;
+  for (int n = n_begin + wave; n < n_end; n += DKV_WAVES) {
     const int j = g * group + n / ntile;
     const int i0 = (nqt - 1 - n % ntile) * Q_TILE;
     lds::wait_lgkm0();  // this wave's reads of its slot are done
@@ -258,6 +283,19 @@ __global__ void __launch_bounds__(64 * DKV_WAVES, 1) attn_bwd_dkv_kernel(BwdArgs
   }
   __syncthreads();
   const int key = k0 + l32;
+  if (part >= 0) {  // a half: fp32 sums, unscaled, in [u][e][lane] order
+    float* dst = a.dkv_part + ((int64_t)(bg * a.split + kb) * 2 + part) * (2 * DT * 16 * 64);
+    for (int u = wave; u < 2 * DT; u += DKV_WAVES) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float x = red[slot_of(0, u, e)];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) x += red[slot_of(w, u, e)];
+        dst[(u * 16 + e) * 64 + lane] = x;
+      }
+    }
+    return;
+  }
   for (int u = wave; u < 2 * DT; u += DKV_WAVES) {
     const bool is_k = u < DT;
     const int dt = is_k ? u : u - DT;
@@ -278,6 +316,38 @@ __global__ void __launch_bounds__(64 * DKV_WAVES, 1) attn_bwd_dkv_kernel(BwdArgs
       }
     }
   }
+}
+
+// dK/dV of the split key blocks: the two halves added in a fixed order (first
+// + second), dK scaled, stored as bf16.  One thread per (block, u, lane, q4):
+// the four values 4 q4 .. 4 q4 + 3 of a lane's accumulator, i.e. four
+// consecutive head dims of one key, as the whole-block path stores them.
+template <int D>
+__global__ void __launch_bounds__(NTHREADS) attn_bwd_dkv_combine_kernel(BwdArgs a) {
+  constexpr int DT = D / 32, PART = 2 * DT * 16 * 64;
+  const int64_t t = (int64_t)blockIdx.x * NTHREADS + threadIdx.x;
+  if (t >= (int64_t)a.b * a.kv * a.split * 2 * DT * 256) return;
+  const int q4 = (int)(t & 3), lane = (int)((t >> 2) & 63);
+  const int u = (int)((t >> 8) % (2 * DT));
+  const int blk = (int)((t >> 8) / (2 * DT));  // bg * split + kb
+  const int bg = blk / a.split, kb = blk % a.split;
+  const int beta = bg / a.kv, g = bg % a.kv;
+  const int key = kb * KEY_BLOCK + (lane & 31), h = lane >> 5;
+  if (key >= a.s) return;
+  const float* p0 = a.dkv_part + (int64_t)blk * 2 * PART + u * 16 * 64 + lane;
+  const float* p1 = p0 + PART;
+  const bool is_k = u < DT;
+  const int dt = is_k ? u : u - DT;
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = (4 * q4 + e) * 64;
+    const float x = p0[r] + p1[r];
+    v[e] = is_k ? x * a.scale : x;
+  }
+  uint16_t* dst = a.dqkv + ((int64_t)beta * a.s + key) * a.ld_qkv + (int64_t)(is_k ? a.q + g : a.q + a.kv + g) * D +
+                  32 * dt + 8 * q4 + 4 * h;
+  Elem<uint16_t>::store4(dst, v);
 }
 
 // ---- dQ ----------------------------------------------------------------------
@@ -420,12 +490,31 @@ hipError_t launch_attn_bwd_stats(const attnb::BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Key blocks worth splitting (see BwdArgs::split): the heavier half of them
+// for a causal mask, none otherwise (every block then sees every query).
+inline int attn_bwd_dkv_split(int s, int causal) {
+  const int nkb = (s + attnb::KEY_BLOCK - 1) / attnb::KEY_BLOCK;
+  return causal ? nkb / 2 : 0;
+}
+// Floats of dkv_part for `split` split key blocks.
+inline int64_t attn_bwd_dkv_part_floats(int b, int kv, int split, int d) {
+  return (int64_t)b * kv * split * 2 * (2 * (d / 32) * 16 * 64);
+}
+
+// dK/dV (a.split and a.dkv_part set by the caller; split <= nkb / 2), then
+// the kernel that finishes the split blocks.
 template <int D>
 hipError_t launch_attn_bwd_dkv(const attnb::BwdArgs& a, hipStream_t stream) {
   const int nkb = (a.s + attnb::KEY_BLOCK - 1) / attnb::KEY_BLOCK;
-  if (nkb == 0 || a.b * a.kv == 0) return hipSuccess;
-  hipLaunchKernelGGL((attnb::attn_bwd_dkv_kernel<D>), dim3(nkb, a.b * a.kv), dim3(64 * attnb::DKV_WAVES), 0, stream,
-                     a);
+  const int BG = a.b * a.kv;
+  if (nkb == 0 || BG == 0) return hipSuccess;
+  hipLaunchKernelGGL((attnb::attn_bwd_dkv_kernel<D>), dim3(BG * (nkb + a.split)), dim3(64 * attnb::DKV_WAVES), 0,
+                     stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.split == 0) return e;
+  const int64_t n = (int64_t)BG * a.split * 2 * (D / 32) * 256;
+  hipLaunchKernelGGL((attnb::attn_bwd_dkv_combine_kernel<D>), dim3((unsigned)((n + attnb::NTHREADS - 1) / attnb::NTHREADS)),
+                     dim3(attnb::NTHREADS), 0, stream, a);
   return hipGetLastError();
 }
 

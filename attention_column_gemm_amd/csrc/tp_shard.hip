@@ -83,8 +83,9 @@ GemmProblem problem(int M, int N, int K, const void* A, int64_t lda, const void*
 // chip clocks higher), with 128 or fewer the small tile wins.
 // TPSHARD_TILE=large|small overrides the choice (used by the tests to cover
 // both tile shapes at small sizes).
-// TPSHARD_SPLIT_TAIL=0 turns the split of a GEMM's last round off (the
-// tests compare both ways).
+// TPSHARD_SPLIT_TAIL=0 turns off the split of a GEMM's last round and the
+// split of the attention backward's heaviest key blocks (the tests compare
+// both ways).
 bool split_tail_enabled() {
   const char* v = std::getenv("TPSHARD_SPLIT_TAIL");
   return !(v && !std::strcmp(v, "0"));
@@ -578,6 +579,11 @@ int tp_attn_shard_bwd(const tp_attn_desc* d, const void* dZ, const void* X, cons
   a.causal = d->causal ? 1 : 0;
   a.scale = (float)(1.0 / std::sqrt((double)D));
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  // dK/dV's heaviest key blocks run as two halves whose fp32 sums go to
+  // dWqkv_i's memory, written only by the last GEMM below
+  a.split = split_tail_enabled() ? attn_bwd_dkv_split(a.s, a.causal) : 0;
+  if (attn_bwd_dkv_part_floats(a.b, a.kv, a.split, D) * 4 > d->h * nqkv64 * 4) a.split = 0;
+  a.dkv_part = dWqkv_i;
   const int hg = heads_per_wg(q / kv);
   hipError_t e;
   {

@@ -196,3 +196,27 @@ def test_attention_backward_cfg5_rank0():
     sh, X, w, dZ = _run_bwd(c, 0)
     torch.cuda.synchronize()
     _check_bwd("r0", c, sh, X, w, dZ, True)
+
+
+@pytest.mark.parametrize("name", ["gqa4_d128_ragged", "gqa8_d64_causal"])
+def test_attention_backward_key_block_split(name, monkeypatch):
+    """The causal dK/dV kernel runs its heavier half of key blocks as two
+    work-groups each (fp32 halves in dWqkv_i's memory, added by a second
+    kernel).  Against the oracle with the split on and off; the two runs
+    differ in rounding (proof that the split ran) and dWqkv_i, written over
+    the halves afterwards, is right in both."""
+    torch = need_gpu()
+    c, causal = SMALL[name]
+    got = {}
+    for split in ("1", "0"):
+        monkeypatch.setenv("TPSHARD_SPLIT_TAIL", split)
+        banner(f"attn bwd key split={split} {name}")
+        sh, X, w, dZ = _run_bwd(c, 0, causal)
+        torch.cuda.synchronize()
+        _check_bwd(f"split{split}", c, sh, X, w, dZ, causal)
+        got[split] = sh.dQKV.clone()
+        del sh
+    q, kv, d = c.q, c.kv, c.d
+    kvcols = slice(q * d, (q + 2 * kv) * d)
+    assert not torch.equal(got["1"][:, kvcols], got["0"][:, kvcols]), "the key-block split did not run"
+    assert torch.equal(got["1"][:, :q * d], got["0"][:, :q * d]), "dQ must not depend on the dK/dV split"
