@@ -235,7 +235,10 @@ int tp_attn_shard_fwd(const tp_attn_desc* desc, const void* X, const void* Wqkv_
  *   dO_i    [T, q d]           out, bf16: gradient of O_i
  *   stats_i [b, q, s, 2] fp32  scratch: per row {lse * log2(e), rowsum(dO * O)}
  *   dQKV_i  [T, (q+2kv) d]     out, bf16
- *   dWqkv_i [h, (q+2kv) d] fp32 out
+ *   dWqkv_i [h, (q+2kv) d] fp32 out.  Its memory is also scratch for the
+ *                          dK/dV kernel (fp32 halves of the split causal key
+ *                          blocks) before the last GEMM writes it, so it
+ *                          must not overlap any other argument.
  *   dWo_i   [q d, h] fp32      out
  *   dX_i    [T, h]             out, bf16 partial input gradient
  * Same descriptor and conditions as tp_attn_shard_fwd.  The result does not
