@@ -18,7 +18,10 @@
 //    tile) item of the causal range, last query tile first, each wave
 //    streaming its own Q and dO tiles into LDS with LDS-direct loads, and
 //    the eight waves' partial sums are added in a fixed order through LDS at
-//    the end (deterministic, no atomics).
+//    the end (deterministic, no atomics).  The heavier half of the causal
+//    key blocks (the first ones, which see the most queries) are split over
+//    two work-groups, each taking half of the items; a small kernel adds the
+//    two halves in a fixed order.
 //  * dQ: the forward's layout (waves own 32 query rows; the work-group shares
 //    64-key K and V blocks in LDS).
 // Operand layouts: with v_mfma_f32_32x32x16_bf16 computing C[i][j] += sum_k
@@ -130,7 +133,6 @@ __global__ void __launch_bounds__(64 * DKV_WAVES, 1) attn_bwd_dkv_kernel(BwdArgs
   // Job J of the 1-D grid, heaviest first: for i < split, three jobs per
   // (sequence, KV head): both halves of key block i, then whole block
   // split + i; the remaining whole blocks 2 split .. nkb-1 follow in order.
-  const int nkb = (a.s + KEY_BLOCK - 1) / KEY_BLOCK;
   const int BG = a.b * a.kv, J = blockIdx.x;
   int kb, bg, part;  // part: -1 whole, else the half
   if (J < 3 * BG * a.split) {
@@ -144,7 +146,6 @@ __global__ void __launch_bounds__(64 * DKV_WAVES, 1) attn_bwd_dkv_kernel(BwdArgs
     const int r = J - 3 * BG * a.split;
     kb = 2 * a.split + r / BG; part = -1; bg = r % BG;
   }
-  (void)nkb;
   const int k0 = kb * KEY_BLOCK;
   const int beta = bg / a.kv, g = bg % a.kv;
   const int group = a.q / a.kv;

@@ -35,6 +35,11 @@
 //    lane's accumulators are four consecutive output columns (8- or 16-byte
 //    stores).  Accumulators stay in arch VGPRs (the AGPR form measured slower).
 //  * The blockIdx -> tile map is the XCD-aware grouped map of gemm_common.hpp.
+//  * Launch shapes around the tile body: one problem per launch; two
+//    independent problems in one launch (gemm_dma_pair_kernel), so each
+//    fills the CUs the other's last round leaves idle; and a split tail
+//    (SplitTail), where the tiles of a last round at most half full each run
+//    as two K halves whose fp32 partials a second kernel adds.
 #pragma once
 
 #include <type_traits>
