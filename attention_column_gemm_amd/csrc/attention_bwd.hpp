@@ -75,7 +75,33 @@ struct BwdArgs {
   // ([b kv split][2][2 D/32][16][64]) and attn_bwd_dkv_combine_kernel adds them.
   float* dkv_part;
   int split;
+  // dQ load balance: the heavier dq_split query blocks of every (sequence,
+  // head group) are each taken by two work-groups over the two halves of
+  // their key blocks; the halves' fp32 sums go to dq_part
+  // ([dq_split ny][2][4 waves][D/32 * 16][64]) and attn_bwd_dq_combine_kernel
+  // adds them.
+  float* dq_part;
+  int dq_split;
 };
+
+// Job j of the dQ launch (npb query blocks x ny head groups, dq_split of the
+// blocks split), heaviest first: for i < dq_split, both halves of block
+// npb-1-i for every head group, then whole block npb-1-dq_split-i; the
+// remaining whole blocks follow in decreasing order.  part: -1 whole, else
+// the half; slot: index of a split block (i ny + y).
+__device__ __forceinline__ void dq_job(int J, int npb, int ny, int S, int& pb, int& y, int& part, int& slot) {
+  if (J < 3 * ny * S) {
+    const int i = J / (3 * ny), r = J % (3 * ny);
+    if (r < 2 * ny) {
+      pb = npb - 1 - i; part = r / ny; y = r % ny; slot = i * ny + y;
+    } else {
+      pb = npb - 1 - S - i; part = -1; y = r - 2 * ny; slot = -1;
+    }
+  } else {
+    const int r = J - 3 * ny * S;
+    pb = npb - 1 - 2 * S - r / ny; part = -1; y = r % ny; slot = -1;
+  }
+}
 
 // ---- stats -------------------------------------------------------------------
 // Row r = (beta q + j) s + i: stats[2r] = lse * log2(e), stats[2r+1] = Delta.
@@ -368,8 +394,12 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_kernel(BwdArgs a, int
   const int npb = (a.s + rows_per_wg - 1) / rows_per_wg;
   const int group = a.q / a.kv;
   const int sub_per_kv = group / hg;
-  int pb, y;
-  attnt::causal_block_order(npb, a.b * a.kv * sub_per_kv, pb, y);
+  const int ny = a.b * a.kv * sub_per_kv;
+  int pb, y, part = -1, slot = -1;
+  if (a.dq_split > 0)
+    dq_job((int)blockIdx.x, npb, ny, a.dq_split, pb, y, part, slot);
+  else
+    attnt::causal_block_order(npb, ny, pb, y);
   const int beta = y / (a.kv * sub_per_kv);
   const int rem = y % (a.kv * sub_per_kv);
   const int g = rem / sub_per_kv;
@@ -408,13 +438,16 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_kernel(BwdArgs a, int
     for (int e = 0; e < 16; ++e) dq[t][e] = 0.0f;
 
   const int kv_end = a.causal ? min(a.s, pos0 + rows_per_wg) : a.s;
-  const int nkb = (kv_end + DQ_KEYS - 1) / DQ_KEYS;
+  const int nkb_all = (kv_end + DQ_KEYS - 1) / DQ_KEYS;
+  // a half takes key blocks [kb0, kb0 + nkb)
+  const int kb0 = part == 1 ? nkb_all / 2 : 0;
+  const int nkb = part < 0 ? nkb_all : (part == 0 ? nkb_all / 2 : nkb_all - nkb_all / 2);
   const u32x4 rkv = lds::sgpr_rsrc(a.qkv + tok0 * a.ld_qkv, (uint32_t)a.s * ldq);
   const uint32_t kcol = (uint32_t)(a.q + g) * D * 2u, vcol = (uint32_t)(a.q + a.kv + g) * D * 2u;
   auto issue = [&](int kb, int st) {
     const uint32_t dst = lds_base + (uint32_t)st * STAGE;
-    dma_tile<D, DQ_KEYS>(rkv, ldq, kb * DQ_KEYS, a.s, kcol, dst, wave, 4);
-    dma_tile<D, DQ_KEYS>(rkv, ldq, kb * DQ_KEYS, a.s, vcol, dst + TILE, wave, 4);
+    dma_tile<D, DQ_KEYS>(rkv, ldq, (kb0 + kb) * DQ_KEYS, a.s, kcol, dst, wave, 4);
+    dma_tile<D, DQ_KEYS>(rkv, ldq, (kb0 + kb) * DQ_KEYS, a.s, vcol, dst + TILE, wave, 4);
   };
   if (nkb > 0) issue(0, 0);
   for (int kb = 0; kb < nkb; ++kb) {
@@ -423,7 +456,7 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_kernel(BwdArgs a, int
     lds::wait_lgkm0();
     lds::barrier();  // block kb is in LDS for every wave; every wave is done with block kb-1
     if (kb + 1 < nkb) issue(kb + 1, st ^ 1);
-    const int key0 = kb * DQ_KEYS;
+    const int key0 = (kb0 + kb) * DQ_KEYS;
     if (a.causal && key0 > rp0 + 31) continue;
     const lds_u8* tk = lds + st * STAGE;
     const lds_u8* tv = tk + TILE;
@@ -466,6 +499,14 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_kernel(BwdArgs a, int
     }
   }
 
+  if (part >= 0) {  // a half: fp32 sums, unscaled, in [dt * 16 + e][lane] order
+    float* dst = a.dq_part + ((int64_t)(slot * 2 + part) * 4 + wave) * (DT * 16 * 64);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dst[(dt * 16 + e) * 64 + lane] = dq[dt][e];
+    return;
+  }
   if (my_row < a.s) {
     uint16_t* dst = a.dqkv + (tok0 + my_row) * a.ld_qkv + (int64_t)j * D;
 #pragma unroll
@@ -476,6 +517,39 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_kernel(BwdArgs a, int
                              dq[dt][4 * q4 + 3] * a.scale};
         Elem<uint16_t>::store4(dst + 32 * dt + 8 * q4 + 4 * h, w4);
       }
+  }
+}
+
+// dQ of the split query blocks: the two halves added in a fixed order (first
+// + second), scaled and stored as bf16, with the row and head mapping of
+// attn_bwd_dq_kernel.  One thread per (slot, wave, lane, dt).
+template <int D>
+__global__ void __launch_bounds__(NTHREADS) attn_bwd_dq_combine_kernel(BwdArgs a, int hg) {
+  constexpr int DT = D / 32, PART = 4 * DT * 16 * 64;
+  const int rows_per_wg = 32 * (4 / hg);
+  const int npb = (a.s + rows_per_wg - 1) / rows_per_wg;
+  const int group = a.q / a.kv, sub_per_kv = group / hg;
+  const int ny = a.b * a.kv * sub_per_kv;
+  const int64_t t = (int64_t)blockIdx.x * NTHREADS + threadIdx.x;
+  if (t >= (int64_t)a.dq_split * ny * 4 * 64 * DT) return;
+  const int dt = (int)(t % DT), lane = (int)((t / DT) & 63), wave = (int)((t / (DT * 64)) & 3);
+  const int slot = (int)(t / (DT * 64 * 4));
+  const int i = slot / ny, y = slot % ny;
+  const int pb = npb - 1 - i;
+  const int beta = y / (a.kv * sub_per_kv), rem = y % (a.kv * sub_per_kv);
+  const int g = rem / sub_per_kv;
+  const int j = g * group + (rem % sub_per_kv) * hg + (wave % hg);
+  const int my_row = pb * rows_per_wg + (wave / hg) * 32 + (lane & 31), h = lane >> 5;
+  if (my_row >= a.s) return;
+  const float* p0 = a.dq_part + ((int64_t)(slot * 2) * 4 + wave) * (DT * 16 * 64) + dt * 16 * 64 + lane;
+  const float* p1 = p0 + PART;
+  uint16_t* dst = a.dqkv + ((int64_t)beta * a.s + my_row) * a.ld_qkv + (int64_t)j * D + 32 * dt + 4 * h;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (p0[(4 * q4 + e) * 64] + p1[(4 * q4 + e) * 64]) * a.scale;
+    Elem<uint16_t>::store4(dst + 8 * q4, v);
   }
 }
 
@@ -519,13 +593,40 @@ hipError_t launch_attn_bwd_dkv(const attnb::BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Query blocks of the dQ launch worth splitting (BwdArgs::dq_split): the
+// heavier half for a causal mask when the unsplit launch leaves some of the
+// 512 work-group slots (two per CU) empty, none otherwise (with every slot
+// taken, the heavy-light pairing of causal_block_order measured faster than
+// the split); and the floats of dq_part.
+inline int attn_bwd_dq_split(int s, int causal, int b, int q, int kv, int hg) {
+  const int rows_per_wg = 32 * (4 / hg);
+  const int npb = (s + rows_per_wg - 1) / rows_per_wg;
+  const int64_t wgs = (int64_t)npb * b * kv * ((q / kv) / hg);
+  return causal && wgs < 512 ? npb / 2 : 0;
+}
+inline int64_t attn_bwd_dq_part_floats(int b, int q, int kv, int hg, int dq_split, int d) {
+  return (int64_t)dq_split * b * kv * ((q / kv) / hg) * 2 * 4 * (d / 32) * 16 * 64;
+}
+
+// dQ (a.dq_split and a.dq_part set by the caller; dq_split <= npb / 2), then
+// the kernel that finishes the split blocks.
 template <int D>
 hipError_t launch_attn_bwd_dq(const attnb::BwdArgs& a, int hg, hipStream_t stream) {
   const int rows_per_wg = 32 * (4 / hg);
   const int npb = (a.s + rows_per_wg - 1) / rows_per_wg;
   const int ny = a.b * a.kv * ((a.q / a.kv) / hg);
   if (npb == 0 || ny == 0) return hipSuccess;
-  hipLaunchKernelGGL((attnb::attn_bwd_dq_kernel<D>), dim3(npb, ny), dim3(attnb::NTHREADS), 0, stream, a, hg);
+  if (a.dq_split == 0) {
+    hipLaunchKernelGGL((attnb::attn_bwd_dq_kernel<D>), dim3(npb, ny), dim3(attnb::NTHREADS), 0, stream, a, hg);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((attnb::attn_bwd_dq_kernel<D>), dim3((npb + a.dq_split) * ny), dim3(attnb::NTHREADS), 0, stream,
+                     a, hg);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)a.dq_split * ny * 4 * 64 * (D / 32);
+  hipLaunchKernelGGL((attnb::attn_bwd_dq_combine_kernel<D>), dim3((unsigned)((n + attnb::NTHREADS - 1) / attnb::NTHREADS)),
+                     dim3(attnb::NTHREADS), 0, stream, a, hg);
   return hipGetLastError();
 }
 

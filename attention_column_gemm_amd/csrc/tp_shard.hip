@@ -585,6 +585,11 @@ int tp_attn_shard_bwd(const tp_attn_desc* d, const void* dZ, const void* X, cons
   if (attn_bwd_dkv_part_floats(a.b, a.kv, a.split, D) * 4 > d->h * nqkv64 * 4) a.split = 0;
   a.dkv_part = dWqkv_i;
   const int hg = heads_per_wg(q / kv);
+  // dQ's heaviest query blocks likewise, their halves' sums in dX_i's memory
+  // (written only by the last GEMM below)
+  a.dq_split = split_tail_enabled() ? attn_bwd_dq_split(a.s, a.causal, a.b, a.q, a.kv, hg) : 0;
+  if (attn_bwd_dq_part_floats(a.b, a.q, a.kv, hg, a.dq_split, D) * 4 > T64 * d->h * 2) a.dq_split = 0;
+  a.dq_part = static_cast<float*>(dX_i);
   hipError_t e;
   {
     Probe pr(st);

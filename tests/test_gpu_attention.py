@@ -198,15 +198,25 @@ def test_attention_backward_cfg5_rank0():
     _check_bwd("r0", c, sh, X, w, dZ, True)
 
 
-@pytest.mark.parametrize("name", ["gqa4_d128_ragged", "gqa8_d64_causal"])
+SPLIT_BWD = {
+    # (config, causal, dQ split expected): dX_i's memory holds dQ's partials only in the last case
+    "gqa4_d128_ragged": (SMALL["gqa4_d128_ragged"][0], True, False),
+    "gqa8_d64_causal": (SMALL["gqa8_d64_causal"][0], True, False),
+    "mqa4_d128_h2048": (I.custom_attn(207, 1, 256, 2048, 4, 1, 128, 1), True, True),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT_BWD))
 def test_attention_backward_key_block_split(name, monkeypatch):
     """The causal dK/dV kernel runs its heavier half of key blocks as two
-    work-groups each (fp32 halves in dWqkv_i's memory, added by a second
-    kernel).  Against the oracle with the split on and off; the two runs
-    differ in rounding (proof that the split ran) and dWqkv_i, written over
-    the halves afterwards, is right in both."""
+    work-groups each (fp32 halves in dWqkv_i's memory), and dQ its heavier
+    half of query blocks as two work-groups over the halves of their keys
+    (fp32 halves in dX_i's memory, when it holds them); second kernels add
+    the halves.  Against the oracle with the splits on and off; the runs
+    differ in rounding where a split ran (proof that it ran), and dWqkv_i
+    and dX_i, written over the halves afterwards, are right in both."""
     torch = need_gpu()
-    c, causal = SMALL[name]
+    c, causal, dq_split = SPLIT_BWD[name]
     got = {}
     for split in ("1", "0"):
         monkeypatch.setenv("TPSHARD_SPLIT_TAIL", split)
@@ -219,4 +229,5 @@ def test_attention_backward_key_block_split(name, monkeypatch):
     q, kv, d = c.q, c.kv, c.d
     kvcols = slice(q * d, (q + 2 * kv) * d)
     assert not torch.equal(got["1"][:, kvcols], got["0"][:, kvcols]), "the key-block split did not run"
-    assert torch.equal(got["1"][:, :q * d], got["0"][:, :q * d]), "dQ must not depend on the dK/dV split"
+    same_q = torch.equal(got["1"][:, :q * d], got["0"][:, :q * d])
+    assert same_q != dq_split, "the dQ split ran where it should not, or did not run where it should"
