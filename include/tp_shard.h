@@ -240,7 +240,11 @@ int tp_attn_shard_fwd(const tp_attn_desc* desc, const void* X, const void* Wqkv_
  *                          blocks) before the last GEMM writes it, so it
  *                          must not overlap any other argument.
  *   dWo_i   [q d, h] fp32      out
- *   dX_i    [T, h]             out, bf16 partial input gradient
+ *   dX_i    [T, h]             out, bf16 partial input gradient.  Its memory is
+ *                              also scratch for the dQ kernel (fp32 halves of
+ *                              split causal query blocks) before the last GEMM
+ *                              writes it, so it must not overlap any other
+ *                              argument.
  * Same descriptor and conditions as tp_attn_shard_fwd.  The result does not
  * depend on the order in which work-groups run (no atomics).
  */
