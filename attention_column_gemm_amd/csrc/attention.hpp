@@ -55,7 +55,33 @@ struct AttnArgs {
   int b, s, q, kv, hg;   // hg: query heads per work-group
   int causal;
   float scale_log2;      // log2(e) / sqrt(d)
+  // Load balance when the launch leaves work-group slots empty: the heavier
+  // `split` query blocks of every head group are each taken by two
+  // work-groups over the two halves of their key blocks; each half leaves
+  // its unnormalized output, running maximum and row sums in `part`
+  // ([split ny][2][4 waves][D/32 * 16 + 2][64]) and attn_fwd_merge_kernel
+  // combines them.
+  float* part;
+  int split;
 };
+
+// Job J of a split launch (npb query blocks x ny head groups, S of the blocks
+// split), heaviest first: for i < S, both halves of block npb-1-i for every
+// head group, then whole block npb-1-S-i; the remaining whole blocks follow
+// in decreasing order.  part: -1 whole, else the half; slot: i ny + y.
+__device__ __forceinline__ void split_job(int J, int npb, int ny, int S, int& pb, int& y, int& part, int& slot) {
+  if (J < 3 * ny * S) {
+    const int i = J / (3 * ny), r = J % (3 * ny);
+    if (r < 2 * ny) {
+      pb = npb - 1 - i; part = r / ny; y = r % ny; slot = i * ny + y;
+    } else {
+      pb = npb - 1 - S - i; part = -1; y = r - 2 * ny; slot = -1;
+    }
+  } else {
+    const int r = J - 3 * ny * S;
+    pb = npb - 1 - 2 * S - r / ny; part = -1; y = r % ny; slot = -1;
+  }
+}
 
 template <int D>
 __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(AttnArgs a) {
@@ -73,8 +99,12 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(AttnArgs a) {
   const int npb = (a.s + rows_per_wg - 1) / rows_per_wg;
   const int group = a.q / a.kv;
   const int sub_per_kv = group / a.hg;
-  int pb, y;
-  attnt::causal_block_order(npb, a.b * a.kv * sub_per_kv, pb, y);
+  const int ny = a.b * a.kv * sub_per_kv;
+  int pb, y, part = -1, slot = -1;
+  if (a.split > 0)
+    split_job((int)blockIdx.x, npb, ny, a.split, pb, y, part, slot);
+  else
+    attnt::causal_block_order(npb, ny, pb, y);
   const int beta = y / (a.kv * sub_per_kv);
   const int rem = y % (a.kv * sub_per_kv);
   const int g = rem / sub_per_kv;
@@ -98,13 +128,16 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): keep these out of the block pipeline's counts
 
   const int kv_end = a.causal ? min(a.s, pos0 + rows_per_wg) : a.s;
-  const int nkb = (kv_end + BKV - 1) / BKV;
+  const int nkb_all = (kv_end + BKV - 1) / BKV;
+  // a half takes key blocks [kb0, kb0 + nkb)
+  const int kb0 = part == 1 ? nkb_all / 2 : 0;
+  const int nkb = part < 0 ? nkb_all : (part == 0 ? nkb_all / 2 : nkb_all - nkb_all / 2);
   const u32x4 rkv = lds::sgpr_rsrc(a.qkv + tok0 * a.ld_qkv, (uint32_t)a.s * ldb);
   const uint32_t kcol = (uint32_t)(a.q + g) * D * 2u, vcol = (uint32_t)(a.q + a.kv + g) * D * 2u;
   auto issue = [&](int kb, int st) {
     const uint32_t dst = lds_base + (uint32_t)st * STAGE;
-    attnt::dma_tile<D, BKV>(rkv, ldb, kb * BKV, a.s, kcol, dst, wave, 4);
-    attnt::dma_tile<D, BKV>(rkv, ldb, kb * BKV, a.s, vcol, dst + TILE, wave, 4);
+    attnt::dma_tile<D, BKV>(rkv, ldb, (kb0 + kb) * BKV, a.s, kcol, dst, wave, 4);
+    attnt::dma_tile<D, BKV>(rkv, ldb, (kb0 + kb) * BKV, a.s, vcol, dst + TILE, wave, 4);
   };
 
   f32x16 oacc[DT];
@@ -121,7 +154,7 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(AttnArgs a) {
     lds::wait_lgkm0();
     lds::barrier();  // block kb is in LDS for every wave; every wave is done with block kb-1
     if (kb + 1 < nkb) issue(kb + 1, st ^ 1);
-    const int key0 = kb * BKV;
+    const int key0 = (kb0 + kb) * BKV;
     if (a.causal && key0 > rp0 + 31) continue;
     const lds::lds_u8* tk = lds + st * STAGE;
     const lds::lds_u8* tv = tk + TILE;
@@ -194,6 +227,16 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(AttnArgs a) {
                                                             oacc[t], 0, 0, 0);
   }
 
+  if (part >= 0) {  // a half: unnormalized output, running maximum and row sum, [i][lane] order
+    float* dst = a.part + ((int64_t)(slot * 2 + part) * 4 + wave) * ((DT * 16 + 2) * 64) + lane;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dst[(t * 16 + e) * 64] = oacc[t][e];
+    dst[(DT * 16) * 64] = m_run;
+    dst[(DT * 16 + 1) * 64] = l_run;
+    return;
+  }
   // finalize
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (my_row < a.s) {
@@ -212,7 +255,69 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(AttnArgs a) {
   }
 }
 
+// Merge of the two halves of every split query block, one thread per (slot,
+// wave, lane): both halves rescaled to the common maximum (exp2, the scores
+// being in log2 units) and added in a fixed order (first + second), then
+// normalized and stored with the row and head mapping of attn_fwd_kernel.
+template <int D>
+__global__ void __launch_bounds__(NTHREADS) attn_fwd_merge_kernel(AttnArgs a) {
+  constexpr int DT = D / 32, W = (DT * 16 + 2) * 64;
+  const int rows_per_wg = 32 * (4 / a.hg);
+  const int npb = (a.s + rows_per_wg - 1) / rows_per_wg;
+  const int group = a.q / a.kv, sub_per_kv = group / a.hg;
+  const int ny = a.b * a.kv * sub_per_kv;
+  const int64_t t = (int64_t)blockIdx.x * NTHREADS + threadIdx.x;
+  if (t >= (int64_t)a.split * ny * 4 * 64) return;
+  const int lane = (int)(t & 63), wave = (int)((t >> 6) & 3), slot = (int)(t >> 8);
+  const int i = slot / ny, y = slot % ny;
+  const int pb = npb - 1 - i;
+  const int beta = y / (a.kv * sub_per_kv), rem = y % (a.kv * sub_per_kv);
+  const int g = rem / sub_per_kv;
+  const int j = g * group + (rem % sub_per_kv) * a.hg + (wave % a.hg);
+  const int my_row = pb * rows_per_wg + (wave / a.hg) * 32 + (lane & 31), hgrp = lane >> 5;
+  if (my_row >= a.s) return;
+  const float* h0 = a.part + ((int64_t)(slot * 2) * 4 + wave) * W;
+  const float* h1 = h0 + 4 * W;
+  const float m0 = h0[DT * 16 * 64 + lane], m1 = h1[DT * 16 * 64 + lane];
+  const float l0 = h0[(DT * 16 + 1) * 64 + lane] + h0[(DT * 16 + 1) * 64 + (lane ^ 32)];
+  const float l1 = h1[(DT * 16 + 1) * 64 + lane] + h1[(DT * 16 + 1) * 64 + (lane ^ 32)];
+  const float m = fmaxf(m0, m1);
+  const float c0 = m0 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m0 - m);
+  const float c1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+  const float l = l0 * c0 + l1 * c1;
+  const float inv = 1.0f / l;
+  uint16_t* orow = a.o + ((int64_t)beta * a.s + my_row) * a.ld_o + (int64_t)j * D;
+#pragma unroll
+  for (int tt = 0; tt < DT; ++tt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = (tt * 16 + 4 * q4 + e) * 64 + lane;
+        v[e] = (h0[r] * c0 + h1[r] * c1) * inv;
+      }
+      Elem<uint16_t>::store4(orow + tt * 32 + 8 * q4 + 4 * hgrp, v);
+    }
+  if (a.lse && hgrp == 0)
+    a.lse[((int64_t)beta * a.q + j) * a.s + my_row] = (m + __log2f(l)) * 0.69314718055994531f;
+}
+
 }  // namespace attn
+
+// Query blocks of the forward launch worth splitting (AttnArgs::split): the
+// heavier half for a causal mask when the unsplit launch leaves some of its
+// 512 work-group slots (two per CU) empty, none otherwise; and the floats of
+// AttnArgs::part.
+inline int attn_fwd_split(int s, int causal, int b, int q, int kv, int hg) {
+  const int rows_per_wg = 32 * (4 / hg);
+  const int npb = (s + rows_per_wg - 1) / rows_per_wg;
+  const int64_t wgs = (int64_t)npb * b * kv * ((q / kv) / hg);
+  return causal && wgs < 512 ? npb / 2 : 0;
+}
+inline int64_t attn_fwd_part_floats(int b, int q, int kv, int hg, int split, int d) {
+  return (int64_t)split * b * kv * ((q / kv) / hg) * 2 * 4 * ((d / 32) * 16 + 2) * 64;
+}
 
 template <int D>
 hipError_t launch_attn_fwd(const attn::AttnArgs& a, hipStream_t stream) {
@@ -220,7 +325,16 @@ hipError_t launch_attn_fwd(const attn::AttnArgs& a, hipStream_t stream) {
   const int npb = (a.s + rows_per_wg - 1) / rows_per_wg;
   const int ny = a.b * a.kv * ((a.q / a.kv) / a.hg);
   if (npb == 0 || ny == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn::attn_fwd_kernel<D>), dim3(npb, ny), dim3(attn::NTHREADS), 0, stream, a);
+  if (a.split == 0) {
+    hipLaunchKernelGGL((attn::attn_fwd_kernel<D>), dim3(npb, ny), dim3(attn::NTHREADS), 0, stream, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((attn::attn_fwd_kernel<D>), dim3((npb + a.split) * ny), dim3(attn::NTHREADS), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)a.split * ny * 4 * 64;
+  hipLaunchKernelGGL((attn::attn_fwd_merge_kernel<D>), dim3((unsigned)((n + attn::NTHREADS - 1) / attn::NTHREADS)),
+                     dim3(attn::NTHREADS), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -84,8 +84,8 @@ GemmProblem problem(int M, int N, int K, const void* A, int64_t lda, const void*
 // TPSHARD_TILE=large|small overrides the choice (used by the tests to cover
 // both tile shapes at small sizes).
 // TPSHARD_SPLIT_TAIL=0 turns off the split of a GEMM's last round and the
-// split of the attention backward's heaviest key blocks (the tests compare
-// both ways).
+// splits of the attention kernels' heaviest key and query blocks (the tests
+// compare both ways).
 bool split_tail_enabled() {
   const char* v = std::getenv("TPSHARD_SPLIT_TAIL");
   return !(v && !std::strcmp(v, "0"));
@@ -520,6 +520,12 @@ int tp_attn_shard_fwd(const tp_attn_desc* d, const void* X, const void* Wqkv_i, 
   a.hg = heads_per_wg(q / kv);
   a.causal = d->causal ? 1 : 0;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  // the heaviest query blocks of a launch that leaves slots empty run as two
+  // halves whose softmax state goes to Z_i's memory (written only by the
+  // output projection below)
+  a.split = split_tail_enabled() ? attn_fwd_split(a.s, a.causal, a.b, a.q, a.kv, a.hg) : 0;
+  if (attn_fwd_part_floats(a.b, a.q, a.kv, a.hg, a.split, D) * 4 > (int64_t)T_ * h * 2) a.split = 0;
+  a.part = static_cast<float*>(Z_i);
   hipError_t e;
   {
     Probe pr(st);

@@ -207,7 +207,11 @@ int tp_mlp_shard_bwd(const tp_mlp_desc* desc, const void* dOut, float p_drop, ui
  *   QKV_i  [T, (q+2kv) d]      out, bf16 (also the attention's input)
  *   O_i    [T, q d]            out, bf16, heads concatenated head-major
  *   lse_i  [b, q, s] fp32      out, natural-log sum of exp of the scaled masked scores per row, or NULL
- *   Z_i    [T, h]              out, bf16 partial
+ *   Z_i    [T, h]              out, bf16 partial.  Its memory is also scratch
+ *                              for the attention kernel (softmax state of split
+ *                              causal query blocks) before the output
+ *                              projection writes it, so it must not overlap any
+ *                              other argument.
  * Head widths 64 and 128 are provided.
  */
 int tp_attn_shard_fwd(const tp_attn_desc* desc, const void* X, const void* Wqkv_i, const void* Wo_i,

@@ -231,3 +231,36 @@ def test_attention_backward_key_block_split(name, monkeypatch):
     assert not torch.equal(got["1"][:, kvcols], got["0"][:, kvcols]), "the key-block split did not run"
     same_q = torch.equal(got["1"][:, :q * d], got["0"][:, :q * d])
     assert same_q != dq_split, "the dQ split ran where it should not, or did not run where it should"
+
+
+@pytest.mark.parametrize("name", ["mqa4_d128_h2048", "gqa4_d128_ragged"])
+def test_attention_forward_query_block_split(name, monkeypatch):
+    """A causal forward whose launch leaves work-group slots empty runs its
+    heavier half of query blocks as two work-groups over the halves of the
+    keys (softmax state in Z_i's memory, merged by a second kernel).  O_i,
+    lse_i and Z_i against the oracle with the split on and off; O_i differs
+    in rounding where the split ran (proof that it ran: Z_i's memory holds
+    the halves only for h = 2048)."""
+    torch = need_gpu()
+    c, causal, expect = SPLIT_BWD[name]
+    ref = None
+    got = {}
+    for split in ("1", "0"):
+        monkeypatch.setenv("TPSHARD_SPLIT_TAIL", split)
+        banner(f"attn fwd query split={split} {name}")
+        sh, X, w = _run(c, 0, causal)
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = OA.shard_forward(X, w["Wqkv"], w["Wo"], b=c.b, s=c.s, q=c.q, kv=c.kv, d=c.d, causal=causal)
+        check(f"split{split}.O_i", _np(sh.O), ref["O"], BF)
+        check(f"split{split}.lse_i", _np(sh.lse), ref["lse"], BF)
+        check(f"split{split}.Z_i", _np(sh.Z), ref["Z"], BF)
+        q, kv, d = c.q, c.kv, c.d
+        QKV = _np(sh.QKV)
+        Oc, lc = OA.core(QKV[:, :q * d], QKV[:, q * d:(q + kv) * d], QKV[:, (q + kv) * d:], b=c.b, s=c.s,
+                         n_q=q, n_kv=kv, d=d, causal=causal)
+        check(f"split{split}.core(O_i)", _np(sh.O), Oc, 1e-2)
+        check(f"split{split}.core(lse_i)", _np(sh.lse), lc, 1e-3)
+        got[split] = sh.O.clone()
+        del sh
+    assert torch.equal(got["1"], got["0"]) != expect, "the query-block split ran where it should not, or did not run"
