@@ -97,16 +97,33 @@ int64_t tile_count(const GemmProblem& p, int bm, int bn) {
 bool use_small_tile(int64_t big) {
   if (const char* force = std::getenv("TPSHARD_TILE")) {
     if (!std::strcmp(force, "large")) return false;
-    if (!std::strcmp(force, "small")) return true;
+    if (!std::strcmp(force, "small") || !std::strcmp(force, "tiny")) return true;
   }
   return big < (int64_t)kNumCUs * 9 / 16;
+}
+// Among launches that take the small tile, those whose small tiles would
+// fill fewer than half of the 512 work-group slots (two per CU) take the
+// 64 x 64 tile of four 32 x 32 waves instead (single-B epilogues only): small
+// GEMMs with few tiles are bound by the latency of their K loop, and four
+// times the work-groups hide it.  TPSHARD_TILE=tiny forces it.
+bool use_tiny_tile(int64_t small) {
+  if (const char* force = std::getenv("TPSHARD_TILE")) {
+    if (!std::strcmp(force, "tiny")) return true;
+    if (!std::strcmp(force, "large") || !std::strcmp(force, "small")) return false;
+  }
+  return small < (int64_t)kNumCUs;
 }
 
 template <int AL, int BL, class Epi>
 hipError_t gemm_bf16(const GemmProblem& p, const Epi& epi, hipStream_t st) {
   constexpr int BN = Epi::NB == 1 ? 256 : 128;
   Probe pr(st);
-  if (use_small_tile(tile_count(p, 256, BN))) return launch_gemm_dma<128, BN / 2, 2, 2, 64, AL, BL>(p, epi, st);
+  if (use_small_tile(tile_count(p, 256, BN))) {
+    if constexpr (Epi::NB == 1) {
+      if (use_tiny_tile(tile_count(p, 128, 128))) return launch_gemm_dma<64, 64, 2, 2, 64, AL, BL>(p, epi, st);
+    }
+    return launch_gemm_dma<128, BN / 2, 2, 2, 64, AL, BL>(p, epi, st);
+  }
   return launch_gemm_dma<256, BN, 4, 2, 64, AL, BL>(p, epi, st);
 }
 
@@ -136,9 +153,15 @@ hipError_t gemm_bf16_pair(const GemmProblem& p1, const E1& e1, const GemmProblem
                           hipStream_t st) {
   constexpr int BN1 = E1::NB == 1 ? 256 : 128, BN2 = E2::NB == 1 ? 256 : 128;
   Probe pr(st);
-  if (use_small_tile(tile_count(p1, 256, BN1) + tile_count(p2, 256, BN2)))
+  if (use_small_tile(tile_count(p1, 256, BN1) + tile_count(p2, 256, BN2))) {
+    if constexpr (E1::NB == 1 && E2::NB == 1) {
+      if (use_tiny_tile(tile_count(p1, 128, 128) + tile_count(p2, 128, 128)))
+        return launch_gemm_dma_pair<gemm3::TileCfg<64, 64, 2, 2, 64, AL1, BL1>,
+                                    gemm3::TileCfg<64, 64, 2, 2, 64, AL2, BL2>>(p1, e1, p2, e2, st);
+    }
     return launch_gemm_dma_pair<gemm3::TileCfg<128, BN1 / 2, 2, 2, 64, AL1, BL1>,
                                 gemm3::TileCfg<128, BN2 / 2, 2, 2, 64, AL2, BL2>>(p1, e1, p2, e2, st);
+  }
   return launch_gemm_dma_pair<gemm3::TileCfg<256, BN1, 4, 2, 64, AL1, BL1>,
                               gemm3::TileCfg<256, BN2, 4, 2, 64, AL2, BL2>>(p1, e1, p2, e2, st);
 }

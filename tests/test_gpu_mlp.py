@@ -74,7 +74,7 @@ SMALL = {
 }
 
 
-@pytest.mark.parametrize("tile", ["auto", "large", "small"])
+@pytest.mark.parametrize("tile", ["auto", "large", "small", "tiny"])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_mlp_all_ranks_full_parity(name, tile, monkeypatch):
     torch = need_gpu()
