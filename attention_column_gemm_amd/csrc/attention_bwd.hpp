@@ -18,10 +18,11 @@
 //    tile) item of the causal range, last query tile first, each wave
 //    streaming its own Q and dO tiles into LDS with LDS-direct loads, and
 //    the eight waves' partial sums are added in a fixed order through LDS at
-//    the end (deterministic, no atomics).  The heavier half of the causal
-//    key blocks (the first ones, which see the most queries) are split over
-//    two work-groups, each taking half of the items; a small kernel adds the
-//    two halves in a fixed order.
+//    the end (deterministic, no atomics).  The causal key blocks but the
+//    lightest eighth (the first ones see the most queries) are split over
+//    two work-groups, each taking half of the items, and the jobs go out in
+//    decreasing order of work; a small kernel adds the two halves in a fixed
+//    order.
 //  * dQ: the forward's layout (waves own 32 query rows; the work-group shares
 //    64-key K and V blocks in LDS).
 // Operand layouts: with v_mfma_f32_32x32x16_bf16 computing C[i][j] += sum_k
@@ -156,21 +157,28 @@ __global__ void __launch_bounds__(64 * DKV_WAVES, 1) attn_bwd_dkv_kernel(BwdArgs
 
   const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Job J of the 1-D grid, heaviest first: for i < split, three jobs per
-  // (sequence, KV head): both halves of key block i, then whole block
-  // split + i; the remaining whole blocks 2 split .. nkb-1 follow in order.
+  // Job J of the 1-D grid, in decreasing order of work: the two halves of a
+  // split key block i < split (work (nkb - i) / 2 each) and the whole blocks
+  // split .. nkb-1 (work nkb - kb) merged by work, halves first on ties; each
+  // entry of that order covers every (sequence, KV head), b kv jobs.
+  const int nkb = (a.s + KEY_BLOCK - 1) / KEY_BLOCK;
   const int BG = a.b * a.kv, J = blockIdx.x;
-  int kb, bg, part;  // part: -1 whole, else the half
-  if (J < 3 * BG * a.split) {
-    const int i = J / (3 * BG), r = J % (3 * BG);
-    if (r < 2 * BG) {
-      kb = i; part = r / BG; bg = r % BG;
-    } else {
-      kb = a.split + i; part = -1; bg = r - 2 * BG;
+  const int u = J / BG, bg = J % BG;
+  int kb = 0, part = -1;  // part: -1 whole, else the half
+  {
+    int i = 0, w = a.split, pos = 0;  // next split block, next whole block, entries passed
+    for (int step = 0; step < nkb; ++step) {  // nkb = split + (nkb - split) entries at most
+      const bool take_split = i < a.split && (w >= nkb || (nkb - i) >= 2 * (nkb - w));
+      if (take_split) {
+        if (u < pos + 2) { kb = i; part = u - pos; break; }
+        pos += 2;
+        ++i;
+      } else {
+        if (u == pos) { kb = w; break; }
+        pos += 1;
+        ++w;
+      }
     }
-  } else {
-    const int r = J - 3 * BG * a.split;
-    kb = 2 * a.split + r / BG; part = -1; bg = r % BG;
   }
   const int k0 = kb * KEY_BLOCK;
   const int beta = bg / a.kv, g = bg % a.kv;
@@ -565,19 +573,21 @@ hipError_t launch_attn_bwd_stats(const attnb::BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Key blocks worth splitting (see BwdArgs::split): the heavier half of them
-// for a causal mask, none otherwise (every block then sees every query).
+// Key blocks worth splitting (see BwdArgs::split): all but the lightest
+// eighth for a causal mask (a model of the in-order dispatch of the jobs,
+// heaviest first, gives the shortest kernel there), none otherwise (every
+// block then sees every query).
 inline int attn_bwd_dkv_split(int s, int causal) {
   const int nkb = (s + attnb::KEY_BLOCK - 1) / attnb::KEY_BLOCK;
-  return causal ? nkb / 2 : 0;
+  return causal ? nkb - nkb / 8 : 0;
 }
 // Floats of dkv_part for `split` split key blocks.
 inline int64_t attn_bwd_dkv_part_floats(int b, int kv, int split, int d) {
   return (int64_t)b * kv * split * 2 * (2 * (d / 32) * 16 * 64);
 }
 
-// dK/dV (a.split and a.dkv_part set by the caller; split <= nkb / 2), then
-// the kernel that finishes the split blocks.
+// dK/dV (a.split and a.dkv_part set by the caller; split <= nkb), then the
+// kernel that finishes the split blocks.
 template <int D>
 hipError_t launch_attn_bwd_dkv(const attnb::BwdArgs& a, hipStream_t stream) {
   const int nkb = (a.s + attnb::KEY_BLOCK - 1) / attnb::KEY_BLOCK;

@@ -611,7 +611,11 @@ int tp_attn_shard_bwd(const tp_attn_desc* d, const void* dZ, const void* X, cons
   // dK/dV's heaviest key blocks run as two halves whose fp32 sums go to
   // dWqkv_i's memory, written only by the last GEMM below
   a.split = split_tail_enabled() ? attn_bwd_dkv_split(a.s, a.causal) : 0;
-  if (attn_bwd_dkv_part_floats(a.b, a.kv, a.split, D) * 4 > d->h * nqkv64 * 4) a.split = 0;
+  if (a.split > 0) {  // as many as dWqkv_i's memory holds
+    const int64_t per_block = attn_bwd_dkv_part_floats(a.b, a.kv, 1, D);
+    const int64_t fits = per_block > 0 ? d->h * nqkv64 / per_block : 0;
+    if (fits < a.split) a.split = (int)fits;
+  }
   a.dkv_part = dWqkv_i;
   const int hg = heads_per_wg(q / kv);
   // dQ's heaviest query blocks likewise, their halves' sums in dX_i's memory
