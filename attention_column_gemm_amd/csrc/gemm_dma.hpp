@@ -198,9 +198,11 @@ constexpr int smem_bytes() {
 // work-group with `smem` (smem_bytes() bytes, 1 KiB aligned) as its LDS.
 // With KRANGE the K tiles kt_begin .. kt_begin + n_kt - 1 are accumulated
 // (the K tiles of the segments numbered consecutively), otherwise all of them.
+// With rows_win > 0, w numbers the tiles of the tile rows tm_lo ..
+// tm_lo + rows_win - 1 only (the same XCD-aware order within that window).
 template <int BM, int BN, int WGM, int WGN, int BK, int AL, int BL, class Epi, bool KRANGE = false>
 __device__ __forceinline__ void gemm_dma_tile(const GemmProblem& p, const Epi& epi, int w, uint8_t* smem,
-                                              int kt_begin = 0, int n_kt = 0) {
+                                              int kt_begin = 0, int n_kt = 0, int tm_lo = 0, int rows_win = 0) {
   constexpr int NW = WGM * WGN;
   constexpr int NB = Epi::NB;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -213,7 +215,8 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmProblem& p, const Epi& e
 
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   int tm, tn;
-  gemm::tile_coords(w, tiles_m, tiles_n, tm, tn);
+  gemm::tile_coords(w, rows_win > 0 ? rows_win : tiles_m, tiles_n, tm, tn);
+  tm += tm_lo;
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -536,6 +539,37 @@ __global__ void __launch_bounds__(C1::THREADS, 1)
     gemm_dma_tile<C2::BM, C2::BN, C2::WGM, C2::WGN, C2::BK, C2::AL, C2::BL, E2>(p2, e2, w - tiles1, smem);
 }
 
+// A paired launch whose problem 2 runs its last tile rows as half-width
+// tiles: work-groups 0 .. tiles1-1 take problem 1, the next ones problem 2's
+// tile rows 0 .. rows2-1 at full width, the rest its remaining rows as
+// BM x BN/2 tiles, dispatched last.  When the launch's last round of full
+// tiles would leave CUs idle, those rows fill it with twice as many tiles of
+// half the work.  Each output element sums the same K tiles in the same
+// order as with full-width tiles, so the result is bit-identical.
+template <class C1, class E1, class C2, class E2>
+__global__ void __launch_bounds__(C1::THREADS, 1)
+    gemm_dma_pair_tail_kernel(GemmProblem p1, E1 e1, GemmProblem p2, E2 e2, int tiles1, int rows2) {
+  static_assert(C1::THREADS == C2::THREADS, "both problems run on work-groups of one size");
+  constexpr int HBN = C2::BN / 2;
+  constexpr int S1 = smem_bytes<C1::BM, C1::BN, C1::WGM, C1::WGN, C1::BK, E1::NB>();
+  constexpr int S2 = smem_bytes<C2::BM, C2::BN, C2::WGM, C2::WGN, C2::BK, E2::NB>();
+  constexpr int S12 = S1 > S2 ? S1 : S2;
+  constexpr int S3 = smem_bytes<C2::BM, HBN, C2::WGM, C2::WGN, C2::BK, E2::NB>();
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S12 > S3 ? S12 : S3];
+  const int w = blockIdx.x;
+  const int tiles2 = rows2 * ((p2.N + C2::BN - 1) / C2::BN);
+  if (w < tiles1) {
+    gemm_dma_tile<C1::BM, C1::BN, C1::WGM, C1::WGN, C1::BK, C1::AL, C1::BL, E1>(p1, e1, w, smem);
+  } else if (w < tiles1 + tiles2) {
+    gemm_dma_tile<C2::BM, C2::BN, C2::WGM, C2::WGN, C2::BK, C2::AL, C2::BL, E2>(p2, e2, w - tiles1, smem, 0, 0, 0,
+                                                                              rows2);
+  } else {
+    const int rows3 = (p2.M + C2::BM - 1) / C2::BM - rows2;
+    gemm_dma_tile<C2::BM, HBN, C2::WGM, C2::WGN, C2::BK, C2::AL, C2::BL, E2>(p2, e2, w - tiles1 - tiles2, smem, 0, 0,
+                                                                           rows2, rows3);
+  }
+}
+
 }  // namespace gemm3
 
 // Host-side launcher: grid of ceil(M/BM) * ceil(N/BN) work-groups of 64 * WGM * WGN threads.
@@ -586,6 +620,34 @@ hipError_t launch_gemm_dma_pair(const GemmProblem& p1, const E1& e1, const GemmP
   if (t1 + t2 == 0) return hipSuccess;
   hipLaunchKernelGGL((gemm3::gemm_dma_pair_kernel<C1, E1, C2, E2>), dim3(t1 + t2), dim3(C1::THREADS), 0, stream,
                      p1, e1, p2, e2, t1);
+  return hipGetLastError();
+}
+
+// Tile rows of problem 2 that a paired launch keeps at full width, or -1 when
+// the half-width tail does not apply: the launch has more than one round of
+// tiles, its last round is at most half full, and the fewest whole tile rows
+// of problem 2 that cover that round's tiles leave at least one row whole.
+template <class C1, class C2>
+int pair_tail_rows(const GemmProblem& p1, const GemmProblem& p2) {
+  const int t1 = ((p1.M + C1::BM - 1) / C1::BM) * ((p1.N + C1::BN - 1) / C1::BN);
+  const int rows = (p2.M + C2::BM - 1) / C2::BM, cols = (p2.N + C2::BN - 1) / C2::BN;
+  const int total = t1 + rows * cols, tail = total % 256;
+  if (total <= 256 || tail == 0 || tail > 128 || cols == 0) return -1;
+  const int split = (tail + cols - 1) / cols;
+  return split < rows ? rows - split : -1;
+}
+
+// Paired launcher with problem 2's last tile rows at half width (rows2 from
+// pair_tail_rows, at least 0).
+template <class C1, class C2, class E1, class E2>
+hipError_t launch_gemm_dma_pair_tail(const GemmProblem& p1, const E1& e1, const GemmProblem& p2, const E2& e2,
+                                     int rows2, hipStream_t stream) {
+  const int t1 = ((p1.M + C1::BM - 1) / C1::BM) * ((p1.N + C1::BN - 1) / C1::BN);
+  const int rows = (p2.M + C2::BM - 1) / C2::BM;
+  const int t2 = rows2 * ((p2.N + C2::BN - 1) / C2::BN);
+  const int t3 = (rows - rows2) * ((p2.N + C2::BN / 2 - 1) / (C2::BN / 2));
+  hipLaunchKernelGGL((gemm3::gemm_dma_pair_tail_kernel<C1, E1, C2, E2>), dim3(t1 + t2 + t3), dim3(C1::THREADS), 0,
+                     stream, p1, e1, p2, e2, t1, rows2);
   return hipGetLastError();
 }
 

@@ -83,9 +83,9 @@ GemmProblem problem(int M, int N, int K, const void* A, int64_t lda, const void*
 // chip clocks higher), with 128 or fewer the small tile wins.
 // TPSHARD_TILE=large|small overrides the choice (used by the tests to cover
 // both tile shapes at small sizes).
-// TPSHARD_SPLIT_TAIL=0 turns off the split of a GEMM's last round and the
-// splits of the attention kernels' heaviest key and query blocks (the tests
-// compare both ways).
+// TPSHARD_SPLIT_TAIL=0 turns off the split of a GEMM's last round (in K for
+// a single GEMM, in N for a pair), and the splits of the attention kernels'
+// heaviest key and query blocks (the tests compare both ways).
 bool split_tail_enabled() {
   const char* v = std::getenv("TPSHARD_SPLIT_TAIL");
   return !(v && !std::strcmp(v, "0"));
@@ -147,7 +147,9 @@ hipError_t gemm_bf16_split(const GemmProblem& p, const Epi& epi, hipStream_t st,
 // crossover above, then both the small one.  A GEMM whose last round of tiles
 // leaves CUs idle costs about a full round on its own (a power-limited chip
 // clocks only a little higher when partly idle); in a pair the other
-// problem's tiles take those CUs.
+// problem's tiles take those CUs.  If the pair's last round is still at most
+// half full, problem 2's last tile rows run as tiles of half the width,
+// twice as many and half as long.
 template <int AL1, int BL1, int AL2, int BL2, class E1, class E2>
 hipError_t gemm_bf16_pair(const GemmProblem& p1, const E1& e1, const GemmProblem& p2, const E2& e2,
                           hipStream_t st) {
@@ -162,8 +164,14 @@ hipError_t gemm_bf16_pair(const GemmProblem& p1, const E1& e1, const GemmProblem
     return launch_gemm_dma_pair<gemm3::TileCfg<128, BN1 / 2, 2, 2, 64, AL1, BL1>,
                                 gemm3::TileCfg<128, BN2 / 2, 2, 2, 64, AL2, BL2>>(p1, e1, p2, e2, st);
   }
-  return launch_gemm_dma_pair<gemm3::TileCfg<256, BN1, 4, 2, 64, AL1, BL1>,
-                              gemm3::TileCfg<256, BN2, 4, 2, 64, AL2, BL2>>(p1, e1, p2, e2, st);
+  using C1 = gemm3::TileCfg<256, BN1, 4, 2, 64, AL1, BL1>;
+  using C2 = gemm3::TileCfg<256, BN2, 4, 2, 64, AL2, BL2>;
+  if constexpr (E2::NB == 1) {
+    // last round at most half full: problem 2's last tile rows as 256 x 128 tiles
+    const int rows2 = split_tail_enabled() ? pair_tail_rows<C1, C2>(p1, p2) : -1;
+    if (rows2 >= 0) return launch_gemm_dma_pair_tail<C1, C2>(p1, e1, p2, e2, rows2, st);
+  }
+  return launch_gemm_dma_pair<C1, C2>(p1, e1, p2, e2, st);
 }
 
 // Operands stored in bf16 run on the matrix cores, operands stored in fp32 on

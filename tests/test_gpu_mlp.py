@@ -240,3 +240,41 @@ def test_mlp_split_tail_parity(name, monkeypatch):
         del sh
     ran = not torch.equal(outs["1"], outs["0"])
     assert ran == ("no_room" not in name), "the split ran where it should not, or did not run where it should"
+
+
+PAIR_TAIL_CASES = {
+    # dWg, dWu (13 x 16 tiles of 256 x 128) + dX (4 x 13 tiles of 256 x 256): 260 tiles, the last
+    # round holding 4, so dX's last tile row runs as 26 tiles of 256 x 128; ragged in T, h and f
+    "swiglu_dW1_dX_T1000_h3304_f2040": I.custom_mlp(108, 1, 1000, 3304, 2040, 1, "swiglu", "bf16"),
+    # dH (18 x 13) + dW2 (13 x 2): 260 tiles, so dW2's last two tile rows run at half width;
+    # GeLU with both biases and dropout, ragged in T, h and f
+    "gelu_dH_dW2_T4600_h504_f3304": I.custom_mlp(109, 2, 2300, 504, 3304, 1, "gelu", "bf16", p_drop=0.1,
+                                                 bias=True),
+}
+
+
+@pytest.mark.parametrize("name", list(PAIR_TAIL_CASES))
+def test_mlp_pair_half_width_tail_parity(name, monkeypatch):
+    """A paired backward launch whose last round of large tiles is at most
+    half full runs problem 2's last tile rows as 256 x 128 tiles.  Every
+    output against the oracle with the tail on and off; each output element
+    sums the same K tiles in the same order either way, so the two runs are
+    bit-identical."""
+    torch = need_gpu()
+    c = PAIR_TAIL_CASES[name]
+    X, dOut = I.mlp_activation(c)
+    w = I.mlp_rank_weights(c, 0)
+    fw, bw = O.shard_step(dOut, X, w["W1"], w["W2"], act=c.act, Wu_i=w["Wu"], b1_i=w["b1"], p=c.p_drop, seed=c.seed)
+    runs = {}
+    for split in ("1", "0"):
+        monkeypatch.setenv("TPSHARD_SPLIT_TAIL", split)
+        banner(f"mlp pair tail={split} {name}")
+        sh = _gpu_rank(c, 0, X, dOut, w)
+        torch.cuda.synchronize()
+        _compare_rank(c, sh, fw, bw, tag=f"split{split}.")
+        _compare_rank_grads(c, sh, bw, tag=f"split{split}.")
+        check(f"split{split}.db2", _np(sh.db2), bw["db2"], TOL[c.dtype])
+        runs[split] = [t.clone() for t in (sh.dA, sh.dW1, sh.dW2, sh.dX)]
+        del sh
+    for a, b in zip(runs["1"], runs["0"]):
+        assert torch.equal(a, b), "the half-width tail changed a result"
