@@ -243,13 +243,13 @@ def test_mlp_split_tail_parity(name, monkeypatch):
 
 
 PAIR_TAIL_CASES = {
-    # dWg, dWu (13 x 16 tiles of 256 x 128) + dX (4 x 13 tiles of 256 x 256): 260 tiles, the last
-    # round holding 4, so dX's last tile row runs as 26 tiles of 256 x 128; ragged in T, h and f
-    "swiglu_dW1_dX_T1000_h3304_f2040": I.custom_mlp(108, 1, 1000, 3304, 2040, 1, "swiglu", "bf16"),
-    # dH (18 x 13) + dW2 (13 x 2): 260 tiles, so dW2's last two tile rows run at half width;
-    # GeLU with both biases and dropout, ragged in T, h and f
-    "gelu_dH_dW2_T4600_h504_f3304": I.custom_mlp(109, 2, 2300, 504, 3304, 1, "gelu", "bf16", p_drop=0.1,
-                                                 bias=True),
+    # dWg, dWu (15 x 4 tiles of 256 x 128) + dX (18 x 15 tiles of 256 x 256): 330 tiles, the last
+    # round holding 74, so dX's last five tile rows run as 145 tiles of 256 x 128; ragged in T, h, f
+    "swiglu_dW1_dX_T4400_h3704_f504": I.custom_mlp(108, 2, 2200, 3704, 504, 1, "swiglu", "bf16"),
+    # dH (5 x 16) + dW2 (16 x 16): 336 tiles, the last round holding 80, so dW2's last five tile
+    # rows run at half width; GeLU with both biases and dropout, ragged in T, h and f
+    "gelu_dH_dW2_T1200_h3960_f3960": I.custom_mlp(109, 2, 600, 3960, 3960, 1, "gelu", "bf16", p_drop=0.1,
+                                                  bias=True),
 }
 
 
