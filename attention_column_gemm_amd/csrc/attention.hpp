@@ -256,9 +256,10 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_fwd_kernel(AttnArgs a) {
 }
 
 // Merge of the two halves of every split query block, one thread per (slot,
-// wave, lane): both halves rescaled to the common maximum (exp2, the scores
-// being in log2 units) and added in a fixed order (first + second), then
-// normalized and stored with the row and head mapping of attn_fwd_kernel.
+// wave, 32-wide d tile, lane): both halves' values loaded first, each half
+// rescaled to the common maximum (exp2, the scores being in log2 units) and
+// the halves added in a fixed order (first + second), then normalized and
+// stored with the row and head mapping of attn_fwd_kernel.
 template <int D>
 __global__ void __launch_bounds__(NTHREADS) attn_fwd_merge_kernel(AttnArgs a) {
   constexpr int DT = D / 32, W = (DT * 16 + 2) * 64;
@@ -267,8 +268,10 @@ __global__ void __launch_bounds__(NTHREADS) attn_fwd_merge_kernel(AttnArgs a) {
   const int group = a.q / a.kv, sub_per_kv = group / a.hg;
   const int ny = a.b * a.kv * sub_per_kv;
   const int64_t t = (int64_t)blockIdx.x * NTHREADS + threadIdx.x;
-  if (t >= (int64_t)a.split * ny * 4 * 64) return;
-  const int lane = (int)(t & 63), wave = (int)((t >> 6) & 3), slot = (int)(t >> 8);
+  if (t >= (int64_t)a.split * ny * 4 * DT * 64) return;
+  const int lane = (int)(t & 63), tt = (int)((t >> 6) % DT);
+  const int64_t sw = (t >> 6) / DT;
+  const int wave = (int)(sw & 3), slot = (int)(sw >> 2);
   const int i = slot / ny, y = slot % ny;
   const int pb = npb - 1 - i;
   const int beta = y / (a.kv * sub_per_kv), rem = y % (a.kv * sub_per_kv);
@@ -278,6 +281,12 @@ __global__ void __launch_bounds__(NTHREADS) attn_fwd_merge_kernel(AttnArgs a) {
   if (my_row >= a.s) return;
   const float* h0 = a.part + ((int64_t)(slot * 2) * 4 + wave) * W;
   const float* h1 = h0 + 4 * W;
+  float x0[16], x1[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    x0[e] = h0[(tt * 16 + e) * 64 + lane];
+    x1[e] = h1[(tt * 16 + e) * 64 + lane];
+  }
   const float m0 = h0[DT * 16 * 64 + lane], m1 = h1[DT * 16 * 64 + lane];
   const float l0 = h0[(DT * 16 + 1) * 64 + lane] + h0[(DT * 16 + 1) * 64 + (lane ^ 32)];
   const float l1 = h1[(DT * 16 + 1) * 64 + lane] + h1[(DT * 16 + 1) * 64 + (lane ^ 32)];
@@ -286,20 +295,15 @@ __global__ void __launch_bounds__(NTHREADS) attn_fwd_merge_kernel(AttnArgs a) {
   const float c1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
   const float l = l0 * c0 + l1 * c1;
   const float inv = 1.0f / l;
-  uint16_t* orow = a.o + ((int64_t)beta * a.s + my_row) * a.ld_o + (int64_t)j * D;
+  uint16_t* orow = a.o + ((int64_t)beta * a.s + my_row) * a.ld_o + (int64_t)j * D + tt * 32;
 #pragma unroll
-  for (int tt = 0; tt < DT; ++tt)
+  for (int q4 = 0; q4 < 4; ++q4) {
+    float v[4];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      float v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = (tt * 16 + 4 * q4 + e) * 64 + lane;
-        v[e] = (h0[r] * c0 + h1[r] * c1) * inv;
-      }
-      Elem<uint16_t>::store4(orow + tt * 32 + 8 * q4 + 4 * hgrp, v);
-    }
-  if (a.lse && hgrp == 0)
+    for (int e = 0; e < 4; ++e) v[e] = (x0[4 * q4 + e] * c0 + x1[4 * q4 + e] * c1) * inv;
+    Elem<uint16_t>::store4(orow + 8 * q4 + 4 * hgrp, v);
+  }
+  if (a.lse && hgrp == 0 && tt == 0)
     a.lse[((int64_t)beta * a.q + j) * a.s + my_row] = (m + __log2f(l)) * 0.69314718055994531f;
 }
 
@@ -332,7 +336,7 @@ hipError_t launch_attn_fwd(const attn::AttnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((attn::attn_fwd_kernel<D>), dim3((npb + a.split) * ny), dim3(attn::NTHREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n = (int64_t)a.split * ny * 4 * 64;
+  const int64_t n = (int64_t)a.split * ny * 4 * (D / 32) * 64;
   hipLaunchKernelGGL((attn::attn_fwd_merge_kernel<D>), dim3((unsigned)((n + attn::NTHREADS - 1) / attn::NTHREADS)),
                      dim3(attn::NTHREADS), 0, stream, a);
   return hipGetLastError();

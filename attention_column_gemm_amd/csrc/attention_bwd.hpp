@@ -530,7 +530,8 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_kernel(BwdArgs a, int
 
 // dQ of the split query blocks: the two halves added in a fixed order (first
 // + second), scaled and stored as bf16, with the row and head mapping of
-// attn_bwd_dq_kernel.  One thread per (slot, wave, lane, dt).
+// attn_bwd_dq_kernel.  One thread per (slot, wave, dt, lane), the lane
+// fastest so that every load reads 64 consecutive floats.
 template <int D>
 __global__ void __launch_bounds__(NTHREADS) attn_bwd_dq_combine_kernel(BwdArgs a, int hg) {
   constexpr int DT = D / 32, PART = 4 * DT * 16 * 64;
@@ -540,8 +541,8 @@ __global__ void __launch_bounds__(NTHREADS) attn_bwd_dq_combine_kernel(BwdArgs a
   const int ny = a.b * a.kv * sub_per_kv;
   const int64_t t = (int64_t)blockIdx.x * NTHREADS + threadIdx.x;
   if (t >= (int64_t)a.dq_split * ny * 4 * 64 * DT) return;
-  const int dt = (int)(t % DT), lane = (int)((t / DT) & 63), wave = (int)((t / (DT * 64)) & 3);
-  const int slot = (int)(t / (DT * 64 * 4));
+  const int lane = (int)(t & 63), dt = (int)((t >> 6) % DT), wave = (int)(((t >> 6) / DT) & 3);
+  const int slot = (int)((t >> 6) / DT / 4);
   const int i = slot / ny, y = slot % ny;
   const int pb = npb - 1 - i;
   const int beta = y / (a.kv * sub_per_kv), rem = y % (a.kv * sub_per_kv);
@@ -552,11 +553,17 @@ __global__ void __launch_bounds__(NTHREADS) attn_bwd_dq_combine_kernel(BwdArgs a
   const float* p0 = a.dq_part + ((int64_t)(slot * 2) * 4 + wave) * (DT * 16 * 64) + dt * 16 * 64 + lane;
   const float* p1 = p0 + PART;
   uint16_t* dst = a.dqkv + ((int64_t)beta * a.s + my_row) * a.ld_qkv + (int64_t)j * D + 32 * dt + 4 * h;
+  float x0[16], x1[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    x0[e] = p0[e * 64];
+    x1[e] = p1[e * 64];
+  }
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
     float v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (p0[(4 * q4 + e) * 64] + p1[(4 * q4 + e) * 64]) * a.scale;
+    for (int e = 0; e < 4; ++e) v[e] = (x0[4 * q4 + e] + x1[4 * q4 + e]) * a.scale;
     Elem<uint16_t>::store4(dst + 8 * q4, v);
   }
 }

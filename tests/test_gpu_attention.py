@@ -233,16 +233,28 @@ def test_attention_backward_key_block_split(name, monkeypatch):
     assert same_q != dq_split, "the dQ split ran where it should not, or did not run where it should"
 
 
-@pytest.mark.parametrize("name", ["mqa4_d128_h2048", "gqa4_d128_ragged"])
+FWD_SPLIT = {
+    # (config, causal, split expected)
+    # 8 query blocks, the heavier 4 as two halves each
+    "mqa4_d128_h2048": (SPLIT_BWD["mqa4_d128_h2048"][0], True, True),
+    # Z_i's memory too small for the halves: runs unsplit both ways
+    "gqa4_d128_ragged_no_room": (SMALL["gqa4_d128_ragged"][0], True, False),
+    # h = 4096, one sequence of 256
+    "mqa4_d128_h4096": (I.custom_attn(208, 1, 256, 4096, 4, 1, 128, 1), True, True),
+    # two sequences of 200 (ragged last block): the heavier 3 of 7 query blocks per sequence split
+    "mqa4_d128_s200_ragged": (I.custom_attn(209, 2, 200, 4096, 4, 1, 128, 1), True, True),
+}
+
+
+@pytest.mark.parametrize("name", list(FWD_SPLIT))
 def test_attention_forward_query_block_split(name, monkeypatch):
     """A causal forward whose launch leaves work-group slots empty runs its
     heavier half of query blocks as two work-groups over the halves of the
     keys (softmax state in Z_i's memory, merged by a second kernel).  O_i,
     lse_i and Z_i against the oracle with the split on and off; O_i differs
-    in rounding where the split ran (proof that it ran: Z_i's memory holds
-    the halves only for h = 2048)."""
+    in rounding where the split ran (proof that it ran)."""
     torch = need_gpu()
-    c, causal, expect = SPLIT_BWD[name]
+    c, causal, expect = FWD_SPLIT[name]
     ref = None
     got = {}
     for split in ("1", "0"):
