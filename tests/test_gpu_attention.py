@@ -276,3 +276,16 @@ def test_attention_forward_query_block_split(name, monkeypatch):
         got[split] = sh.O.clone()
         del sh
     assert torch.equal(got["1"], got["0"]) != expect, "the query-block split ran where it should not, or did not run"
+
+
+def test_attention_backward_pair_half_width_tail():
+    """The paired dWqkv + dX launch at h = 4088, T = 4000 with eight local
+    query heads and one KV head: 16 x 5 + 16 x 16 = 336 large tiles, 80 in
+    the last round, so dX's last five tile rows run as 256 x 128 tiles
+    (ragged in both directions).  Every backward output against the oracle."""
+    torch = need_gpu()
+    c = I.custom_attn(210, 4, 1000, 4088, 8, 1, 128, 1)
+    banner(f"attn bwd pair half-width tail b={c.b} s={c.s} h={c.h} n_q={c.n_q} n_kv={c.n_kv} d={c.d}")
+    sh, X, w, dZ = _run_bwd(c, 0, True)
+    torch.cuda.synchronize()
+    _check_bwd("tail", c, sh, X, w, dZ, True)
