@@ -68,11 +68,26 @@ __device__ __forceinline__ uint32_t kofs(int row, int c) {
   return row * 128 + ((c ^ ((row ^ (row >> 3)) & 7)) << 4);
 }
 
-// Byte offset of 16-byte chunk c of k-row k in an M/N-contiguous [32][ROWS] tile.
+// XOR applied to the 16-byte chunk index within k-row k of an M/N-contiguous
+// tile of NCH chunks per k-row.  A transposing fragment read serves 32 lanes
+// per pass from four consecutive k-rows (k = 4j .. 4j+3) and four chunks of
+// each; with 64 banks of 4 bytes, k-rows of 256 or 512 bytes start on the
+// same bank, so those four k-rows must land in four different groups of four
+// chunks: XOR with 4 (k & 3).  k-rows of 128 bytes alternate between the two
+// bank halves by themselves, and XOR with 2 (k & 7) keeps them apart.
+template <int NCH>
+__device__ __forceinline__ int mswz(int k) {
+  if constexpr (NCH >= 16)
+    return ((k & 3) << 2) & (NCH - 1);
+  else
+    return ((k & 7) << 1) & (NCH - 1);
+}
+
+// Byte offset of 16-byte chunk c of k-row k in an M/N-contiguous [BK][ROWS] tile.
 template <int ROWS>
 __device__ __forceinline__ uint32_t mofs(int k, int c) {
   constexpr int NCH = ROWS / 8;
-  return k * ROWS * 2 + ((c ^ (((k & 7) << 1) & (NCH - 1))) << 4);
+  return k * ROWS * 2 + ((c ^ mswz<NCH>(k)) << 4);
 }
 
 struct DOperand {
@@ -126,7 +141,7 @@ struct DmaLoader {
         constexpr int NCH = ROWS / 8;
         const int kk = q / NCH, p = q % NCH;
         k = kk;
-        r = (p ^ (((kk & 7) << 1) & (NCH - 1))) * 8;
+        r = (p ^ mswz<NCH>(kk)) * 8;
       }
       r += row0;
       kloc[i] = r < rows ? k : (1 << 30);
