@@ -30,13 +30,17 @@ __device__ __forceinline__ void causal_block_order(int npb, int ny, int& pb, int
 }
 
 // 16-byte chunk permutation of a row-major [rows][D] bf16 tile: logical chunk
-// c of row r sits at chunk c ^ swz(r).  Sixteen consecutive rows at one
-// logical chunk (a 128-bit fragment read) and four consecutive rows at one
-// aligned chunk pair (a transposing read) both land on distinct banks.
+// c of row r sits at chunk c ^ swz(r).  Two reads must both be conflict-free
+// on gfx950's 64 banks of 4 bytes: 128-bit row fragments (16 lanes per pass,
+// 16 consecutive rows, one chunk each) and transposing reads (32 lanes per
+// pass, four consecutive rows, four chunks each).  D = 128 (256-byte rows, each starting on the same
+// bank): the low two row bits pick one of four groups of four chunks and the
+// next two the chunk within the group.  D = 64 (128-byte rows, even and odd
+// rows in opposite bank halves): row bit 1 picks the group, bits 2-3 the chunk.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  if (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
-  return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);  // D = 64: row parity picks the bank half
+  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 template <int D>
 __device__ __forceinline__ uint32_t tile_off(int r, int c) {
