@@ -15,6 +15,8 @@ import ctypes
 import os
 import re
 
+from . import validate as V
+
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB_PATH = os.path.join(PKG, "libtpshard.so")
@@ -23,6 +25,7 @@ HEADER = os.path.join(ROOT, "include", "tp_shard.h")
 TP_F32, TP_BF16 = 0, 1
 TP_GELU, TP_SWIGLU = 0, 1
 TP_OK, TP_EINVAL, TP_ENOTDIV, TP_EDTYPE, TP_EALIGN, TP_EHIP, TP_EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+TP_TILE_AUTO, TP_TILE_LARGE, TP_TILE_SMALL, TP_TILE_TINY = 0, 1, 2, 3
 
 
 class TPError(RuntimeError):
@@ -79,11 +82,15 @@ def lib() -> ctypes.CDLL:
         L.tp_attn_shard_heads.argtypes = [ctypes.c_int32] * 4 + [ctypes.POINTER(ctypes.c_int32)] * 4
         L.tp_comm_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.POINTER(tp_comm)]
+        L.tp_set_options.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        L.tp_get_options.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+        L.tp_profile_arm.argtypes = [ctypes.POINTER(_VP), ctypes.c_int32]
         L.tp_status_string.argtypes = [ctypes.c_int]
         L.tp_status_string.restype = ctypes.c_char_p
         for name in ("tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_attn_shard_fwd", "tp_attn_shard_bwd",
                      "tp_sum_partials", "tp_sum_partials_residual", "tp_reduce_scatter", "tp_all_gather",
-                     "tp_mlp_shard_cols", "tp_attn_shard_heads", "tp_comm_bytes"):
+                     "tp_mlp_shard_cols", "tp_attn_shard_heads", "tp_comm_bytes", "tp_set_options",
+                     "tp_get_options", "tp_profile_arm"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -108,6 +115,8 @@ def _ptr(x):
     if hasattr(x, "data_ptr"):
         if hasattr(x, "is_cuda") and not x.is_cuda:
             raise ValueError("tensor arguments must live in GPU memory")
+        if hasattr(x, "is_contiguous") and not x.is_contiguous():
+            raise ValueError("tensor arguments must be contiguous (the library reads dense row-major memory)")
         return x.data_ptr()
     raise TypeError(f"cannot pass {type(x)} as a device pointer")
 
@@ -126,13 +135,53 @@ def _check(rc: int, where: str):
         raise TPError(rc, where)
 
 
+def _mlp_sizes(desc):
+    """(T, h, f, n_saved) of a descriptor, or None when the library would reject it anyway."""
+    try:
+        f, _ = tp_mlp_shard_cols(desc.h_ffn, desc.t, desc.rank, desc.dtype)
+    except (TPError, ctypes.ArgumentError):
+        return None
+    return desc.tokens, desc.h, f, (1 if desc.act == TP_GELU else 2)
+
+
+def _attn_sizes(desc):
+    """(T, h, q*d, (q+2kv)*d, b*q*s) of a descriptor, or None when the library would reject it anyway."""
+    try:
+        q, kv, _, _ = tp_attn_shard_heads(desc.n_q, desc.n_kv, desc.t, desc.rank)
+    except (TPError, ctypes.ArgumentError):
+        return None
+    return desc.b * desc.s, desc.h, q * desc.d, (q + 2 * kv) * desc.d, desc.b * q * desc.s
+
+
+def _need(code, **sized):
+    for name, (x, n) in sized.items():
+        V.at_least(name, x, n, code)
+
+
+def _need_f32(**sized):
+    for name, (x, n) in sized.items():
+        V.at_least_f32(name, x, n)
+
+
 def tp_mlp_shard_fwd(desc: tp_mlp_desc, X, W1_i, Wu_i, b1_i, W2_i, saved_i, H_i, Z_i, stream=None):
+    z = _mlp_sizes(desc)
+    if z:
+        T, h, f, ns = z
+        _need(desc.dtype, X=(X, T * h), W1_i=(W1_i, h * f), Wu_i=(Wu_i, h * f), b1_i=(b1_i, f), W2_i=(W2_i, f * h),
+              saved_i=(saved_i, ns * T * f), H_i=(H_i, T * f), Z_i=(Z_i, T * h))
     _check(lib().tp_mlp_shard_fwd(ctypes.byref(desc), _ptr(X), _ptr(W1_i), _ptr(Wu_i), _ptr(b1_i), _ptr(W2_i),
                                   _ptr(saved_i), _ptr(H_i), _ptr(Z_i), _stream(stream)), "tp_mlp_shard_fwd")
 
 
 def tp_mlp_shard_bwd(desc: tp_mlp_desc, dOut, p_drop: float, seed: int, X, W1_i, Wu_i, W2_i, saved_i, H_i,
                      dY, db2, dA_i, dW1_i, db1_i, dW2_i, dX_i, stream=None):
+    z = _mlp_sizes(desc)
+    if z:
+        T, h, f, ns = z
+        _need(desc.dtype, dOut=(dOut, T * h), X=(X, T * h), W1_i=(W1_i, h * f), Wu_i=(Wu_i, h * f),
+              W2_i=(W2_i, f * h), saved_i=(saved_i, ns * T * f), H_i=(H_i, T * f), dY=(dY, T * h),
+              dA_i=(dA_i, ns * T * f), dX_i=(dX_i, T * h))
+        _need_f32(db2=(db2, h), dW1_i=(dW1_i, ns * h * f), db1_i=(db1_i, f), dW2_i=(dW2_i, f * h))
     _check(lib().tp_mlp_shard_bwd(ctypes.byref(desc), _ptr(dOut), float(p_drop), int(seed) & (2 ** 64 - 1),
                                   _ptr(X), _ptr(W1_i), _ptr(Wu_i), _ptr(W2_i), _ptr(saved_i), _ptr(H_i), _ptr(dY),
                                   _ptr(db2), _ptr(dA_i), _ptr(dW1_i), _ptr(db1_i), _ptr(dW2_i), _ptr(dX_i),
@@ -140,19 +189,40 @@ def tp_mlp_shard_bwd(desc: tp_mlp_desc, dOut, p_drop: float, seed: int, X, W1_i,
 
 
 def tp_attn_shard_fwd(desc: tp_attn_desc, X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, Z_i, stream=None):
+    z = _attn_sizes(desc)
+    if z:
+        T, h, nq, nqkv, rows = z
+        _need(TP_BF16, X=(X, T * h), Wqkv_i=(Wqkv_i, h * nqkv), Wo_i=(Wo_i, nq * h), QKV_i=(QKV_i, T * nqkv),
+              O_i=(O_i, T * nq), Z_i=(Z_i, T * h))
+        _need_f32(lse_i=(lse_i, rows))
     _check(lib().tp_attn_shard_fwd(ctypes.byref(desc), _ptr(X), _ptr(Wqkv_i), _ptr(Wo_i), _ptr(QKV_i), _ptr(O_i),
                                    _ptr(lse_i), _ptr(Z_i), _stream(stream)), "tp_attn_shard_fwd")
 
 
 def tp_attn_shard_bwd(desc: tp_attn_desc, dZ, X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, dO_i, stats_i, dQKV_i, dWqkv_i,
                       dWo_i, dX_i, stream=None):
+    z = _attn_sizes(desc)
+    if z:
+        T, h, nq, nqkv, rows = z
+        _need(TP_BF16, dZ=(dZ, T * h), X=(X, T * h), Wqkv_i=(Wqkv_i, h * nqkv), Wo_i=(Wo_i, nq * h),
+              QKV_i=(QKV_i, T * nqkv), O_i=(O_i, T * nq), dO_i=(dO_i, T * nq), dQKV_i=(dQKV_i, T * nqkv),
+              dX_i=(dX_i, T * h))
+        _need_f32(lse_i=(lse_i, rows), stats_i=(stats_i, 2 * rows), dWqkv_i=(dWqkv_i, h * nqkv),
+                  dWo_i=(dWo_i, nq * h))
     _check(lib().tp_attn_shard_bwd(ctypes.byref(desc), _ptr(dZ), _ptr(X), _ptr(Wqkv_i), _ptr(Wo_i), _ptr(QKV_i),
                                    _ptr(O_i), _ptr(lse_i), _ptr(dO_i), _ptr(stats_i), _ptr(dQKV_i), _ptr(dWqkv_i),
                                    _ptr(dWo_i), _ptr(dX_i), _stream(stream)), "tp_attn_shard_bwd")
 
 
+def _need_list(code, name, xs, n):
+    for i, x in enumerate(xs):
+        V.at_least(f"{name}[{i}]", x, n, code)
+
+
 def tp_sum_partials(rows: int, cols: int, t: int, dtype: int, partials, bias, p_drop: float, seed: int, out,
                     stream=None):
+    _need_list(dtype, "partials", partials, rows * cols)
+    _need(dtype, bias=(bias, cols), out=(out, rows * cols))
     arr = (_VP * max(1, len(partials)))(*[_ptr(p) for p in partials])
     _check(lib().tp_sum_partials(int(rows), int(cols), int(t), int(dtype), arr, _ptr(bias), float(p_drop),
                                  int(seed) & (2 ** 64 - 1), _ptr(out), _stream(stream)), "tp_sum_partials")
@@ -160,6 +230,8 @@ def tp_sum_partials(rows: int, cols: int, t: int, dtype: int, partials, bias, p_
 
 def tp_sum_partials_residual(rows: int, cols: int, t: int, dtype: int, partials, bias, p_drop: float, seed: int,
                              residual, out, stream=None):
+    _need_list(dtype, "partials", partials, rows * cols)
+    _need(dtype, bias=(bias, cols), residual=(residual, rows * cols), out=(out, rows * cols))
     arr = (_VP * max(1, len(partials)))(*[_ptr(p) for p in partials])
     _check(lib().tp_sum_partials_residual(int(rows), int(cols), int(t), int(dtype), arr, _ptr(bias), float(p_drop),
                                           int(seed) & (2 ** 64 - 1), _ptr(residual), _ptr(out), _stream(stream)),
@@ -168,6 +240,9 @@ def tp_sum_partials_residual(rows: int, cols: int, t: int, dtype: int, partials,
 
 def tp_reduce_scatter(rows: int, cols: int, t: int, rank: int, dtype: int, partials, bias, p_drop: float, seed: int,
                       residual_r, out_r, stream=None):
+    _need_list(dtype, "partials", partials, rows * cols)
+    n = rows // t if t > 0 else 0
+    _need(dtype, bias=(bias, cols), residual_r=(residual_r, n * cols), out_r=(out_r, n * cols))
     arr = (_VP * max(1, len(partials)))(*[_ptr(p) for p in partials])
     _check(lib().tp_reduce_scatter(int(rows), int(cols), int(t), int(rank), int(dtype), arr, _ptr(bias),
                                    float(p_drop), int(seed) & (2 ** 64 - 1), _ptr(residual_r), _ptr(out_r),
@@ -175,9 +250,40 @@ def tp_reduce_scatter(rows: int, cols: int, t: int, rank: int, dtype: int, parti
 
 
 def tp_all_gather(rows_per_rank: int, cols: int, t: int, dtype: int, slices, out, stream=None):
+    _need_list(dtype, "slices", slices, rows_per_rank * cols)
+    _need(dtype, out=(out, t * rows_per_rank * cols))
     arr = (_VP * max(1, len(slices)))(*[_ptr(p) for p in slices])
     _check(lib().tp_all_gather(int(rows_per_rank), int(cols), int(t), int(dtype), arr, _ptr(out), _stream(stream)),
            "tp_all_gather")
+
+
+def tp_set_options(tile: int = TP_TILE_AUTO, split_tail: int = 1):
+    _check(lib().tp_set_options(int(tile), int(split_tail)), "tp_set_options")
+
+
+def tp_get_options():
+    """(tile, split_tail) currently in force."""
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().tp_get_options(ctypes.byref(a), ctypes.byref(b)), "tp_get_options")
+    return a.value, b.value
+
+
+class options:
+    """Context manager: ``with options(tile=TP_TILE_SMALL, split_tail=0): ...``
+    sets the library's launch options and restores the previous ones on exit."""
+
+    def __init__(self, tile=None, split_tail=None):
+        self.tile, self.split_tail = tile, split_tail
+
+    def __enter__(self):
+        self.saved = tp_get_options()
+        tp_set_options(self.saved[0] if self.tile is None else self.tile,
+                       self.saved[1] if self.split_tail is None else self.split_tail)
+        return self
+
+    def __exit__(self, *exc):
+        tp_set_options(*self.saved)
+        return False
 
 
 def tp_mlp_shard_cols(h_ffn: int, t: int, rank: int, dtype: int):

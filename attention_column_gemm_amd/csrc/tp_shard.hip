@@ -4,11 +4,11 @@
 // this file.  The interface is declared and documented in include/tp_shard.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
-#include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/tp_shard.h"
@@ -27,26 +27,39 @@ namespace {
 constexpr int kNumCUs = 256;
 
 // Profiling aid (tp_profile_arm): events recorded around the next kernels.
+// `armed` lets an unarmed launch skip the lock; the table itself is guarded
+// by `mu`, so concurrent launches each claim a distinct slot.
 struct ProfileHook {
+  std::mutex mu;
+  std::atomic<bool> armed{false};
   hipEvent_t ev[64];
-  int n_kernels = 0;  // kernels still to bracket
-  int next = 0;
+  int n_kernels = 0;  // kernels to bracket
+  int next = 0;       // next slot to hand out
 } g_prof;
 
 // Brackets one kernel launch with the armed events, if any.
 struct Probe {
   hipStream_t st;
-  int idx = -1;
+  hipEvent_t after = nullptr;
   explicit Probe(hipStream_t s) : st(s) {
+    if (!g_prof.armed.load(std::memory_order_acquire)) return;
+    std::lock_guard<std::mutex> lk(g_prof.mu);
     if (g_prof.next < g_prof.n_kernels) {
-      idx = g_prof.next++;
+      const int idx = g_prof.next++;
       hipEventRecord(g_prof.ev[2 * idx], st);
+      after = g_prof.ev[2 * idx + 1];
+      if (g_prof.next == g_prof.n_kernels) g_prof.armed.store(false, std::memory_order_release);
     }
   }
   ~Probe() {
-    if (idx >= 0) hipEventRecord(g_prof.ev[2 * idx + 1], st);
+    if (after) hipEventRecord(after, st);
   }
 };
+
+// Process-wide launch options (tp_set_options): the tile choice and the
+// splits of last rounds and heavy attention blocks.
+std::atomic<int> g_tile{TP_TILE_AUTO};
+std::atomic<int> g_split{1};
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool fits_int(int64_t v) { return v >= 0 && v <= INT32_MAX; }
@@ -81,37 +94,35 @@ GemmProblem problem(int M, int N, int K, const void* A, int64_t lda, const void*
 // of which two work-groups share a CU.  Measured on gfx950: with 160 or more
 // large tiles the large tile wins even though some CUs idle (a partly idle
 // chip clocks higher), with 128 or fewer the small tile wins.
-// TPSHARD_TILE=large|small overrides the choice (used by the tests to cover
-// both tile shapes at small sizes).
-// TPSHARD_SPLIT_TAIL=0 turns off the split of a GEMM's last round (in K for
-// a single GEMM, in N for a pair), and the splits of the attention kernels'
+// tp_set_options can force one tile shape (the tests cover every shape at
+// small sizes) and turn off the split of a GEMM's last round (in K for a
+// single GEMM, in N for a pair) and the splits of the attention kernels'
 // heaviest key and query blocks (the tests compare both ways).
-bool split_tail_enabled() {
-  const char* v = std::getenv("TPSHARD_SPLIT_TAIL");
-  return !(v && !std::strcmp(v, "0"));
-}
+bool split_tail_enabled() { return g_split.load(std::memory_order_relaxed) != 0; }
 
 int64_t tile_count(const GemmProblem& p, int bm, int bn) {
   return (int64_t)((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
 }
 bool use_small_tile(int64_t big) {
-  if (const char* force = std::getenv("TPSHARD_TILE")) {
-    if (!std::strcmp(force, "large")) return false;
-    if (!std::strcmp(force, "small") || !std::strcmp(force, "tiny")) return true;
+  switch (g_tile.load(std::memory_order_relaxed)) {
+    case TP_TILE_LARGE: return false;
+    case TP_TILE_SMALL:
+    case TP_TILE_TINY: return true;
+    default: return big < (int64_t)kNumCUs * 9 / 16;
   }
-  return big < (int64_t)kNumCUs * 9 / 16;
 }
 // Among launches that take the small tile, those whose small tiles would
 // fill fewer than half of the 512 work-group slots (two per CU) take the
 // 64 x 64 tile of four 32 x 32 waves instead (single-B epilogues only): small
 // GEMMs with few tiles are bound by the latency of their K loop, and four
-// times the work-groups hide it.  TPSHARD_TILE=tiny forces it.
+// times the work-groups hide it.  TP_TILE_TINY forces it.
 bool use_tiny_tile(int64_t small) {
-  if (const char* force = std::getenv("TPSHARD_TILE")) {
-    if (!std::strcmp(force, "tiny")) return true;
-    if (!std::strcmp(force, "large") || !std::strcmp(force, "small")) return false;
+  switch (g_tile.load(std::memory_order_relaxed)) {
+    case TP_TILE_TINY: return true;
+    case TP_TILE_LARGE:
+    case TP_TILE_SMALL: return false;
+    default: return small < (int64_t)kNumCUs;
   }
-  return small < (int64_t)kNumCUs;
 }
 
 template <int AL, int BL, class Epi>
@@ -382,12 +393,27 @@ extern "C" {
 
 int tp_profile_arm(void* const* events, int32_t n_events) {
   if (n_events < 0 || n_events > 64 || (n_events & 1) || (n_events && !events)) return TP_EINVAL;
-  for (int i = 0; i < n_events; ++i) {
+  for (int i = 0; i < n_events; ++i)
     if (!events[i]) return TP_EINVAL;
-    g_prof.ev[i] = static_cast<hipEvent_t>(events[i]);
-  }
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  for (int i = 0; i < n_events; ++i) g_prof.ev[i] = static_cast<hipEvent_t>(events[i]);
   g_prof.n_kernels = n_events / 2;
   g_prof.next = 0;
+  g_prof.armed.store(n_events > 0, std::memory_order_release);
+  return TP_OK;
+}
+
+int tp_set_options(int32_t tile, int32_t split_tail) {
+  if (tile < TP_TILE_AUTO || tile > TP_TILE_TINY || (split_tail != 0 && split_tail != 1)) return TP_EINVAL;
+  g_tile.store(tile, std::memory_order_relaxed);
+  g_split.store(split_tail, std::memory_order_relaxed);
+  return TP_OK;
+}
+
+int tp_get_options(int32_t* tile, int32_t* split_tail) {
+  if (!tile || !split_tail) return TP_EINVAL;
+  *tile = g_tile.load(std::memory_order_relaxed);
+  *split_tail = g_split.load(std::memory_order_relaxed);
   return TP_OK;
 }
 

@@ -38,6 +38,8 @@ from typing import Optional
 
 import numpy as np
 
+from . import flops as F
+
 TENSOR_IDS = dict(X=1, W1=2, Wu=3, W2=4, Wq=51, Wk=52, Wv=53, Wo=9, b1=6, b2=7, dOut=8)
 
 
@@ -93,8 +95,7 @@ class MLPConfig:
 
     def flops_per_rank(self) -> int:
         """fwd+bwd algorithmic FLOPs of one rank's shard: 12*T*h*f (GeLU) or 18*T*h*f (SwiGLU)."""
-        k = 12 if self.act == "gelu" else 18
-        return k * self.tokens * self.h * self.f
+        return F.mlp_shard(self.tokens, self.h, self.f, self.act)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -123,11 +124,7 @@ class AttnConfig:
 
     def flops_per_rank(self) -> int:
         """Forward FLOPs of one rank: QKV and output GEMMs plus the causal core (unmasked pairs only)."""
-        T, h, d, q, kv = self.tokens, self.h, self.d, self.q, self.kv
-        qkv = 2 * T * h * (q + 2 * kv) * d
-        out = 2 * T * q * d * h
-        core = 4 * d * self.b * q * (self.s * (self.s + 1) // 2)
-        return qkv + out + core
+        return F.attn_shard_fwd(self.b, self.s, self.h, self.q, self.kv, self.d, causal=True)
 
     def flops_bwd_per_rank(self) -> int:
         """Backward FLOPs of one rank: twice each forward term (input- and weight-gradient products)."""

@@ -9,6 +9,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import binding as B
+from . import validate as V
 
 
 def _torch():
@@ -122,28 +123,34 @@ class AttnShard:
     def backward(self, dZ, stream=None):
         """Gradients for the upstream gradient ``dZ`` [T, h] (needs a forward with lse)."""
         self.alloc_backward()
+        V.like("dZ", dZ, (self.b * self.s, self.h), self.X.dtype, self.X.device, optional=False)
         B.tp_attn_shard_bwd(self.desc, dZ, self.X, self.Wqkv, self.Wo, self.QKV, self.O, self.lse, self.dO,
                             self.stats, self.dQKV, self.dWqkv, self.dWo, self.dX, stream)
         return self.dX
 
 
-def _shape_dtype(P0):
-    torch = _torch()
-    rows, cols = P0.shape[0], int(np.prod(P0.shape[1:]))
-    return rows, cols, (B.TP_BF16 if P0.dtype == torch.bfloat16 else B.TP_F32)
+def _rows_cols(shape):
+    if len(shape) < 1:
+        raise ValueError("partials and slices need at least one dimension (rows)")
+    return shape[0], int(np.prod(shape[1:], dtype=np.int64)) if len(shape) > 1 else 1
 
 
 def sum_partials(partials, bias=None, p_drop=0.0, seed=0, out=None, stream=None, residual=None):
     """Emulated all-reduce of same-shaped device tensors (rank order), with the
     residual add fused when ``residual`` is given."""
     torch = _torch()
-    rows, cols, dtype = _shape_dtype(partials[0])
+    shape, code, dev = V.group("partials", partials)
+    rows, cols = _rows_cols(shape)
+    dt = partials[0].dtype
+    V.vector("bias", bias, cols, dt, dev)
+    V.like("residual", residual, shape, dt, dev)
     if out is None:
         out = torch.empty_like(partials[0])
+    V.like("out", out, shape, dt, dev)
     if residual is None:
-        B.tp_sum_partials(rows, cols, len(partials), dtype, list(partials), bias, p_drop, seed, out, stream)
+        B.tp_sum_partials(rows, cols, len(partials), code, list(partials), bias, p_drop, seed, out, stream)
     else:
-        B.tp_sum_partials_residual(rows, cols, len(partials), dtype, list(partials), bias, p_drop, seed, residual,
+        B.tp_sum_partials_residual(rows, cols, len(partials), code, list(partials), bias, p_drop, seed, residual,
                                    out, stream)
     return out
 
@@ -151,21 +158,30 @@ def sum_partials(partials, bias=None, p_drop=0.0, seed=0, out=None, stream=None,
 def reduce_scatter(partials, rank, bias=None, p_drop=0.0, seed=0, residual_r=None, out=None, stream=None):
     """Rank ``rank``'s token slice of the emulated all-reduce (Megatron-SP first half)."""
     torch = _torch()
-    rows, cols, dtype = _shape_dtype(partials[0])
+    shape, code, dev = V.group("partials", partials)
+    rows, cols = _rows_cols(shape)
     t = len(partials)
+    if rows % t:
+        raise ValueError(f"rows {rows} do not divide over t = {t} ranks")
+    dt = partials[0].dtype
+    sl = (rows // t,) + tuple(shape[1:])
+    V.vector("bias", bias, cols, dt, dev)
+    V.like("residual_r", residual_r, sl, dt, dev)
     if out is None:
-        out = torch.empty((rows // t,) + tuple(partials[0].shape[1:]), dtype=partials[0].dtype,
-                          device=partials[0].device)
-    B.tp_reduce_scatter(rows, cols, t, rank, dtype, list(partials), bias, p_drop, seed, residual_r, out, stream)
+        out = torch.empty(sl, dtype=dt, device=dev)
+    V.like("out", out, sl, dt, dev)
+    B.tp_reduce_scatter(rows, cols, t, rank, code, list(partials), bias, p_drop, seed, residual_r, out, stream)
     return out
 
 
 def all_gather(slices, out=None, stream=None):
     """The full tensor from the ranks' token slices (Megatron-SP second half)."""
     torch = _torch()
-    rows, cols, dtype = _shape_dtype(slices[0])
+    shape, code, dev = V.group("slices", slices)
+    rows, cols = _rows_cols(shape)
+    full = (rows * len(slices),) + tuple(shape[1:])
     if out is None:
-        out = torch.empty((rows * len(slices),) + tuple(slices[0].shape[1:]), dtype=slices[0].dtype,
-                          device=slices[0].device)
-    B.tp_all_gather(rows, cols, len(slices), dtype, list(slices), out, stream)
+        out = torch.empty(full, dtype=slices[0].dtype, device=dev)
+    V.like("out", out, full, slices[0].dtype, dev)
+    B.tp_all_gather(rows, cols, len(slices), code, list(slices), out, stream)
     return out

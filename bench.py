@@ -34,6 +34,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+from attention_column_gemm_amd import flops as F  # noqa: E402
+
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E bandwidth (published)
 METRIC = "per-rank TP MLP fwd+bwd TFLOP/s and % of bf16 MFMA peak on 1 MI355X"
@@ -91,7 +93,7 @@ def kernel_plan(mc, ac):
     if ac is not None:
         Ta, ha, q, kv, dh = ac.tokens, ac.h, ac.q, ac.kv, ac.d
         plan += [("attn_qkv_gemm", "a8", 2 * Ta * ha * (q + 2 * kv) * dh, None),
-                 ("attn_core", "a8", 4 * dh * ac.b * q * (ac.s * (ac.s + 1) // 2), None),
+                 ("attn_core", "a8", F.attn_core(ac.b, ac.s, q, dh), None),
                  ("attn_out_gemm", "a8", 2 * Ta * q * dh * ha, None),
                  ("allreduce_attn_sum", "a3", None, (ac.t + 1) * Ta * ha * 2)]
     n1 = 1 if mc.act == "gelu" else 2
@@ -120,7 +122,7 @@ def kernel_plan(mc, ac):
     if ac is not None:
         # attention backward: algorithmic FLOPs per kernel (the score and dP
         # recomputations are not counted): dK/dV do dP, dV and dK, dQ does dQ
-        pairs = ac.b * q * (ac.s * (ac.s + 1) // 2)
+        pairs = ac.b * q * F.causal_pairs(ac.s)
         # dO with dWo, and dWqkv with dX, run as paired launches
         plan += [("attn_bwd_dO_dWo_gemm", "f1", 2 * 2 * Ta * ha * q * dh, None),
                  ("attn_bwd_stats", "f1", None, 2 * Ta * q * dh * 2 + ac.b * q * ac.s * 12),
@@ -207,24 +209,43 @@ def time_uneven_shards(torch, reps=5):
     ash.load(g(b * s, h, std=1.0), g(h, (ash.q + 2 * ash.kv) * d), g(ash.q * d, h))
     dZ = to_device(g(b * s, h, std=1.0), "bf16")
     ms = timed(lambda: (ash.forward(), ash.backward(dZ)))
-    ac = I.custom_attn(0, b, s, h, n_q, n_kv, d, t)
-    fl = 3 * (2 * b * s * h * (ash.q + 2 * ash.kv) * d + 2 * b * s * ash.q * d * h
-              + 4 * d * b * ash.q * (s * (s + 1) // 2))
+    fl = 3 * F.attn_shard_fwd(b, s, h, ash.q, ash.kv, d)
     out.append({"case": f"attention {n_q}q/{n_kv}kv d={d} over t={t} (KV replicated on 2 ranks), rank 0 "
                         f"(q={ash.q}, kv={ash.kv})", "row": "f4", "avg_ms": round(ms, 4),
                 "tflops": round(fl / (ms * 1e-3) / 1e12, 2)})
     return out
 
 
+def host_identity():
+    """The host the CPU baseline ran on: logical CPUs, the CPUs this process
+    may use, the CPU model, and the BLAS threads numpy's BLAS runs."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        pass
+    return {"nproc": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": model, "blas_threads": blas}
+
+
 def cpu_baseline(mc, X, dOut, w, budget_s=12.0):
     """The float64 oracle on a bounded token slice of the same rank-0 shard."""
     import numpy as np
     from oracle import mlp as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    host = host_identity()
     W = {k: (None if v is None else np.asarray(v, dtype=np.float64)) for k, v in w.items()}
     n, elapsed = 16, 0.0
     while True:
@@ -235,11 +256,74 @@ def cpu_baseline(mc, X, dOut, w, budget_s=12.0):
         if elapsed * 2 > budget_s or n * 2 > mc.tokens:
             break
         n *= 2
-    k = 12 if mc.act == "gelu" else 18
-    flops = k * n * mc.h * mc.f
+    flops = F.mlp_shard(n, mc.h, mc.f, mc.act)
+    cores = host["blas_threads"] or host["affinity_cpus"] or host["nproc"] or 1
     return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"rank-0 MLP shard fwd+bwd of workload {mc.cfg} on its first {n} of {mc.tokens} tokens "
-                      f"(all weights; {flops / 1e9:.1f} GFLOP in float64 numpy/BLAS, {elapsed:.1f} s)"}
+                      f"(all weights; {flops / 1e9:.1f} GFLOP in float64 numpy/BLAS, {elapsed:.1f} s)",
+            "threads_used": host["blas_threads"], **{k: v for k, v in host.items() if k != "blas_threads"}}
+
+
+def time_mlp_workload(torch, mcid, steps, warmup=3):
+    """MLP shard fwd+bwd of another workload, rank 0, timed like the headline
+    (the span of the forward and backward calls per step, mean over steps)."""
+    from attention_column_gemm_amd import inputs as I
+    from attention_column_gemm_amd.shard import MLPShard
+    mc = I.MLP_CONFIGS[mcid]
+    X, dOut = I.mlp_activation(mc)
+    w = I.mlp_rank_weights(mc, 0)
+    sh = MLPShard(mc.tokens, mc.h, mc.h_ffn, mc.t, 0, act=mc.act, dtype=mc.dtype)
+    sh.load(X, w["W1"], w["Wu"], w["b1"], w["W2"], dOut)
+    run = lambda: (sh.forward(), sh.backward(mc.p_drop, mc.seed, want_db2=mc.bias, want_db1=mc.bias))
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    fl = mc.flops_per_rank()
+    tf = fl / (ms * 1e-3) / 1e12
+    del sh
+    return {"workload": f"{mc.act} MLP shard fwd+bwd, T={mc.tokens} h={mc.h} h_ffn={mc.h_ffn} t={mc.t} "
+                        f"(f={mc.f}), {mc.dtype}, p_drop={mc.p_drop}, bias={mc.bias}, rank 0",
+            "cfg": mcid, "steps": steps, "mlp_ms": round(ms, 4), "flops": fl, "tflops": round(tf, 2),
+            "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+
+
+def tp_record(mc, ac, per_step):
+    """The per-layer record of a TP experiment ([L11] section 6): TP degree
+    and rank, shapes, the layout of every linear, the all-reduces (count,
+    logical payload and dtype) and their time over the timed steps (mean,
+    P95; on one GPU every emulated all-reduce runs alone on the stream, so
+    its whole time is exposed)."""
+    import numpy as np
+    dt = "bf16" if mc.bf16 else "fp32"
+    delta = 2 if mc.bf16 else 4
+    layouts = {"mlp": {"W1 (gate)" if mc.act == "swiglu" else "W1": "column (output dim split, input replicated)",
+                       **({"Wu (up)": "column (output dim split, input replicated)"} if mc.act == "swiglu" else {}),
+                       "W2 (down)" if mc.act == "swiglu" else "W2": "row (input dim split, output partial)"}}
+    if ac is not None:
+        layouts["attention"] = {"Wqkv": f"column by head ({ac.q} q / {ac.kv} kv heads of {ac.n_q} / {ac.n_kv})",
+                                "Wo": "row (input dim split by head, output partial)"}
+    ars = []
+    names = [("allreduce_attn_fwd", "allreduce_attn_fwd", "g after the attention output projection"),
+             ("allreduce_fwd", "allreduce_fwd", "g after the MLP down/W2 projection"),
+             ("allreduce_bwd", "allreduce_bwd", "f at the MLP input (sum of dX_i)"),
+             ("allreduce_attn_bwd", "allreduce_attn_bwd", "f at the attention input (sum of dX_i)")]
+    for label, key, where in names:
+        if key not in per_step:
+            continue
+        v = np.asarray(per_step[key])
+        ars.append({"where": where, "payload_bytes": mc.tokens * mc.h * delta, "dtype": dt,
+                    "mean_ms": round(float(v.mean()), 5), "p95_ms": round(float(np.percentile(v, 95)), 5),
+                    "exposed_ms": round(float(v.mean()), 5)})
+    return {"t": mc.t, "rank": 0, "tokens": mc.tokens, "h": mc.h, "h_ffn": mc.h_ffn,
+            "layouts": layouts, "allreduce_dtype": dt,
+            "allreduces_per_layer": 4 if ac is not None else 2, "allreduces": ars}
 
 
 def load_traffic(kernel_label, workload):
@@ -339,9 +423,10 @@ def main():
         if attn is not None:
             e0 = ev(); e0.record()
             attn.forward(want_lse=True)
-            sum_partials([attn.Z] + za_others, None, 0.0, 0, out=zasum)
             e1 = ev(); e1.record()
-            marks.append(("attention_fwd_and_allreduce", e0, e1))
+            sum_partials([attn.Z] + za_others, None, 0.0, 0, out=zasum)
+            e2 = ev(); e2.record()
+            marks += [("attention_fwd", e0, e1), ("allreduce_attn_fwd", e1, e2)]
         e0 = ev(); e0.record()
         mlp.forward()
         e1 = ev(); e1.record()
@@ -392,11 +477,11 @@ def main():
         for i in range(nk):
             kern_ms[i] += hip.elapsed_ms(kev[2 * i], kev[2 * i + 1])
     kern_ms /= args.steps
-    span = {}
+    per_step = {}
     for marks in all_marks:
         for name, a, b in marks:
-            span[name] = span.get(name, 0.0) + a.elapsed_time(b)
-    span = {k: v / args.steps for k, v in span.items()}
+            per_step.setdefault(name, []).append(a.elapsed_time(b))
+    span = {k: sum(v) / len(v) for k, v in per_step.items()}
 
     mlp_flops = mc.flops_per_rank()
     mlp_ms = span["mlp_fwd"] + span["mlp_bwd"]
@@ -456,12 +541,13 @@ def main():
         "roofline": roof,
         "comm": {"n_allreduce_per_layer": comm.n_allreduce_fwd + comm.n_allreduce_bwd,
                  "payload_bytes": comm.payload_bytes, "ring_bytes_per_rank": comm.ring_bytes_per_rank},
+        "tp_record": tp_record(mc, ac, per_step),
         "wall_s_timed": round(wall, 3),
         "source_hash": source_hash(),
     }
     if attn is not None:
         af = I.ATTN_CONFIGS[acid].flops_per_rank()
-        res["attention_fwd_tflops"] = round(af / (span["attention_fwd_and_allreduce"] * 1e-3) / 1e12, 2)
+        res["attention_fwd_tflops"] = round(af / (span["attention_fwd"] * 1e-3) / 1e12, 2)
         ab = I.ATTN_CONFIGS[acid].flops_bwd_per_rank()
         res["attention_bwd_tflops"] = round(ab / (span["attention_bwd"] * 1e-3) / 1e12, 2)
     if mc.tokens % mc.t == 0 and not args.no_extras:
@@ -470,6 +556,10 @@ def main():
         del attn, mlp, z_others, dx_others, za_others, dxa_others
         torch.cuda.empty_cache()
         res["uneven_shards"] = time_uneven_shards(torch)
+    if args.workload == "cfg5" and not args.no_extras:
+        log("[bench] other workloads' MLP fwd+bwd")
+        res["other_workloads"] = [time_mlp_workload(torch, 3, args.steps), time_mlp_workload(torch, 2, args.steps)]
+        torch.cuda.empty_cache()
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 2
         src = torch.empty(n, dtype=torch.bfloat16, device="cuda").fill_(1.0)

@@ -22,9 +22,16 @@
  *    orientation of [L11] section 1).
  *  - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
  *    aligned.  A tensor with no elements may be passed as NULL.  The library
- *    never allocates, frees or keeps device memory, and holds no state
- *    between calls other than the profiling hook of tp_profile_arm.
- *    Outputs may not alias inputs.
+ *    never allocates, frees or keeps device memory.  Outputs may not alias
+ *    inputs.
+ *  - Process-wide inputs, the only state kept between calls (the environment
+ *    is never read):
+ *      * the launch options of tp_set_options (tile shape, splits), which
+ *        change how work is divided, never what is computed beyond rounding
+ *        order; default TP_TILE_AUTO with splits on;
+ *      * the profiling hook of tp_profile_arm (events only, no results).
+ *    Both are safe to set and read from several threads; a call made while
+ *    another thread changes the options uses either the old or the new ones.
  *  - Storage type: TP_F32 means every activation, weight and bias is fp32;
  *    TP_BF16 means they are bf16 (products accumulate in fp32).  Weight and
  *    bias gradients (dW*, db*) are always fp32.
@@ -61,6 +68,14 @@ enum {
   TP_EHIP = -5,         /* the HIP runtime reported an error when enqueuing a kernel */
   TP_EUNSUPPORTED = -6  /* a size the kernels do not implement (head width other than 64 or 128, t > 64,
                            an attention shard with s >= 2^24 or a QKV row of 2^24 bytes or more) */
+};
+
+/* Tile shape of the matrix-core GEMMs (tp_set_options). */
+enum {
+  TP_TILE_AUTO = 0,   /* chosen per launch from the tile count (the default) */
+  TP_TILE_LARGE = 1,  /* 256 x 256 (256 x 128 with two B operands), eight waves */
+  TP_TILE_SMALL = 2,  /* 128 x 128 (128 x 64), four waves */
+  TP_TILE_TINY = 3    /* 64 x 64 for single-B launches, else as TP_TILE_SMALL */
 };
 
 /* One rank's MLP shard. */
@@ -342,10 +357,29 @@ int tp_comm_bytes(int64_t tokens, int64_t h, int32_t t, int32_t delta, tp_comm* 
  * even and at most 64.  Each of the next n_events/2 kernels the library
  * enqueues records events[2i] just before and events[2i+1] just after kernel i,
  * on that kernel's stream; after that the hook is idle again.  n_events = 0
- * disarms it.  Process-wide and not thread-safe (one profiling client).
+ * disarms it.  Process-wide: with several threads launching, each kernel
+ * claims the next free pair under a lock, so which kernel gets which pair
+ * follows the order the launches happen in.
  * Returns TP_EINVAL for an odd or out-of-range count or a NULL handle.
  */
 int tp_profile_arm(void* const* events, int32_t n_events);
+
+/*
+ * tp_set_options -- process-wide launch options of every later call (host only).
+ *   tile        TP_TILE_AUTO, or a tile shape every bf16 GEMM then takes
+ *   split_tail  1 (default): a GEMM whose last round of tiles is at most half
+ *               full splits it (over K into a caller buffer that the entry
+ *               point documents as scratch, or over N in a paired launch), and
+ *               the attention kernels split their heaviest causal blocks;
+ *               0: no splits.
+ * The results are the same either way up to fp32 rounding order (paired
+ * half-width tails are bit-identical).  Returns TP_EINVAL for values outside
+ * these ranges (the options are then unchanged).
+ */
+int tp_set_options(int32_t tile, int32_t split_tail);
+
+/* tp_get_options -- the current options; TP_EINVAL for a NULL output. */
+int tp_get_options(int32_t* tile, int32_t* split_tail);
 
 /* Human-readable name of a status code (static string; never NULL). */
 const char* tp_status_string(int status);

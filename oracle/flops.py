@@ -29,11 +29,18 @@ def mlp_shard(tokens: int, h: int, f: int, act: str) -> dict:
     return dict(fwd=fwd, bwd=bwd, total=fwd + bwd)
 
 
+def attention_pairs(s: int, causal: bool = True) -> int:
+    """(query, key) pairs of one sequence and head that the mask leaves
+    visible: every key at or before the query (``1 + 2 + ... + s``) under the
+    causal mask, all ``s^2`` without it."""
+    return s * (s + 1) // 2 if causal else s * s
+
+
 def attention_shard_fwd(b: int, s: int, h: int, q: int, kv: int, d: int, causal: bool = True) -> dict:
     """Per-rank forward FLOPs: QKV GEMM, core (QK^T and PV over the key/query
     pairs actually computed) and the output projection."""
     T = b * s
-    pairs = s * (s + 1) // 2 if causal else s * s
+    pairs = attention_pairs(s, causal)
     qkv = gemm(T, h, (q + 2 * kv) * d)
     core = 2 * (2 * d) * b * q * pairs
     out = gemm(T, q * d, h)

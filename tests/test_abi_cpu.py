@@ -225,3 +225,110 @@ def test_status_strings():
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert B.status_string(code).startswith("TP_")
     assert B.status_string(-99) == "unknown status"
+
+
+def test_launch_options_are_explicit_and_validated():
+    """The launch options are set by tp_set_options (the library reads no
+    environment variable); invalid values leave them unchanged."""
+    L = B.lib()
+    saved = B.tp_get_options()
+    try:
+        assert saved == (B.TP_TILE_AUTO, 1) or saved[0] in range(4)
+        for tile in (B.TP_TILE_AUTO, B.TP_TILE_LARGE, B.TP_TILE_SMALL, B.TP_TILE_TINY):
+            for split in (0, 1):
+                B.tp_set_options(tile, split)
+                assert B.tp_get_options() == (tile, split)
+        B.tp_set_options(B.TP_TILE_SMALL, 0)
+        for bad in [(-1, 1), (4, 1), (0, 2), (0, -1)]:
+            assert L.tp_set_options(*bad) == B.TP_EINVAL
+            assert B.tp_get_options() == (B.TP_TILE_SMALL, 0)
+        a = ctypes.c_int32()
+        assert L.tp_get_options(None, ctypes.byref(a)) == B.TP_EINVAL
+        assert L.tp_get_options(ctypes.byref(a), None) == B.TP_EINVAL
+        with B.options(tile=B.TP_TILE_LARGE):
+            assert B.tp_get_options() == (B.TP_TILE_LARGE, 0)
+        assert B.tp_get_options() == (B.TP_TILE_SMALL, 0)
+    finally:
+        B.tp_set_options(*saved)
+    lib_bytes = open(B.LIB_PATH, "rb").read()
+    assert b"TPSHARD_TILE" not in lib_bytes and b"TPSHARD_SPLIT_TAIL" not in lib_bytes
+
+
+def test_profile_arm_validation():
+    L = B.lib()
+    arr = (ctypes.c_void_p * 4)(1, 2, 3, 4)
+    assert L.tp_profile_arm(arr, 3) == B.TP_EINVAL          # odd
+    assert L.tp_profile_arm(arr, 66) == B.TP_EINVAL         # too many
+    assert L.tp_profile_arm(None, 2) == B.TP_EINVAL
+    bad = (ctypes.c_void_p * 2)(1, None)
+    assert L.tp_profile_arm(bad, 2) == B.TP_EINVAL
+    assert L.tp_profile_arm(None, 0) == B.TP_OK             # disarm
+
+
+# ---------------------------------------------------------------- validation
+
+def test_tensor_validation_on_cpu_tensors():
+    """The host-side checks the binding and the shard wrappers make before any
+    launch: storage type, contiguity, device and shape agreement, and the
+    element count every raw-pointer argument must hold."""
+    import torch
+    from attention_column_gemm_amd import validate as V
+    bf = lambda *s: torch.zeros(*s, dtype=torch.bfloat16)
+    f32 = lambda *s: torch.zeros(*s, dtype=torch.float32)
+    assert V.storage_code(torch.bfloat16) == B.TP_BF16 and V.storage_code(torch.float32) == B.TP_F32
+    for dt in (torch.float16, torch.float64, torch.int32):
+        with pytest.raises(TypeError):
+            V.storage_code(dt)
+    assert V.group("p", [bf(4, 8), bf(4, 8)]) == ((4, 8), B.TP_BF16, torch.device("cpu"))
+    with pytest.raises(TypeError):
+        V.group("p", [torch.zeros(4, 8, dtype=torch.float16)] * 2)          # fp16 is not fp32
+    with pytest.raises(TypeError):
+        V.group("p", [bf(4, 8), f32(4, 8)])                                 # mixed storage
+    with pytest.raises(ValueError):
+        V.group("p", [bf(4, 8), bf(4, 16)])                                 # a short partial
+    with pytest.raises(ValueError):
+        V.group("p", [bf(8, 4).t(), bf(4, 8)])                              # non-contiguous view
+    with pytest.raises(ValueError):
+        V.group("p", [])
+    V.vector("bias", bf(8), 8, torch.bfloat16, torch.device("cpu"))
+    with pytest.raises(ValueError):
+        V.vector("bias", bf(7), 8, torch.bfloat16, torch.device("cpu"))
+    with pytest.raises(TypeError):
+        V.vector("bias", f32(8), 8, torch.bfloat16, torch.device("cpu"))
+    V.like("res", None, (4, 8), torch.bfloat16, torch.device("cpu"))
+    with pytest.raises(ValueError):
+        V.like("res", None, (4, 8), torch.bfloat16, torch.device("cpu"), optional=False)
+    with pytest.raises(ValueError):
+        V.like("res", bf(2, 8), (4, 8), torch.bfloat16, torch.device("cpu"))
+    V.at_least("x", bf(64), 64, B.TP_BF16)
+    V.at_least("x", 0x1000, 10 ** 9, B.TP_BF16)                            # raw addresses pass
+    with pytest.raises(ValueError):
+        V.at_least("x", bf(63), 64, B.TP_BF16)
+    with pytest.raises(TypeError):
+        V.at_least("x", f32(64), 64, B.TP_BF16)
+    with pytest.raises(TypeError):
+        V.at_least_f32("dW", bf(64), 64)
+
+
+def test_binding_rejects_short_or_mistyped_tensors_before_the_call():
+    """The binding checks torch tensors against the sizes the descriptor
+    implies before calling the library (CPU tensors: the check fires before
+    the device check of the pointer marshalling)."""
+    import torch
+    desc = B.mlp_desc(16, 32, 64, 2, 0, B.TP_BF16, B.TP_GELU)
+    bf = lambda n: torch.zeros(n, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="X"):
+        B.tp_mlp_shard_fwd(desc, bf(16 * 32 - 1), None, None, None, None, None, None, None)
+    with pytest.raises(TypeError, match="W1_i"):
+        B.tp_mlp_shard_fwd(desc, bf(16 * 32), torch.zeros(32 * 32, dtype=torch.float16), None, None, None, None,
+                           None, None)
+    with pytest.raises(ValueError, match=r"partials\[1\]"):
+        B.tp_sum_partials(4, 8, 2, B.TP_BF16, [bf(32), bf(31)], None, 0.0, 0, None)
+    with pytest.raises(TypeError, match=r"partials\[0\]"):
+        B.tp_sum_partials(4, 8, 1, B.TP_BF16, [torch.zeros(32, dtype=torch.float16)], None, 0.0, 0, None)
+    with pytest.raises(ValueError, match="out_r"):
+        B.tp_reduce_scatter(4, 8, 2, 0, B.TP_BF16, [bf(32), bf(32)], None, 0.0, 0, None, bf(15))
+    ad = B.attn_desc(1, 16, 32, 4, 2, 64, 2, 0)
+    with pytest.raises(ValueError, match="stats_i"):
+        B.tp_attn_shard_bwd(ad, None, None, None, None, None, None, None, None,
+                            torch.zeros(2 * 2 * 16 - 1), None, None, None, None)

@@ -55,3 +55,28 @@ def test_kernel_plan_matches_the_paired_launches():
     c = I.MLP_CONFIGS[5]
     total = sum(p[2] or 0 for p in bench.kernel_plan(c, None) if p[0].startswith("mlp_"))
     assert total == c.flops_per_rank()
+
+
+def test_tp_record_fields():
+    """[L11] section 6's record: layouts per linear, all-reduce count, payload,
+    dtype, mean and P95 time."""
+    from attention_column_gemm_amd import inputs as I
+    bench = _bench_module()
+    steps = {"allreduce_attn_fwd": [0.2, 0.21, 0.25], "allreduce_fwd": [0.2, 0.2, 0.2],
+             "allreduce_bwd": [0.1, 0.3, 0.2], "allreduce_attn_bwd": [0.2] * 3}
+    r = bench.tp_record(I.MLP_CONFIGS[5], I.ATTN_CONFIGS[5], steps)
+    assert r["allreduces_per_layer"] == 4 and len(r["allreduces"]) == 4
+    assert r["allreduce_dtype"] == "bf16"
+    assert set(r["layouts"]) == {"mlp", "attention"}
+    assert "column" in r["layouts"]["mlp"]["W1 (gate)"] and "row" in r["layouts"]["mlp"]["W2 (down)"]
+    for a in r["allreduces"]:
+        assert a["payload_bytes"] == 8192 * 8192 * 2 and a["p95_ms"] >= a["mean_ms"] - 1e-12
+    r1 = bench.tp_record(I.MLP_CONFIGS[1], None, {"allreduce_fwd": [1.0], "allreduce_bwd": [2.0]})
+    assert r1["allreduce_dtype"] == "fp32" and r1["allreduces"][0]["payload_bytes"] == 64 * 128 * 4
+
+
+def test_host_identity_fields():
+    bench = _bench_module()
+    h = bench.host_identity()
+    assert h["nproc"] >= 1 and h["affinity_cpus"] >= 1
+    assert set(h) == {"nproc", "affinity_cpus", "cpu_model", "blas_threads"}

@@ -207,7 +207,7 @@ SPLIT_BWD = {
 
 
 @pytest.mark.parametrize("name", list(SPLIT_BWD))
-def test_attention_backward_key_block_split(name, monkeypatch):
+def test_attention_backward_key_block_split(name, lib_options):
     """The causal dK/dV kernel runs its heavier half of key blocks as two
     work-groups each (fp32 halves in dWqkv_i's memory), and dQ its heavier
     half of query blocks as two work-groups over the halves of their keys
@@ -219,7 +219,7 @@ def test_attention_backward_key_block_split(name, monkeypatch):
     c, causal, dq_split = SPLIT_BWD[name]
     got = {}
     for split in ("1", "0"):
-        monkeypatch.setenv("TPSHARD_SPLIT_TAIL", split)
+        lib_options(split_tail=int(split))
         banner(f"attn bwd key split={split} {name}")
         sh, X, w, dZ = _run_bwd(c, 0, causal)
         torch.cuda.synchronize()
@@ -247,7 +247,7 @@ FWD_SPLIT = {
 
 
 @pytest.mark.parametrize("name", list(FWD_SPLIT))
-def test_attention_forward_query_block_split(name, monkeypatch):
+def test_attention_forward_query_block_split(name, lib_options):
     """A causal forward whose launch leaves work-group slots empty runs its
     heavier half of query blocks as two work-groups over the halves of the
     keys (softmax state in Z_i's memory, merged by a second kernel).  O_i,
@@ -258,7 +258,7 @@ def test_attention_forward_query_block_split(name, monkeypatch):
     ref = None
     got = {}
     for split in ("1", "0"):
-        monkeypatch.setenv("TPSHARD_SPLIT_TAIL", split)
+        lib_options(split_tail=int(split))
         banner(f"attn fwd query split={split} {name}")
         sh, X, w = _run(c, 0, causal)
         torch.cuda.synchronize()

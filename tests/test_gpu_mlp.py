@@ -12,6 +12,7 @@ import os
 import numpy as np
 import pytest
 
+from attention_column_gemm_amd import binding as B
 from attention_column_gemm_amd import inputs as I
 from oracle import mlp as O
 from parity import TOL, banner, check, edge_indices, need_gpu
@@ -76,13 +77,13 @@ SMALL = {
 
 @pytest.mark.parametrize("tile", ["auto", "large", "small", "tiny"])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_mlp_all_ranks_full_parity(name, tile, monkeypatch):
+def test_mlp_all_ranks_full_parity(name, tile, lib_options):
     torch = need_gpu()
     c = SMALL[name]
     if tile != "auto":
         if c.dtype == "fp32":
             pytest.skip("tile override applies to the bf16 matrix-core GEMM only")
-        monkeypatch.setenv("TPSHARD_TILE", tile)
+        lib_options(tile={"large": B.TP_TILE_LARGE, "small": B.TP_TILE_SMALL, "tiny": B.TP_TILE_TINY}[tile])
     banner(f"mlp {name} tile={tile} T={c.tokens} h={c.h} h_ffn={c.h_ffn} t={c.t} {c.act} {c.dtype} p={c.p_drop}")
     from attention_column_gemm_amd.shard import sum_partials, to_device
     X, dOut = I.mlp_activation(c)
@@ -210,7 +211,7 @@ SPLIT_CASES = {
 
 
 @pytest.mark.parametrize("name", list(SPLIT_CASES))
-def test_mlp_split_tail_parity(name, monkeypatch):
+def test_mlp_split_tail_parity(name, lib_options):
     """A column GEMM whose last round of large tiles is at most half full runs
     it as two K halves per tile (fp32 partial tiles in Z_i's memory), finished
     by a kernel that adds the halves and runs the SwiGLU epilogue.  Forward
@@ -225,7 +226,7 @@ def test_mlp_split_tail_parity(name, monkeypatch):
     fw = O.shard_forward(X, w["W1"], w["W2"], act=c.act, Wu_i=w["Wu"])
     outs = {}
     for split in ("1", "0"):
-        monkeypatch.setenv("TPSHARD_SPLIT_TAIL", split)
+        lib_options(split_tail=int(split))
         banner(f"mlp split tail={split} T={c.tokens} h={c.h} f={c.f}")
         sh = MLPShard(c.tokens, c.h, c.h_ffn, c.t, 0, act=c.act, dtype=c.dtype)
         sh.load(X, w["W1"], w["Wu"], w["b1"], w["W2"], dOut)
@@ -254,7 +255,7 @@ PAIR_TAIL_CASES = {
 
 
 @pytest.mark.parametrize("name", list(PAIR_TAIL_CASES))
-def test_mlp_pair_half_width_tail_parity(name, monkeypatch):
+def test_mlp_pair_half_width_tail_parity(name, lib_options):
     """A paired backward launch whose last round of large tiles is at most
     half full runs problem 2's last tile rows as 256 x 128 tiles.  Every
     output against the oracle with the tail on and off; each output element
@@ -267,7 +268,7 @@ def test_mlp_pair_half_width_tail_parity(name, monkeypatch):
     fw, bw = O.shard_step(dOut, X, w["W1"], w["W2"], act=c.act, Wu_i=w["Wu"], b1_i=w["b1"], p=c.p_drop, seed=c.seed)
     runs = {}
     for split in ("1", "0"):
-        monkeypatch.setenv("TPSHARD_SPLIT_TAIL", split)
+        lib_options(split_tail=int(split))
         banner(f"mlp pair tail={split} {name}")
         sh = _gpu_rank(c, 0, X, dOut, w)
         torch.cuda.synchronize()

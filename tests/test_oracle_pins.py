@@ -728,3 +728,62 @@ def test_flops_match_page_totals():
     assert a["total"] == 8 * B * S * d * d + 4 * B * S * S * d
     ab = flops.attention_shard_bwd(B, S, d, heads, heads, dh, causal=False)
     assert ab["total"] == 16 * B * S * d * d + 8 * B * S * S * d
+
+
+@pytest.mark.parametrize("s", [1, 2, 3, 5, 8, 17, 64])
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_pair_count_brute_force(s, causal):
+    """The pairs the attention core is credited with ([HJ] Attention: QK^T and
+    PV are 2 d FLOPs per computed pair) are the pairs the oracle's mask leaves
+    visible.  Counted two ways that do not use the closed form: a loop over
+    (query, key) positions, and the oracle's own attention with Q = 0, whose
+    uniform weights make exp(lse) the number of visible keys of each row."""
+    loop = sum(1 for sq in range(s) for sk in range(s) if (sk <= sq or not causal))
+    g = _rng(900 + s)
+    b, d = 2, 4
+    K, V = g.standard_normal((b * s, d)), g.standard_normal((b * s, d))
+    _, lse = att.core(np.zeros((b * s, d)), K, V, b=b, s=s, n_q=1, n_kv=1, d=d, causal=causal)
+    counted = np.exp(lse)
+    assert np.allclose(counted, np.rint(counted), atol=1e-9)
+    per_seq = int(np.rint(counted).sum()) // b
+    assert per_seq == loop
+    assert flops.attention_pairs(s, causal) == loop
+    q, dh = 3, 8
+    core = flops.attention_shard_fwd(b, s, 16, q, 1, dh, causal)["core"]
+    assert core == 4 * dh * b * q * loop
+    # the product side's accounting (bench and the workload tables) counts the same pairs
+    from attention_column_gemm_amd import flops as PF
+    assert PF.causal_pairs(s, causal) == loop
+    assert PF.attn_core(b, s, q, dh, causal) == core
+    assert PF.attn_shard_fwd(b, s, 16, q, 1, dh, causal) == flops.attention_shard_fwd(b, s, 16, q, 1, dh,
+                                                                                         causal)["total"]
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_product_side_mlp_flops_match_oracle(act):
+    from attention_column_gemm_amd import flops as PF
+    for T, h, f in [(5, 6, 8), (8192, 8192, 3584), (4096, 4096, 1376)]:
+        assert PF.mlp_shard(T, h, f, act) == flops.mlp_shard(T, h, f, act)["total"]
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+@pytest.mark.parametrize("t", [2, 4])
+def test_missing_rank_fails_the_sum_invariant(act, t):
+    """Negative test of the Sigma-invariant ([L11] sections 2-3; [TP1]
+    operators f and g): leaving any one rank's partial Z_i out of the forward
+    sum, or its dX_i out of the backward sum, no longer gives the unsharded
+    result, while the complete sums do."""
+    c = _mlp_case(40 + t, act=act, bias=False)
+    full = mlp.backward(c["dOut"], c["X"], c["W1"], c["W2"], act=act, Wu=c["Wu"])
+    Zs, dXs = [], []
+    for s in _shards(c, t, act):
+        fw, bw = mlp.shard_step(c["dOut"], c["X"], s["W1"], s["W2"], act=act, Wu_i=s["Wu"])
+        Zs.append(fw["Z"])
+        dXs.append(bw["dX"])
+    rel = lambda a, b: np.abs(a - b).max() / np.abs(b).max()
+    assert rel(mlp.sum_partials(Zs), full["fwd"]["Out"]) < 1e-12
+    assert rel(mlp.sum_partials(dXs), full["dX"]) < 1e-12
+    for miss in range(t):
+        keep = [i for i in range(t) if i != miss]
+        assert rel(mlp.sum_partials([Zs[i] for i in keep]), full["fwd"]["Out"]) > 1e-3, miss
+        assert rel(mlp.sum_partials([dXs[i] for i in keep]), full["dX"]) > 1e-3, miss
