@@ -787,3 +787,112 @@ def test_missing_rank_fails_the_sum_invariant(act, t):
         keep = [i for i in range(t) if i != miss]
         assert rel(mlp.sum_partials([Zs[i] for i in keep]), full["fwd"]["Out"]) > 1e-3, miss
         assert rel(mlp.sum_partials([dXs[i] for i in keep]), full["dX"]) > 1e-3, miss
+
+
+# ------------------------------------------------- norm on the token slice
+
+def _norm_loops(x, kind, gamma, beta, eps):
+    """Pure-Python loops, one token at a time, from the definitions."""
+    out = []
+    for row in x.tolist():
+        n = len(row)
+        if kind == "rms":
+            ms = sum(v * v for v in row) / n
+            r = 1.0 / math.sqrt(ms + eps)
+            out.append([row[j] * r * gamma[j] for j in range(n)])
+        else:
+            mu = sum(row) / n
+            var = sum((v - mu) ** 2 for v in row) / n
+            r = 1.0 / math.sqrt(var + eps)
+            out.append([(row[j] - mu) * r * gamma[j] + beta[j] for j in range(n)])
+    return np.array(out)
+
+
+@pytest.mark.parametrize("kind", ["rms", "layer"])
+def test_norm_brute_force(kind):
+    g = _rng(50)
+    x = g.standard_normal((5, 7)) * 3 + 1
+    gamma, beta = g.standard_normal(7), g.standard_normal(7)
+    eps = 1e-3
+    got = sp.norm(x, kind, gamma, beta if kind == "layer" else None, eps)
+    ref = _norm_loops(x, kind, gamma, beta if kind == "layer" else np.zeros(7), eps)
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_norm_closed_forms():
+    """[3, 4, 0, 0]: RMS 2.5, so RMSNorm gives [1.2, 1.6, 0, 0]; mean 1.75 and
+    variance 3.1875 for LayerNorm.  A constant row c maps to sign(c) gamma
+    under RMSNorm (eps = 0) and to beta under LayerNorm.  RMSNorm of a
+    zero-mean row is LayerNorm's with beta = 0."""
+    x = np.array([[3.0, 4.0, 0.0, 0.0]])
+    np.testing.assert_allclose(sp.rms_norm(x, eps=0.0), [[1.2, 1.6, 0.0, 0.0]], rtol=1e-15)
+    ln = sp.layer_norm(x, eps=0.0)
+    np.testing.assert_allclose(ln, (x - 1.75) / math.sqrt(3.1875), rtol=1e-14)
+    gamma, beta = np.array([1.0, -2.0, 0.5, 3.0]), np.array([0.1, 0.2, -0.3, 0.4])
+    for c in (2.5, -0.75):
+        row = np.full((1, 4), c)
+        np.testing.assert_allclose(sp.rms_norm(row, gamma, eps=0.0), [np.sign(c) * gamma], rtol=1e-15)
+        np.testing.assert_array_equal(sp.layer_norm(row, gamma, beta, eps=1e-5), [beta])
+    g = _rng(51)
+    z = g.standard_normal((3, 6))
+    z -= z.mean(axis=1, keepdims=True)
+    np.testing.assert_allclose(sp.rms_norm(z, gamma=np.arange(6.0), eps=1e-4),
+                               sp.layer_norm(z, gamma=np.arange(6.0), eps=1e-4), rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("kind", ["rms", "layer"])
+def test_norm_invariants(kind):
+    """Scale invariance norm(c x) = norm(x) for c > 0 (eps = 0); unit RMS
+    (RMSNorm) or zero mean and unit variance (LayerNorm) with gamma = 1."""
+    g = _rng(52)
+    x = g.standard_normal((4, 32)) + 0.5
+    for c in (0.01, 3.0, 1e4):
+        np.testing.assert_allclose(sp.norm(c * x, kind, eps=0.0), sp.norm(x, kind, eps=0.0), rtol=1e-12)
+    y = sp.norm(x, kind, eps=0.0)
+    if kind == "rms":
+        np.testing.assert_allclose(np.sqrt((y * y).mean(axis=1)), 1.0, rtol=1e-13)
+    else:
+        np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-14)
+        np.testing.assert_allclose(y.var(axis=1), 1.0, rtol=1e-13)
+
+
+def test_norm_matches_torch_reference_routines():
+    """Special cases that reduce to library routines: torch's layer_norm and
+    rms_norm in float64 on the CPU."""
+    import torch
+    g = _rng(53)
+    x = g.standard_normal((6, 40)) * 2
+    gamma, beta = g.standard_normal(40), g.standard_normal(40)
+    tx = torch.from_numpy(x)
+    ln = torch.nn.functional.layer_norm(tx, (40,), torch.from_numpy(gamma), torch.from_numpy(beta), eps=1e-5)
+    np.testing.assert_allclose(sp.layer_norm(x, gamma, beta, 1e-5), ln.numpy(), rtol=1e-12, atol=1e-12)
+    rn = torch.nn.functional.rms_norm(tx, (40,), torch.from_numpy(gamma), eps=1e-6)
+    np.testing.assert_allclose(sp.rms_norm(x, gamma, 1e-6), rn.numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("kind", ["rms", "layer"])
+def test_norm_on_slices_equals_norm_of_the_all_reduce(kind):
+    """[LP] III.III: the token-wise norm on each rank's slice, then the
+    all-gather, gives the norm of the full all-reduce, element for element;
+    the residual slices gather to the full block output."""
+    g = _rng(54)
+    for t in (1, 2, 4):
+        P, b, R = _partials(55 + t, t=t, T=6 * t, h=20)
+        gamma, beta = g.standard_normal(20), (g.standard_normal(20) if kind == "layer" else None)
+        T = P[0].shape[0]
+        for p in (0.0, 0.2):
+            full_out, full_n = sp.sum_partials_norm(P, b, p, 9, R, kind, gamma, beta, 1e-5)
+            outs, normeds = [], []
+            for r in range(t):
+                rows = sp.slice_rows(T, t, r)
+                o, n = sp.reduce_scatter_norm(P, t, r, b, p, 9, R[rows], kind, gamma, beta, 1e-5)
+                outs.append(o)
+                normeds.append(n)
+            np.testing.assert_array_equal(sp.all_gather(outs), full_out)
+            np.testing.assert_array_equal(sp.all_gather(normeds), full_n)
+            np.testing.assert_allclose(full_n, sp.norm(sp.sum_partials_residual(P, b, p, 9, R), kind, gamma, beta,
+                                                       1e-5), rtol=0, atol=0)
+    with pytest.raises(ValueError):
+        sp.norm(np.ones((1, 3)), "rms", None, np.ones(3))
+    with pytest.raises(ValueError):
+        sp.norm(np.ones((1, 3)), "batch")
