@@ -26,6 +26,7 @@ TP_F32, TP_BF16 = 0, 1
 TP_GELU, TP_SWIGLU = 0, 1
 TP_OK, TP_EINVAL, TP_ENOTDIV, TP_EDTYPE, TP_EALIGN, TP_EHIP, TP_EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
 TP_TILE_AUTO, TP_TILE_LARGE, TP_TILE_SMALL, TP_TILE_TINY = 0, 1, 2, 3
+TP_NORM_RMS, TP_NORM_LAYER = 0, 1
 
 
 class TPError(RuntimeError):
@@ -75,6 +76,13 @@ def lib() -> ctypes.CDLL:
         L.tp_reduce_scatter.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.POINTER(_VP), _VP, ctypes.c_float, ctypes.c_uint64,
                                         _VP, _VP, _VP]
+        L.tp_sum_partials_norm.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.POINTER(_VP), _VP, ctypes.c_float, ctypes.c_uint64, _VP,
+                                           ctypes.c_int32, _VP, _VP, ctypes.c_float, _VP, _VP, _VP]
+        L.tp_reduce_scatter_norm.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.POINTER(_VP), _VP, ctypes.c_float,
+                                             ctypes.c_uint64, _VP, ctypes.c_int32, _VP, _VP, ctypes.c_float, _VP,
+                                             _VP, _VP]
         L.tp_all_gather.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.POINTER(_VP), _VP, _VP]
         L.tp_mlp_shard_cols.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -89,7 +97,7 @@ def lib() -> ctypes.CDLL:
         L.tp_status_string.restype = ctypes.c_char_p
         for name in ("tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_attn_shard_fwd", "tp_attn_shard_bwd",
                      "tp_sum_partials", "tp_sum_partials_residual", "tp_reduce_scatter", "tp_all_gather",
-                     "tp_mlp_shard_cols", "tp_attn_shard_heads", "tp_comm_bytes", "tp_set_options",
+                     "tp_sum_partials_norm", "tp_reduce_scatter_norm", "tp_mlp_shard_cols", "tp_attn_shard_heads", "tp_comm_bytes", "tp_set_options",
                      "tp_get_options", "tp_profile_arm"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -247,6 +255,30 @@ def tp_reduce_scatter(rows: int, cols: int, t: int, rank: int, dtype: int, parti
     _check(lib().tp_reduce_scatter(int(rows), int(cols), int(t), int(rank), int(dtype), arr, _ptr(bias),
                                    float(p_drop), int(seed) & (2 ** 64 - 1), _ptr(residual_r), _ptr(out_r),
                                    _stream(stream)), "tp_reduce_scatter")
+
+
+def tp_sum_partials_norm(rows: int, cols: int, t: int, dtype: int, partials, bias, p_drop: float, seed: int,
+                         residual, norm: int, gamma, beta, eps: float, out, normed, stream=None):
+    _need_list(dtype, "partials", partials, rows * cols)
+    _need(dtype, bias=(bias, cols), residual=(residual, rows * cols), gamma=(gamma, cols), beta=(beta, cols),
+          out=(out, rows * cols), normed=(normed, rows * cols))
+    arr = (_VP * max(1, len(partials)))(*[_ptr(p) for p in partials])
+    _check(lib().tp_sum_partials_norm(int(rows), int(cols), int(t), int(dtype), arr, _ptr(bias), float(p_drop),
+                                      int(seed) & (2 ** 64 - 1), _ptr(residual), int(norm), _ptr(gamma), _ptr(beta),
+                                      float(eps), _ptr(out), _ptr(normed), _stream(stream)), "tp_sum_partials_norm")
+
+
+def tp_reduce_scatter_norm(rows: int, cols: int, t: int, rank: int, dtype: int, partials, bias, p_drop: float,
+                           seed: int, residual_r, norm: int, gamma, beta, eps: float, out_r, normed_r, stream=None):
+    _need_list(dtype, "partials", partials, rows * cols)
+    n = rows // t if t > 0 else 0
+    _need(dtype, bias=(bias, cols), residual_r=(residual_r, n * cols), gamma=(gamma, cols), beta=(beta, cols),
+          out_r=(out_r, n * cols), normed_r=(normed_r, n * cols))
+    arr = (_VP * max(1, len(partials)))(*[_ptr(p) for p in partials])
+    _check(lib().tp_reduce_scatter_norm(int(rows), int(cols), int(t), int(rank), int(dtype), arr, _ptr(bias),
+                                        float(p_drop), int(seed) & (2 ** 64 - 1), _ptr(residual_r), int(norm),
+                                        _ptr(gamma), _ptr(beta), float(eps), _ptr(out_r), _ptr(normed_r),
+                                        _stream(stream)), "tp_reduce_scatter_norm")
 
 
 def tp_all_gather(rows_per_rank: int, cols: int, t: int, dtype: int, slices, out, stream=None):

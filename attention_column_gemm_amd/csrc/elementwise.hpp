@@ -1,9 +1,10 @@
 // HBM-bound kernels of the shard: the emulated all-reduce (rank-ordered sum
-// of partials, bias once, dropout), dropout backward, and deterministic
-// column sums for the bias gradients.
+// of partials, bias once, dropout, residual), the same fused with the
+// token-wise norm of each row, the all-gather copy, dropout backward, and
+// deterministic column sums for the bias gradients.
 //
-// All three stream 16-byte vectors (8 bf16 or 4 fp32) with grid-stride loops;
-// they do no reuse, so their roofline is HBM bandwidth.
+// They stream 16-byte vectors (8 bf16 or 4 fp32) and do no reuse, so their
+// roofline is HBM bandwidth.
 #pragma once
 
 #include "common.hpp"
@@ -40,6 +41,15 @@ template <> struct Vec<uint16_t> {
     for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
     *reinterpret_cast<u32x4*>(p) = w;
   }
+  // the values as store() writes them (round to nearest even), back in fp32
+  __device__ __forceinline__ static void round(const float (&v)[8], float (&r)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+      r[2 * i] = bf16lo(w);
+      r[2 * i + 1] = bf16hi(w);
+    }
+  }
 };
 template <> struct Vec<float> {
   static constexpr int N = 4;
@@ -53,6 +63,10 @@ template <> struct Vec<float> {
   }
   __device__ __forceinline__ static void store(float* p, const float (&v)[4]) {
     *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  }
+  __device__ __forceinline__ static void round(const float (&v)[4], float (&r)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = v[i];
   }
 };
 
@@ -109,6 +123,124 @@ __global__ void __launch_bounds__(256) sum_partials_kernel(int64_t n_vec, int64_
       for (int j = 0; j < V; ++j) acc[j] += r[j];
     }
     Vec<T>::store(out + e0, acc);
+  }
+}
+
+// Sum of a block's 256 threads' values in a fixed order: a butterfly within
+// each wave, then the four wave sums in wave order (every thread gets the
+// same bits).  `red` holds four floats of LDS; the caller separates two uses
+// of it with a barrier.
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+// Block output and its token-wise norm, one row per work-group of 256
+// threads.  Row r of this call (global row row0 + r):
+//   out    = residual + Dropout(sum_{i<t} P_i + bias)     (as sum_partials_kernel)
+//   normed = norm(out as stored), RMSNorm x / sqrt(mean(x^2) + eps) * gamma
+//            or LayerNorm (x - mean) / sqrt(var + eps) * gamma + beta.
+// Thread j owns vectors j, j + 256, ... of the row (NV of them at most), so
+// the row stays in registers between the sum and the norm; the statistics
+// are fp32 sums in a fixed order (LayerNorm's variance from the mean-free
+// values).  The partials' pointers are already offset to row0.
+template <class T, int NV>
+__global__ void __launch_bounds__(256) sum_norm_kernel(int64_t cols, int t, PartialPtrs P, const T* __restrict__ bias,
+                                                       uint32_t thr, float scale, uint64_t seed, uint64_t idx0,
+                                                       const T* __restrict__ residual, int layer_norm,
+                                                       const T* __restrict__ gamma, const T* __restrict__ beta,
+                                                       float eps, T* __restrict__ out, T* __restrict__ normed) {
+  constexpr int V = Vec<T>::N;
+  __shared__ float red[2][4];
+  const int64_t r = blockIdx.x;
+  const int nvec = (int)(cols / V);
+  const int64_t row_off = r * cols;  // elements
+  float x[NV][V];
+  float s1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = (int)threadIdx.x + i * 256;
+#pragma unroll
+    for (int j = 0; j < V; ++j) x[i][j] = 0.0f;
+    if (v >= nvec) continue;
+    const int64_t e0 = row_off + (int64_t)v * V;
+    const uint32_t off = (uint32_t)v * 16u;
+    float acc[V];
+    for (int i0 = 0; i0 < t; i0 += 8) {  // up to eight partials' loads in flight, summed in rank order
+      const int nb = t - i0 < 8 ? t - i0 : 8;
+      u32x4 w[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k < nb) w[k] = load_once16(reinterpret_cast<const T*>(P.p[i0 + k]) + row_off, off);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (k >= nb) break;
+        float y[V];
+        Vec<T>::unpack(w[k], y);
+#pragma unroll
+        for (int j = 0; j < V; ++j) acc[j] = (i0 + k == 0) ? y[j] : acc[j] + y[j];
+      }
+    }
+    if (bias) {
+      float b[V];
+      Vec<T>::load(bias + (int64_t)v * V, b);
+#pragma unroll
+      for (int j = 0; j < V; ++j) acc[j] += b[j];
+    }
+    if (thr) {
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        acc[j] = dropout_keep(seed, idx0 + (uint64_t)(e0 + j), thr) ? acc[j] * scale : 0.0f;
+    }
+    if (residual) {
+      float y[V];
+      Vec<T>::unpack(load_once16(residual + row_off, off), y);
+#pragma unroll
+      for (int j = 0; j < V; ++j) acc[j] += y[j];
+    }
+    // store, and keep the value as stored (rounded to the storage type)
+    Vec<T>::store(out + e0, acc);
+    Vec<T>::round(acc, x[i]);
+#pragma unroll
+    for (int j = 0; j < V; ++j) s1 += x[i][j];
+  }
+  const float inv_n = 1.0f / (float)cols;
+  float mean = 0.0f;
+  if (layer_norm) {
+    mean = block_sum256(s1, red[0]) * inv_n;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if ((int)threadIdx.x + i * 256 < nvec)
+#pragma unroll
+        for (int j = 0; j < V; ++j) x[i][j] -= mean;
+  }
+  float s2 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int j = 0; j < V; ++j) s2 += x[i][j] * x[i][j];
+  const float rstd = __builtin_amdgcn_rsqf(block_sum256(s2, red[1]) * inv_n + eps);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = (int)threadIdx.x + i * 256;
+    if (v >= nvec) continue;
+    float g[V], y[V];
+    if (gamma) Vec<T>::load(gamma + (int64_t)v * V, g);
+    else
+#pragma unroll
+      for (int j = 0; j < V; ++j) g[j] = 1.0f;
+#pragma unroll
+    for (int j = 0; j < V; ++j) y[j] = x[i][j] * rstd * g[j];
+    if (beta) {
+      float b[V];
+      Vec<T>::load(beta + (int64_t)v * V, b);
+#pragma unroll
+      for (int j = 0; j < V; ++j) y[j] += b[j];
+    }
+    Vec<T>::store(normed + row_off + (int64_t)v * V, y);
   }
 }
 

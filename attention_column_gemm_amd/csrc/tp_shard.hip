@@ -722,6 +722,80 @@ int sum_rows(int64_t rows_total, int64_t row0, int64_t nrows, int64_t cols, int3
   return hip_status(hipGetLastError());
 }
 
+// Largest row the fused norm keeps in registers: 16 vectors per thread of 256.
+constexpr int64_t kNormMaxVecs = 16 * 256;
+
+template <class T, int NV>
+void launch_sum_norm(int64_t nrows, int64_t cols, int t, const PartialPtrs& P, const void* bias, uint32_t thr,
+                     float scale, uint64_t seed, uint64_t idx0, const void* residual, int layer, const void* gamma,
+                     const void* beta, float eps, void* out, void* normed, hipStream_t st) {
+  hipLaunchKernelGGL((sum_norm_kernel<T, NV>), dim3((unsigned)nrows), dim3(256), 0, st, cols, t, P,
+                     static_cast<const T*>(bias), thr, scale, seed, idx0, static_cast<const T*>(residual), layer,
+                     static_cast<const T*>(gamma), static_cast<const T*>(beta), eps, static_cast<T*>(out),
+                     static_cast<T*>(normed));
+}
+
+template <class T>
+void sum_norm_dispatch(int64_t nrows, int64_t cols, int t, const PartialPtrs& P, const void* bias, uint32_t thr,
+                       float scale, uint64_t seed, uint64_t idx0, const void* residual, int layer, const void* gamma,
+                       const void* beta, float eps, void* out, void* normed, hipStream_t st) {
+  const int64_t per = (cols / Vec<T>::N + 255) / 256;
+  if (per <= 1)
+    launch_sum_norm<T, 1>(nrows, cols, t, P, bias, thr, scale, seed, idx0, residual, layer, gamma, beta, eps, out,
+                          normed, st);
+  else if (per <= 2)
+    launch_sum_norm<T, 2>(nrows, cols, t, P, bias, thr, scale, seed, idx0, residual, layer, gamma, beta, eps, out,
+                          normed, st);
+  else if (per <= 4)
+    launch_sum_norm<T, 4>(nrows, cols, t, P, bias, thr, scale, seed, idx0, residual, layer, gamma, beta, eps, out,
+                          normed, st);
+  else if (per <= 8)
+    launch_sum_norm<T, 8>(nrows, cols, t, P, bias, thr, scale, seed, idx0, residual, layer, gamma, beta, eps, out,
+                          normed, st);
+  else
+    launch_sum_norm<T, 16>(nrows, cols, t, P, bias, thr, scale, seed, idx0, residual, layer, gamma, beta, eps, out,
+                           normed, st);
+}
+
+// Rows [row0, row0 + nrows) of the block output and their norm (shared by the
+// fused all-reduce + norm and the reduce-scatter + norm).
+int sum_rows_norm(int64_t rows_total, int64_t row0, int64_t nrows, int64_t cols, int32_t t, int32_t dtype,
+                  const void* const* partials, const void* bias, float p_drop, uint64_t seed, const void* residual,
+                  int32_t norm, const void* gamma, const void* beta, float eps, void* out, void* normed,
+                  void* stream) {
+  if (norm != TP_NORM_RMS && norm != TP_NORM_LAYER) return TP_EINVAL;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return TP_EINVAL;
+  if (norm == TP_NORM_RMS && beta) return TP_EINVAL;
+  uint32_t thr = 0;
+  float scale = 1.0f;
+  if (int rc = check_dropout(p_drop, &thr, &scale)) return rc;
+  const int vec = dtype == TP_BF16 ? 8 : 4;
+  const int esz = dtype == TP_BF16 ? 2 : 4;
+  if (cols % vec) return TP_EALIGN;
+  if (cols / vec > kNormMaxVecs) return TP_EUNSUPPORTED;
+  if (!present(out, nrows * cols) || !present(normed, nrows * cols)) return TP_EINVAL;
+  PartialPtrs P{};
+  for (int i = 0; i < t; ++i) {
+    if (!present(partials[i], rows_total * cols)) return TP_EINVAL;
+    if (!aligned16(partials[i])) return TP_EALIGN;
+    P.p[i] = partials[i] ? static_cast<const uint8_t*>(partials[i]) + row0 * cols * esz : nullptr;
+  }
+  if (!ptrs_aligned({bias, residual, gamma, beta, out, normed})) return TP_EALIGN;
+  if (nrows == 0 || cols == 0) return TP_OK;
+  if (nrows > INT32_MAX) return TP_EUNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint64_t idx0 = (uint64_t)(row0 * cols);
+  const int layer = norm == TP_NORM_LAYER ? 1 : 0;
+  Probe pr(st);
+  if (dtype == TP_BF16)
+    sum_norm_dispatch<uint16_t>(nrows, cols, t, P, bias, thr, scale, seed, idx0, residual, layer, gamma, beta, eps,
+                                out, normed, st);
+  else
+    sum_norm_dispatch<float>(nrows, cols, t, P, bias, thr, scale, seed, idx0, residual, layer, gamma, beta, eps, out,
+                             normed, st);
+  return hip_status(hipGetLastError());
+}
+
 int check_sum_args(int64_t rows, int64_t cols, int32_t t, int32_t dtype, const void* const* partials) {
   if (dtype != TP_F32 && dtype != TP_BF16) return TP_EDTYPE;
   if (rows < 0 || cols < 0 || t < 1 || !partials) return TP_EINVAL;
@@ -755,6 +829,26 @@ int tp_reduce_scatter(int64_t rows, int64_t cols, int32_t t, int32_t rank, int32
   const int64_t n = rows / t;
   if (!present(out_r, n * cols)) return TP_EINVAL;
   return sum_rows(rows, rank * n, n, cols, t, dtype, partials, bias, p_drop, seed, residual_r, out_r, stream);
+}
+
+int tp_sum_partials_norm(int64_t rows, int64_t cols, int32_t t, int32_t dtype, const void* const* partials,
+                         const void* bias, float p_drop, uint64_t seed, const void* residual, int32_t norm,
+                         const void* gamma, const void* beta, float eps, void* out, void* normed, void* stream) {
+  if (int rc = check_sum_args(rows, cols, t, dtype, partials)) return rc;
+  return sum_rows_norm(rows, 0, rows, cols, t, dtype, partials, bias, p_drop, seed, residual, norm, gamma, beta, eps,
+                       out, normed, stream);
+}
+
+int tp_reduce_scatter_norm(int64_t rows, int64_t cols, int32_t t, int32_t rank, int32_t dtype,
+                           const void* const* partials, const void* bias, float p_drop, uint64_t seed,
+                           const void* residual_r, int32_t norm, const void* gamma, const void* beta, float eps,
+                           void* out_r, void* normed_r, void* stream) {
+  if (int rc = check_sum_args(rows, cols, t, dtype, partials)) return rc;
+  if (rank < 0 || rank >= t) return TP_EINVAL;
+  if (rows % t) return TP_ENOTDIV;
+  const int64_t n = rows / t;
+  return sum_rows_norm(rows, rank * n, n, cols, t, dtype, partials, bias, p_drop, seed, residual_r, norm, gamma, beta,
+                       eps, out_r, normed_r, stream);
 }
 
 int tp_all_gather(int64_t rows_per_rank, int64_t cols, int32_t t, int32_t dtype, const void* const* slices,

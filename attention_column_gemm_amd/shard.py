@@ -185,3 +185,50 @@ def all_gather(slices, out=None, stream=None):
     V.like("out", out, full, slices[0].dtype, dev)
     B.tp_all_gather(rows, cols, len(slices), code, list(slices), out, stream)
     return out
+
+
+_NORMS = {"rms": B.TP_NORM_RMS, "layer": B.TP_NORM_LAYER}
+
+
+def sum_partials_norm(partials, norm="rms", gamma=None, beta=None, eps=1e-6, bias=None, p_drop=0.0, seed=0,
+                      residual=None, out=None, normed=None, stream=None):
+    """Emulated all-reduce with the residual add and the next sublayer's
+    token-wise norm fused: returns (out, normed)."""
+    torch = _torch()
+    shape, code, dev = V.group("partials", partials)
+    rows, cols = _rows_cols(shape)
+    dt = partials[0].dtype
+    for name, vec in (("bias", bias), ("gamma", gamma), ("beta", beta)):
+        V.vector(name, vec, cols, dt, dev)
+    V.like("residual", residual, shape, dt, dev)
+    out = torch.empty_like(partials[0]) if out is None else out
+    normed = torch.empty_like(partials[0]) if normed is None else normed
+    V.like("out", out, shape, dt, dev)
+    V.like("normed", normed, shape, dt, dev)
+    B.tp_sum_partials_norm(rows, cols, len(partials), code, list(partials), bias, p_drop, seed, residual,
+                           _NORMS[norm], gamma, beta, eps, out, normed, stream)
+    return out, normed
+
+
+def reduce_scatter_norm(partials, rank, norm="rms", gamma=None, beta=None, eps=1e-6, bias=None, p_drop=0.0, seed=0,
+                        residual_r=None, out=None, normed=None, stream=None):
+    """Rank ``rank``'s token slice of the block output and its norm
+    (Megatron-SP: reduce-scatter, then the token-wise norm on the slice)."""
+    torch = _torch()
+    shape, code, dev = V.group("partials", partials)
+    rows, cols = _rows_cols(shape)
+    t = len(partials)
+    if rows % t:
+        raise ValueError(f"rows {rows} do not divide over t = {t} ranks")
+    dt = partials[0].dtype
+    sl = (rows // t,) + tuple(shape[1:])
+    for name, vec in (("bias", bias), ("gamma", gamma), ("beta", beta)):
+        V.vector(name, vec, cols, dt, dev)
+    V.like("residual_r", residual_r, sl, dt, dev)
+    out = torch.empty(sl, dtype=dt, device=dev) if out is None else out
+    normed = torch.empty(sl, dtype=dt, device=dev) if normed is None else normed
+    V.like("out", out, sl, dt, dev)
+    V.like("normed", normed, sl, dt, dev)
+    B.tp_reduce_scatter_norm(rows, cols, t, rank, code, list(partials), bias, p_drop, seed, residual_r,
+                             _NORMS[norm], gamma, beta, eps, out, normed, stream)
+    return out, normed

@@ -137,7 +137,8 @@ def time_split_and_residual(torch, mc, partials, residual, bias, reps=10):
     """The block-closing all-reduce with the residual fused, and its
     Megatron-SP split (one rank's reduce-scatter, the all-gather), at the
     workload's [T, h] shape; HBM bytes each call must move."""
-    from attention_column_gemm_amd.shard import all_gather, reduce_scatter, sum_partials
+    from attention_column_gemm_amd.shard import (all_gather, reduce_scatter, reduce_scatter_norm, sum_partials,
+                                                 sum_partials_norm)
     t, T, h = mc.t, mc.tokens, mc.h
     d = 2 if mc.bf16 else 4
     n = T // t
@@ -145,14 +146,26 @@ def time_split_and_residual(torch, mc, partials, residual, bias, reps=10):
     sl = torch.empty((n, h), dtype=partials[0].dtype, device="cuda")
     slices = [sl] + [sl.clone() for _ in range(t - 1)]
     full = torch.empty_like(partials[0])
+    normed = torch.empty_like(partials[0])
+    sl_n = torch.empty_like(sl)
+    gamma = torch.ones(h, dtype=partials[0].dtype, device="cuda")
+    bb = h * d if bias is not None else 0
     calls = {
         "allreduce_residual_fused": (lambda: sum_partials(partials, bias, mc.p_drop, mc.seed, out=out,
                                                           residual=residual),
-                                     (t + 2) * T * h * d + (h * d if bias is not None else 0), "f3"),
+                                     (t + 2) * T * h * d + bb, "f3"),
         "sp_reduce_scatter_rank0": (lambda: reduce_scatter(partials, 0, bias, mc.p_drop, mc.seed,
                                                            residual_r=residual[:n], out=sl),
-                                    T * h * d + 2 * n * h * d + (h * d if bias is not None else 0), "f2"),
+                                    T * h * d + 2 * n * h * d + bb, "f2"),
         "sp_all_gather": (lambda: all_gather(slices, out=full), 2 * T * h * d, "f2"),
+        "allreduce_residual_rmsnorm_fused": (lambda: sum_partials_norm(partials, "rms", gamma, None, 1e-5, bias,
+                                                                       mc.p_drop, mc.seed, residual=residual,
+                                                                       out=out, normed=normed),
+                                             (t + 3) * T * h * d + bb + h * d, "f2"),
+        "sp_reduce_scatter_rmsnorm_rank0": (lambda: reduce_scatter_norm(partials, 0, "rms", gamma, None, 1e-5, bias,
+                                                                        mc.p_drop, mc.seed, residual_r=residual[:n],
+                                                                        out=sl, normed=sl_n),
+                                            T * h * d + 3 * n * h * d + bb + h * d, "f2"),
     }
     res = []
     for name, (fn, nbytes, row) in calls.items():
@@ -264,7 +277,7 @@ def cpu_baseline(mc, X, dOut, w, budget_s=12.0):
             "threads_used": host["blas_threads"], **{k: v for k, v in host.items() if k != "blas_threads"}}
 
 
-def time_mlp_workload(torch, mcid, steps, warmup=3):
+def time_mlp_workload(torch, mcid, steps, warmup=10):
     """MLP shard fwd+bwd of another workload, rank 0, timed like the headline
     (the span of the forward and backward calls per step, mean over steps)."""
     from attention_column_gemm_amd import inputs as I

@@ -329,6 +329,60 @@ int tp_reduce_scatter(int64_t rows, int64_t cols, int32_t t, int32_t rank, int32
                       const void* const* partials, const void* bias, float p_drop, uint64_t seed,
                       const void* residual_r, void* out_r, void* stream);
 
+/* Token-wise norm of tp_sum_partials_norm and tp_reduce_scatter_norm. */
+typedef enum {
+  TP_NORM_RMS = 0,   /* y = x / sqrt(mean(x^2) + eps) * gamma */
+  TP_NORM_LAYER = 1  /* y = (x - mean(x)) / sqrt(mean((x - mean(x))^2) + eps) * gamma + beta */
+} tp_norm;
+
+/*
+ * tp_sum_partials_norm -- the block-closing all-reduce with the residual add
+ * and the next sublayer's token-wise norm fused ([LP] II.III Computational
+ * Details: fused layernorm / RMSnorm, fused bias + dropout + residual add).
+ *
+ *   out    = residual + Dropout_{p, seed}( sum_{i=0}^{t-1} partials[i] + bias )   (as tp_sum_partials_residual)
+ *   normed = norm(out) over the cols features of each row
+ * The norm reads out as stored (rounded to dtype); its statistics are fp32
+ * sums in a fixed order, so every row's result is the same whichever call
+ * computes it.
+ * Arguments:
+ *   rows, cols, t, dtype, partials, bias, p_drop, seed, residual  as tp_sum_partials_residual
+ *   norm         TP_NORM_RMS or TP_NORM_LAYER
+ *   gamma        [cols] gain (dtype), or NULL for ones
+ *   beta         [cols] shift (dtype) for TP_NORM_LAYER, or NULL for zeros; must be NULL for TP_NORM_RMS
+ *   eps          >= 0, finite
+ *   out          [rows, cols] block output (the residual stream); may alias the residual
+ *   normed       [rows, cols] its norm; may alias no other argument
+ * Errors as tp_sum_partials_residual, plus TP_EINVAL for an unknown norm, a
+ * bad eps, beta with TP_NORM_RMS or a NULL normed, and TP_EUNSUPPORTED for
+ * rows of more than 32768 bf16 (16384 fp32) elements.
+ */
+int tp_sum_partials_norm(int64_t rows, int64_t cols, int32_t t, int32_t dtype, const void* const* partials,
+                         const void* bias, float p_drop, uint64_t seed, const void* residual, int32_t norm,
+                         const void* gamma, const void* beta, float eps, void* out, void* normed, void* stream);
+
+/*
+ * tp_reduce_scatter_norm -- Megatron-SP's reduce-scatter with the token-wise
+ * norm on the rank's slice ([LP] III.III Block Layout Contract: after the
+ * reduce-scatter each rank runs the layernorm / dropout of its own tokens;
+ * [LP] II.III; [L11] section 3 places an RMSNorm before the Llama MLP).
+ *
+ * Rank `rank`'s token slice, rows [rank*rows/t, (rank+1)*rows/t), of
+ * tp_sum_partials_norm's two outputs, computed from those rows of the
+ * partials only; row for row bit-identical to tp_sum_partials_norm, so the
+ * all-gather of the t normed slices is its normed output.
+ * Arguments:
+ *   rows, cols, t, rank, dtype, partials, bias, p_drop, seed, residual_r  as tp_reduce_scatter
+ *   norm, gamma, beta, eps   as tp_sum_partials_norm
+ *   out_r        [rows/t, cols] this rank's slice of the block output; may alias residual_r
+ *   normed_r     [rows/t, cols] its norm (the slice the all-gather takes)
+ * Errors as tp_reduce_scatter and tp_sum_partials_norm.
+ */
+int tp_reduce_scatter_norm(int64_t rows, int64_t cols, int32_t t, int32_t rank, int32_t dtype,
+                           const void* const* partials, const void* bias, float p_drop, uint64_t seed,
+                           const void* residual_r, int32_t norm, const void* gamma, const void* beta, float eps,
+                           void* out_r, void* normed_r, void* stream);
+
 /*
  * tp_all_gather -- Megatron-SP's second half, at the next block's entry,
  * emulated on one device ([LP] III.III Block Layout Contract).

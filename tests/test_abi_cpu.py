@@ -332,3 +332,40 @@ def test_binding_rejects_short_or_mistyped_tensors_before_the_call():
     with pytest.raises(ValueError, match="stats_i"):
         B.tp_attn_shard_bwd(ad, None, None, None, None, None, None, None, None,
                             torch.zeros(2 * 2 * 16 - 1), None, None, None, None)
+
+
+def _norm_call(fn, **kw):
+    a = dict(rows=16, cols=64, t=2, rank=0, dtype=B.TP_BF16, bias=None, p=0.0, seed=0, residual=None,
+             norm=B.TP_NORM_RMS, gamma=A16, beta=None, eps=1e-5, out=A16, normed=A16)
+    a.update(kw)
+    arr = (ctypes.c_void_p * 2)(A16, A16)
+    L = B.lib()
+    if fn == "full":
+        return L.tp_sum_partials_norm(a["rows"], a["cols"], a["t"], a["dtype"], arr, a["bias"], a["p"], a["seed"],
+                                      a["residual"], a["norm"], a["gamma"], a["beta"], a["eps"], a["out"],
+                                      a["normed"], None)
+    return L.tp_reduce_scatter_norm(a["rows"], a["cols"], a["t"], a["rank"], a["dtype"], arr, a["bias"], a["p"],
+                                    a["seed"], a["residual"], a["norm"], a["gamma"], a["beta"], a["eps"], a["out"],
+                                    a["normed"], None)
+
+
+@pytest.mark.parametrize("fn", ["full", "slice"])
+def test_norm_entry_points_reject_bad_arguments(fn):
+    assert _norm_call(fn, norm=2) == B.TP_EINVAL
+    assert _norm_call(fn, norm=-1) == B.TP_EINVAL
+    assert _norm_call(fn, beta=A16) == B.TP_EINVAL                      # RMSNorm has no shift
+    assert _norm_call(fn, eps=-1e-6) == B.TP_EINVAL
+    assert _norm_call(fn, eps=float("nan")) == B.TP_EINVAL
+    assert _norm_call(fn, eps=float("inf")) == B.TP_EINVAL
+    assert _norm_call(fn, normed=None) == B.TP_EINVAL
+    assert _norm_call(fn, out=None) == B.TP_EINVAL
+    assert _norm_call(fn, gamma=MIS) == B.TP_EALIGN
+    assert _norm_call(fn, cols=60) == B.TP_EALIGN                       # not a multiple of 8 bf16
+    assert _norm_call(fn, cols=32768 + 8) == B.TP_EUNSUPPORTED
+    assert _norm_call(fn, dtype=B.TP_F32, cols=16384 + 4) == B.TP_EUNSUPPORTED
+    assert _norm_call(fn, dtype=5) == B.TP_EDTYPE
+    assert _norm_call(fn, p=1.0) == B.TP_EINVAL
+    assert _norm_call(fn, rows=0) == B.TP_OK                             # nothing to do, nothing launched
+    if fn == "slice":
+        assert _norm_call(fn, rank=2) == B.TP_EINVAL
+        assert _norm_call(fn, rows=15) == B.TP_ENOTDIV

@@ -97,3 +97,125 @@ def test_split_at_full_layer_shape():
     ref = OS.sum_partials_residual([p[sample].float().cpu().numpy() for p in P], b.float().cpu().numpy(), 0.1, 31,
                                    R[sample].float().cpu().numpy(), rows=sample)
     check("sampled rows", out[sample].float().cpu().numpy(), ref, TOL["bf16"])
+
+
+NORM_CASES = [
+    # (t, rows, cols, p, bias)
+    (1, 1, 8, 0.0, False),          # one row, one vector
+    (2, 64, 264, 0.1, True),        # ragged: 33 bf16 vectors per row
+    (4, 96, 2056, 0.25, True),      # two vectors per thread, ragged
+    (8, 48, 8192, 0.0, False),      # the full-layer width
+    (2, 6, 32768, 0.1, True),       # the widest bf16 row the kernel keeps in registers
+]
+
+
+def _norm_inputs(cols, kind, dtype, seed):
+    from attention_column_gemm_amd.inputs import round_to_bf16
+    rng = np.random.default_rng(seed)
+    gamma = (1.0 + 0.5 * rng.standard_normal(cols)).astype(np.float32)
+    beta = rng.standard_normal(cols).astype(np.float32) if kind == "layer" else None
+    if dtype == "bf16":
+        gamma = round_to_bf16(gamma)
+        beta = None if beta is None else round_to_bf16(beta)
+    return gamma, beta
+
+
+@pytest.mark.parametrize("kind", ["rms", "layer"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("t,rows,cols,p,bias", NORM_CASES)
+def test_norm_on_the_block_output_and_its_slices(kind, dtype, t, rows, cols, p, bias):
+    """The fused all-reduce + residual + token-wise norm against the oracle;
+    each rank's reduce-scatter + norm gives exactly its rows of both outputs,
+    so the all-gather of the normed slices is the normed all-reduce bit for
+    bit ([LP] III.III)."""
+    torch = need_gpu()
+    if dtype == "fp32" and cols > 16384:
+        pytest.skip("fp32 rows are limited to 16384 elements")
+    banner(f"norm {kind} {dtype} t={t} rows={rows} cols={cols} p={p} bias={bias}")
+    from attention_column_gemm_amd.shard import all_gather, reduce_scatter_norm, sum_partials, sum_partials_norm
+    parts, b, R = _case(t, rows, cols, bias, dtype, 300 * t + cols + (kind == "layer"))
+    gamma, beta = _norm_inputs(cols, kind, dtype, cols + 1)
+    eps = 1e-5
+    seed = 777 + t
+    P = [_dev(x, dtype) for x in parts]
+    bd, Rd, gd, btd = _dev(b, dtype), _dev(R, dtype), _dev(gamma, dtype), _dev(beta, dtype)
+    out, normed = sum_partials_norm(P, kind, gd, btd, eps, bd, p, seed, residual=Rd)
+    plain = sum_partials(P, bd, p, seed, residual=Rd)
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain), "the fused norm changed the block output"
+    ref_out, ref_n = OS.sum_partials_norm(parts, b, p, seed, R, kind, gamma, beta, eps)
+    tol = TOL["bf16"] if dtype == "bf16" else 1e-5
+    check("out", out.float().cpu().numpy(), ref_out, tol)
+    check("normed", normed.float().cpu().numpy(), ref_n, tol)
+    # the norm alone, from the block output as stored
+    stored = out.double().cpu().numpy()
+    check("norm(out as stored)", normed.float().cpu().numpy(), OS.norm(stored, kind, gamma, beta, eps),
+          1e-2 if dtype == "bf16" else 1e-5)
+    if rows % t == 0:
+        n = rows // t
+        sl_out, sl_norm = [], []
+        for r in range(t):
+            o, nm = reduce_scatter_norm(P, r, kind, gd, btd, eps, bd, p, seed, residual_r=Rd[r * n:(r + 1) * n])
+            sl_out.append(o)
+            sl_norm.append(nm)
+        full_n = all_gather(sl_norm)
+        torch.cuda.synchronize()
+        assert torch.equal(full_n, normed)
+        assert torch.equal(all_gather(sl_out), out)
+
+
+def test_norm_defaults_and_in_place_residual():
+    """gamma NULL means ones (beta NULL zeros); out may alias the residual."""
+    torch = need_gpu()
+    banner("norm defaults, in place")
+    from attention_column_gemm_amd.shard import sum_partials_norm
+    parts, b, R = _case(2, 32, 520, True, "bf16", 11)
+    P = [_dev(x, "bf16") for x in parts]
+    Rd = _dev(R, "bf16")
+    ones = torch.ones(520, dtype=torch.bfloat16, device="cuda")
+    zeros = torch.zeros(520, dtype=torch.bfloat16, device="cuda")
+    for kind in ("rms", "layer"):
+        o1, n1 = sum_partials_norm(P, kind, None, None, 1e-6, residual=Rd)
+        o2, n2 = sum_partials_norm(P, kind, ones, zeros if kind == "layer" else None, 1e-6, residual=Rd)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(n1, n2)
+    R2 = Rd.clone()
+    o_ref, n_ref = sum_partials_norm(P, "rms", None, None, 1e-6, residual=Rd)
+    o_in, n_in = sum_partials_norm(P, "rms", None, None, 1e-6, residual=R2, out=R2)
+    torch.cuda.synchronize()
+    assert o_in.data_ptr() == R2.data_ptr()
+    assert torch.equal(R2, o_ref) and torch.equal(n_in, n_ref)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("kind", ["rms", "layer"])
+def test_norm_split_at_full_layer_shape(kind):
+    """[8192, 8192] bf16, t = 8, p = 0.1 with bias and residual: the eight
+    reduce-scatter + norm slices gather to the fused all-reduce + norm bit for
+    bit; sampled rows of both outputs against the oracle."""
+    torch = need_gpu()
+    banner(f"RS + {kind} norm at [8192, 8192] t=8")
+    from attention_column_gemm_amd.shard import all_gather, reduce_scatter_norm, sum_partials_norm
+    rows = cols = 8192
+    t = 8
+    g = torch.Generator(device="cuda").manual_seed(4)
+    P = [torch.randn(rows, cols, generator=g, device="cuda").to(torch.bfloat16) for _ in range(t)]
+    b = torch.randn(cols, generator=g, device="cuda").to(torch.bfloat16)
+    R = torch.randn(rows, cols, generator=g, device="cuda").to(torch.bfloat16)
+    gamma = (1 + 0.5 * torch.randn(cols, generator=g, device="cuda")).to(torch.bfloat16)
+    beta = torch.randn(cols, generator=g, device="cuda").to(torch.bfloat16) if kind == "layer" else None
+    out, normed = sum_partials_norm(P, kind, gamma, beta, 1e-5, b, 0.1, 41, residual=R)
+    n = rows // t
+    sl = [reduce_scatter_norm(P, r, kind, gamma, beta, 1e-5, b, 0.1, 41, residual_r=R[r * n:(r + 1) * n])
+          for r in range(t)]
+    full_o = all_gather([s[0] for s in sl])
+    full_n = all_gather([s[1] for s in sl])
+    torch.cuda.synchronize()
+    assert torch.equal(full_o, out) and torch.equal(full_n, normed)
+    sample = edge_indices(rows, tiles=(n,), extra=8, seed=6)
+    f = lambda x: None if x is None else x.float().cpu().numpy()
+    ref_o, ref_n = OS.sum_partials_norm([p[sample].float().cpu().numpy() for p in P], f(b), 0.1, 41,
+                                        R[sample].float().cpu().numpy(), kind, f(gamma), f(beta), 1e-5,
+                                        rows=sample)
+    check("sampled out", out[sample].float().cpu().numpy(), ref_o, TOL["bf16"])
+    check("sampled normed", normed[sample].float().cpu().numpy(), ref_n, TOL["bf16"])
