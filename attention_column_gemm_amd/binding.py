@@ -25,6 +25,7 @@ HEADER = os.path.join(ROOT, "include", "tp_shard.h")
 TP_F32, TP_BF16 = 0, 1
 TP_GELU, TP_SWIGLU = 0, 1
 TP_OK, TP_EINVAL, TP_ENOTDIV, TP_EDTYPE, TP_EALIGN, TP_EHIP, TP_EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+TP_ENOSCRATCH = -7
 TP_TILE_AUTO, TP_TILE_LARGE, TP_TILE_SMALL, TP_TILE_TINY = 0, 1, 2, 3
 TP_NORM_RMS, TP_NORM_LAYER = 0, 1
 
@@ -68,6 +69,7 @@ def lib() -> ctypes.CDLL:
                                        + [_VP] * 6 + [_VP, _VP, _VP, _VP, _VP, _VP, _VP] + [_VP])
         L.tp_attn_shard_fwd.argtypes = [ctypes.POINTER(tp_attn_desc)] + [_VP] * 7 + [_VP]
         L.tp_attn_shard_bwd.argtypes = [ctypes.POINTER(tp_attn_desc)] + [_VP] * 13 + [_VP]
+        L.tp_attn_shard_bwd_noalloc.argtypes = [ctypes.POINTER(tp_attn_desc)] + [_VP] * 12 + [_VP]
         L.tp_sum_partials.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.POINTER(_VP), _VP, ctypes.c_float, ctypes.c_uint64, _VP, _VP]
         L.tp_sum_partials_residual.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -96,6 +98,7 @@ def lib() -> ctypes.CDLL:
         L.tp_status_string.argtypes = [ctypes.c_int]
         L.tp_status_string.restype = ctypes.c_char_p
         for name in ("tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_attn_shard_fwd", "tp_attn_shard_bwd",
+                     "tp_attn_shard_bwd_noalloc",
                      "tp_sum_partials", "tp_sum_partials_residual", "tp_reduce_scatter", "tp_all_gather",
                      "tp_sum_partials_norm", "tp_reduce_scatter_norm", "tp_mlp_shard_cols", "tp_attn_shard_heads", "tp_comm_bytes", "tp_set_options",
                      "tp_get_options", "tp_profile_arm"):
@@ -220,6 +223,21 @@ def tp_attn_shard_bwd(desc: tp_attn_desc, dZ, X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i
     _check(lib().tp_attn_shard_bwd(ctypes.byref(desc), _ptr(dZ), _ptr(X), _ptr(Wqkv_i), _ptr(Wo_i), _ptr(QKV_i),
                                    _ptr(O_i), _ptr(lse_i), _ptr(dO_i), _ptr(stats_i), _ptr(dQKV_i), _ptr(dWqkv_i),
                                    _ptr(dWo_i), _ptr(dX_i), _stream(stream)), "tp_attn_shard_bwd")
+
+
+def tp_attn_shard_bwd_noalloc(desc: tp_attn_desc, dZ, X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, dO_i, dQKV_i, dWqkv_i,
+                              dWo_i, dX_i, stream=None):
+    z = _attn_sizes(desc)
+    if z:
+        T, h, nq, nqkv, rows = z
+        _need(TP_BF16, dZ=(dZ, T * h), X=(X, T * h), Wqkv_i=(Wqkv_i, h * nqkv), Wo_i=(Wo_i, nq * h),
+              QKV_i=(QKV_i, T * nqkv), O_i=(O_i, T * nq), dO_i=(dO_i, T * nq), dQKV_i=(dQKV_i, T * nqkv),
+              dX_i=(dX_i, T * h))
+        _need_f32(lse_i=(lse_i, rows), dWqkv_i=(dWqkv_i, h * nqkv), dWo_i=(dWo_i, nq * h))
+    _check(lib().tp_attn_shard_bwd_noalloc(ctypes.byref(desc), _ptr(dZ), _ptr(X), _ptr(Wqkv_i), _ptr(Wo_i),
+                                           _ptr(QKV_i), _ptr(O_i), _ptr(lse_i), _ptr(dO_i), _ptr(dQKV_i),
+                                           _ptr(dWqkv_i), _ptr(dWo_i), _ptr(dX_i), _stream(stream)),
+           "tp_attn_shard_bwd_noalloc")
 
 
 def _need_list(code, name, xs, n):

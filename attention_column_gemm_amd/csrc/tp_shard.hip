@@ -426,6 +426,7 @@ const char* tp_status_string(int s) {
     case TP_EALIGN: return "TP_EALIGN: pointer or width not aligned to 16 bytes";
     case TP_EHIP: return "TP_EHIP: HIP runtime error at launch";
     case TP_EUNSUPPORTED: return "TP_EUNSUPPORTED: size not implemented by the kernels";
+    case TP_ENOSCRATCH: return "TP_ENOSCRATCH: the problem needs more scratch than the library's fixed device array";
     default: return "unknown status";
   }
 }
@@ -594,9 +595,14 @@ int tp_attn_shard_fwd(const tp_attn_desc* d, const void* X, const void* Wqkv_i, 
   return hip_status(gemm_bf16<KMAJOR, MNMAJOR>(problem(T_, h, q * D, O_i, q * D, Wo_i, nullptr, h), e2, st));
 }
 
-int tp_attn_shard_bwd(const tp_attn_desc* d, const void* dZ, const void* X, const void* Wqkv_i, const void* Wo_i,
-                      const void* QKV_i, const void* O_i, const float* lse_i, void* dO_i, float* stats_i,
-                      void* dQKV_i, float* dWqkv_i, float* dWo_i, void* dX_i, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the attention backward, stats_i aside.
+int check_attn_bwd(const tp_attn_desc* d, const void* dZ, const void* X, const void* Wqkv_i, const void* Wo_i,
+                   const void* QKV_i, const void* O_i, const float* lse_i, const void* dO_i, const void* dQKV_i,
+                   const float* dWqkv_i, const float* dWo_i, const void* dX_i) {
   if (int rc = check_attn_desc(d)) return rc;
   int q, kv;
   local_heads(d, &q, &kv);
@@ -604,16 +610,33 @@ int tp_attn_shard_bwd(const tp_attn_desc* d, const void* dZ, const void* X, cons
   const int64_t nqkv64 = (int64_t)(q + 2 * kv) * d->d, rows64 = d->b * (int64_t)q * d->s;
   if (!present(dZ, T64 * d->h) || !present(X, T64 * d->h) || !present(Wqkv_i, d->h * nqkv64) ||
       !present(Wo_i, nq64 * d->h) || !present(QKV_i, T64 * nqkv64) || !present(O_i, T64 * nq64) ||
-      !present(lse_i, rows64) || !present(dO_i, T64 * nq64) || !present(stats_i, 2 * rows64) ||
-      !present(dQKV_i, T64 * nqkv64) || !present(dWqkv_i, d->h * nqkv64) || !present(dWo_i, nq64 * d->h) ||
-      !present(dX_i, T64 * d->h))
+      !present(lse_i, rows64) || !present(dO_i, T64 * nq64) || !present(dQKV_i, T64 * nqkv64) ||
+      !present(dWqkv_i, d->h * nqkv64) || !present(dWo_i, nq64 * d->h) || !present(dX_i, T64 * d->h))
     return TP_EINVAL;
   if (d->h % 8) return TP_EALIGN;
-  if (!ptrs_aligned({dZ, X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, dO_i, stats_i, dQKV_i, dWqkv_i, dWo_i, dX_i}))
-    return TP_EALIGN;
+  if (!ptrs_aligned({dZ, X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, dO_i, dQKV_i, dWqkv_i, dWo_i, dX_i})) return TP_EALIGN;
   if (!buffer_ok(T64 * d->h, 2) || !buffer_ok(T64 * nqkv64, 2) || !buffer_ok(d->h * nqkv64, 2) ||
       !buffer_ok(2 * rows64, 4))
     return TP_EUNSUPPORTED;
+  return TP_OK;
+}
+
+// Fp32 floats of the per-row statistics the attention backward keeps between its kernels.
+int64_t attn_bwd_stats_floats(const tp_attn_desc* d) {
+  int q, kv;
+  local_heads(d, &q, &kv);
+  return 2 * d->b * (int64_t)q * d->s;
+}
+
+// The attention backward's launches, arguments checked; stats_i holds
+// attn_bwd_stats_floats() floats.
+int attn_bwd_impl(const tp_attn_desc* d, const void* dZ, const void* X, const void* Wqkv_i, const void* Wo_i,
+                  const void* QKV_i, const void* O_i, const float* lse_i, void* dO_i, float* stats_i, void* dQKV_i,
+                  float* dWqkv_i, float* dWo_i, void* dX_i, void* stream) {
+  int q, kv;
+  local_heads(d, &q, &kv);
+  const int64_t T64 = d->b * d->s;
+  const int64_t nqkv64 = (int64_t)(q + 2 * kv) * d->d;
   const int D = d->d;
   const int T_ = (int)T64, h = (int)d->h, nq = q * D, nqkv = (q + 2 * kv) * D;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -680,6 +703,69 @@ int tp_attn_shard_bwd(const tp_attn_desc* d, const void* dZ, const void* X, cons
   return hip_status(gemm_bf16_pair<MNMAJOR, MNMAJOR, KMAJOR, KMAJOR>(
       problem(h, nqkv, T_, X, h, dQKV_i, nullptr, nqkv), e3,
       problem(T_, h, nqkv, dQKV_i, nqkv, Wqkv_i, nullptr, nqkv), e4, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_attn_shard_bwd(const tp_attn_desc* d, const void* dZ, const void* X, const void* Wqkv_i, const void* Wo_i,
+                      const void* QKV_i, const void* O_i, const float* lse_i, void* dO_i, float* stats_i,
+                      void* dQKV_i, float* dWqkv_i, float* dWo_i, void* dX_i, void* stream) {
+  if (int rc = check_attn_bwd(d, dZ, X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, dO_i, dQKV_i, dWqkv_i, dWo_i, dX_i))
+    return rc;
+  if (!present(stats_i, attn_bwd_stats_floats(d))) return TP_EINVAL;
+  if (!aligned16(stats_i)) return TP_EALIGN;
+  return attn_bwd_impl(d, dZ, X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, dO_i, stats_i, dQKV_i, dWqkv_i, dWo_i, dX_i,
+                       stream);
+}
+
+}  // extern "C"
+
+// Device memory of tp_attn_shard_bwd_noalloc: the per-row statistics
+// ({lse * log2(e), rowsum(dO * O)} per row) that tp_attn_shard_bwd keeps in
+// its caller's stats_i.  Every GPU holds its own copy for the life of the
+// process; host code must use the address hipGetSymbolAddress returns for
+// the current device, never the array's name.
+constexpr int64_t kScratchFloats = (int64_t)1 << 20;  // 4 MiB: b * q * s up to 524288 rows
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+struct ScratchTable {
+  std::mutex mu;
+  float* ptr[kMaxDevices] = {};
+} g_scratch;
+
+// Device address of `scratch` on the current device, looked up once per device.
+int scratch_for_current_device(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return TP_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return TP_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch.mu);
+  if (!g_scratch.ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TP_EHIP;
+    g_scratch.ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch.ptr[dev];
+  return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_attn_shard_bwd_noalloc(const tp_attn_desc* d, const void* dZ, const void* X, const void* Wqkv_i,
+                              const void* Wo_i, const void* QKV_i, const void* O_i, const float* lse_i, void* dO_i,
+                              void* dQKV_i, float* dWqkv_i, float* dWo_i, void* dX_i, void* stream) {
+  if (int rc = check_attn_bwd(d, dZ, X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, dO_i, dQKV_i, dWqkv_i, dWo_i, dX_i))
+    return rc;
+  if (attn_bwd_stats_floats(d) > kScratchFloats) return TP_ENOSCRATCH;
+  float* stats = nullptr;
+  if (int rc = scratch_for_current_device(&stats)) return rc;
+  return attn_bwd_impl(d, dZ, X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, dO_i, stats, dQKV_i, dWqkv_i, dWo_i, dX_i, stream);
 }
 
 }  // extern "C"

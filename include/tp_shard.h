@@ -22,8 +22,9 @@
  *    orientation of [L11] section 1).
  *  - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
  *    aligned.  A tensor with no elements may be passed as NULL.  The library
- *    never allocates, frees or keeps device memory.  Outputs may not alias
- *    inputs.
+ *    never allocates or frees device memory; it keeps none of its own except
+ *    the fixed scratch array of tp_attn_shard_bwd_noalloc.  Outputs may not
+ *    alias inputs.
  *  - Process-wide inputs, the only state kept between calls (the environment
  *    is never read):
  *      * the launch options of tp_set_options (tile shape, splits), which
@@ -66,8 +67,9 @@ enum {
   TP_EDTYPE = -3,       /* unknown dtype/activation, or a combination not provided (attention in fp32) */
   TP_EALIGN = -4,       /* a pointer is not 16-byte aligned or a width is not a multiple of the vector width */
   TP_EHIP = -5,         /* the HIP runtime reported an error when enqueuing a kernel */
-  TP_EUNSUPPORTED = -6  /* a size the kernels do not implement (head width other than 64 or 128, t > 64,
+  TP_EUNSUPPORTED = -6, /* a size the kernels do not implement (head width other than 64 or 128, t > 64,
                            an attention shard with s >= 2^24 or a QKV row of 2^24 bytes or more) */
+  TP_ENOSCRATCH = -7    /* tp_attn_shard_bwd_noalloc: the problem needs more than the fixed scratch array */
 };
 
 /* Tile shape of the matrix-core GEMMs (tp_set_options). */
@@ -271,6 +273,30 @@ int tp_attn_shard_bwd(const tp_attn_desc* desc, const void* dZ, const void* X, c
                       const void* Wo_i, const void* QKV_i, const void* O_i, const float* lse_i,
                       void* dO_i, float* stats_i, void* dQKV_i, float* dWqkv_i, float* dWo_i,
                       void* dX_i, void* stream);
+
+/*
+ * tp_attn_shard_bwd_noalloc -- tp_attn_shard_bwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and results, bit for
+ * bit, with the per-row statistics (stats_i) kept in a device array of the
+ * library instead of a caller buffer.  The caller still passes every input
+ * and output (dWqkv_i and dX_i keep their scratch role).
+ *   Limit: 2 * b * q * s floats of statistics, at most 2^20 (4 MiB; b * q * s
+ *   <= 524288 local query rows); larger problems return TP_ENOSCRATCH
+ *   before anything is enqueued.
+ *   The array is per GPU: the call uses the copy of the device current on
+ *   the calling thread, which must be the device `stream` belongs to.  Its
+ *   address is looked up once per device on the first call there (no
+ *   allocation; hipGetSymbolAddress).  Every call on one GPU shares that
+ *   GPU's array, so calls that overlap on one GPU (on different streams, or
+ *   from different threads) race and must be serialised by the caller; calls
+ *   on one stream are ordered and safe.  No part of it needs to start at
+ *   zero (the statistics kernel writes every value it later reads).
+ * Arguments and errors as tp_attn_shard_bwd without stats_i, plus TP_ENOSCRATCH.
+ */
+int tp_attn_shard_bwd_noalloc(const tp_attn_desc* desc, const void* dZ, const void* X, const void* Wqkv_i,
+                              const void* Wo_i, const void* QKV_i, const void* O_i, const float* lse_i, void* dO_i,
+                              void* dQKV_i, float* dWqkv_i, float* dWo_i, void* dX_i, void* stream);
 
 /*
  * tp_sum_partials -- the all-reduce of operators g/f, emulated on one device

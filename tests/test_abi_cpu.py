@@ -369,3 +369,19 @@ def test_norm_entry_points_reject_bad_arguments(fn):
     if fn == "slice":
         assert _norm_call(fn, rank=2) == B.TP_EINVAL
         assert _norm_call(fn, rows=15) == B.TP_ENOTDIV
+
+
+def test_noalloc_backward_rejects_a_problem_beyond_its_array():
+    """tp_attn_shard_bwd_noalloc: 2 * b * q * s statistics floats above 2^20
+    return TP_ENOSCRATCH before anything is enqueued (or any device is
+    touched); invalid arguments are rejected as by tp_attn_shard_bwd."""
+    L = B.lib()
+    big = B.attn_desc(8, 65536, 1024, 2, 2, 64, 1, 0)          # 2 * 8 * 2 * 65536 = 2^21 floats
+    rc = L.tp_attn_shard_bwd_noalloc(ctypes.byref(big), *([A16] * 12), None)
+    assert rc == B.TP_ENOSCRATCH and "scratch" in B.status_string(rc)
+    ok = B.attn_desc(2, 128, 256, 8, 2, 128, 2, 0)
+    assert L.tp_attn_shard_bwd_noalloc(None, *([A16] * 12), None) == B.TP_EINVAL
+    assert L.tp_attn_shard_bwd_noalloc(ctypes.byref(ok), None, *([A16] * 11), None) == B.TP_EINVAL
+    assert L.tp_attn_shard_bwd_noalloc(ctypes.byref(ok), MIS, *([A16] * 11), None) == B.TP_EALIGN
+    bad = B.attn_desc(2, 128, 256, 8, 2, 96, 2, 0)             # head width 96
+    assert L.tp_attn_shard_bwd_noalloc(ctypes.byref(bad), *([A16] * 12), None) == B.TP_EUNSUPPORTED
