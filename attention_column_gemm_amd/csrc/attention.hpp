@@ -46,6 +46,9 @@ namespace attn {
 
 constexpr int BKV = 64;
 constexpr int NTHREADS = 256;
+// Largest growth (log2 units) of a row's scores over its softmax reference
+// before the paired kernel moves the reference and rescales the output.
+constexpr float kLazy = 8.0f;
 
 struct AttnArgs {
   const uint16_t* qkv;   // [T, (q + 2kv) d]
@@ -63,6 +66,7 @@ struct AttnArgs {
   // combines them.
   float* part;
   int split;
+  int paired;  // run attn_fwd_paired_kernel (causal, one full round of paired query blocks)
 };
 
 // Job J of a split launch (npb query blocks x ny head groups, S of the blocks
@@ -307,7 +311,244 @@ __global__ void __launch_bounds__(NTHREADS) attn_fwd_merge_kernel(AttnArgs a) {
     a.lse[((int64_t)beta * a.q + j) * a.s + my_row] = (m + __log2f(l)) * 0.69314718055994531f;
 }
 
+// Causal forward with every work-group given the same work: work-group y of
+// job pair pr takes query block pr and then query block npb-1-pr of head
+// group y (npb-1-pr is skipped when it is pr), together npb+1 row blocks of
+// causal key range, so a single round of work-groups finishes together.  Its
+// eight waves are two sets of four: set `par` (0 or 1) runs attn_fwd_kernel's
+// four row/head roles on the 64-key blocks 2 i + par of each 128-key
+// superblock i, both sets sharing one superblock in LDS ([K even, K odd,
+// V even, V odd]), so each SIMD holds two waves with the same amount of work.
+// At the end of a query block set 1 hands its unnormalized output, running
+// maximum and row sums to set 0 through LDS, which merges them (each half
+// rescaled to the common maximum, first + second), normalizes and stores.
+template <int D>
+__global__ void __launch_bounds__(2 * NTHREADS, 1) attn_fwd_paired_kernel(AttnArgs a) {
+  constexpr int DT = D / 32;                 // 32-wide d tiles of O
+  constexpr int KK = D / 16;                 // k steps of S = Q K^T
+  constexpr int TILE = BKV * D * 2;          // one 64-key K or V block in LDS
+  constexpr int STAGE = 4 * TILE;            // one 128-key superblock
+  static_assert(4 * DT * 16 * 64 * 4 <= STAGE, "set 1's outputs fit in one stage");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  __shared__ float ml[4][2][64];             // set 1's running maximum and row sums
+  const lds::lds_u8* lds = (const lds::lds_u8*)smem;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+  const int lane = threadIdx.x & 63, hgrp = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int par = wave >> 2, w4 = wave & 3;
+  const int rows_per_wg = 32 * (4 / a.hg);
+  const int npb = (a.s + rows_per_wg - 1) / rows_per_wg;
+  const int group = a.q / a.kv;
+  const int sub_per_kv = group / a.hg;
+  const int ny = a.b * a.kv * sub_per_kv;
+  const int y = (int)blockIdx.x % ny, pr = (int)blockIdx.x / ny;
+  const int beta = y / (a.kv * sub_per_kv);
+  const int rem = y % (a.kv * sub_per_kv);
+  const int g = rem / sub_per_kv;
+  const int j = g * group + (rem % sub_per_kv) * a.hg + (w4 % a.hg);
+  const int64_t tok0 = (int64_t)beta * a.s;
+  const uint32_t ldb = (uint32_t)a.ld_qkv * 2u;
+  const rsrc_t seq = make_rsrc(a.qkv + tok0 * a.ld_qkv, (uint32_t)a.s * ldb);
+  const u32x4 rkv = lds::sgpr_rsrc(a.qkv + tok0 * a.ld_qkv, (uint32_t)a.s * ldb);
+  const uint32_t kcol = (uint32_t)(a.q + g) * D * 2u, vcol = (uint32_t)(a.q + a.kv + g) * D * 2u;
+
+  // the job's query blocks and their 128-key superblocks
+  const int pbA = pr, pbB = npb - 1 - pr;
+  auto nkb_of = [&](int pb) { return (min(a.s, (pb + 1) * rows_per_wg) + BKV - 1) / BKV; };
+  const int nsbA = (nkb_of(pbA) + 1) / 2;
+  const int nsbB = pbB != pbA ? (nkb_of(pbB) + 1) / 2 : 0;
+  const int total = nsbA + nsbB;
+  // Loads of superblock idx into stage st: its four 64-key tiles [K even,
+  // K odd, V even, V odd], TILE / 1024 one-KiB instructions each, dealt
+  // out over the eight waves; this wave's share is NPART instructions, of
+  // which part u is instruction wave + 8 (u % (NPART / 4)) of tile
+  // u / (NPART / 4).  Stage st was last read in step idx - 1, which every
+  // wave has finished at the barrier of step idx.
+  constexpr int NPART = 4 * TILE / 1024 / 8;
+  auto issue_part = [&](int idx, int st, int u) {
+    const int sb = idx < nsbA ? idx : idx - nsbA;
+    const int tile = u / (NPART / 4), i = wave + 8 * (u % (NPART / 4));
+    const int row0 = sb * 2 * BKV + (tile & 1) * BKV;
+    attnt::dma_tile_part<D>(rkv, ldb, row0, a.s, tile < 2 ? kcol : vcol,
+                            lds_base + (uint32_t)st * STAGE + (uint32_t)tile * TILE, i);
+  };
+  auto issue = [&](int idx, int st) {
+#pragma unroll
+    for (int u = 0; u < NPART; ++u) issue_part(idx, st, u);
+  };
+
+  bf16x8 qf[KK];
+  f32x16 oacc[DT];
+  float m_run = -INFINITY, l_run = 0.0f;
+  int rp0 = 0, my_row = 0, nkb = 0;
+
+  if (total > 0) issue(0, 0);
+  for (int idx = 0; idx < total; ++idx) {
+    const int st = idx & 1;
+    const bool inB = idx >= nsbA;
+    const int sb = inB ? idx - nsbA : idx;
+    const int pb = inB ? pbB : pbA;
+    lds::wait_vmcnt<0>();
+    lds::wait_lgkm0();
+    lds::barrier();  // superblock idx is in LDS; every wave is done with idx-1's stage and the merge
+    if (sb == 0) {   // a new query block: this lane's Q row (zero beyond the sequence), fresh state
+      const int pos0 = pb * rows_per_wg;
+      rp0 = pos0 + (w4 / a.hg) * 32;
+      my_row = rp0 + l32;
+      nkb = nkb_of(pb);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const uint32_t off = (uint32_t)my_row * ldb + (uint32_t)(j * D + kk * 16 + hgrp * 8) * 2u;
+        qf[kk] = __builtin_bit_cast(bf16x8, buf_load16(seq, my_row < a.s ? off : kOOB));
+      }
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): keep these out of the stage pipeline's counts
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[t][e] = 0.0f;
+      m_run = -INFINITY;
+      l_run = 0.0f;
+    }
+    // The next superblock's loads go out after this block's output MFMAs
+    // (below): a wave issuing LDS-direct loads is held until the CU's
+    // L2-to-LDS path (tens of bytes per clock) accepts them, and held there
+    // the MFMAs it has already issued keep the matrix unit busy; issued at
+    // the top of the step the hold came before any MFMA (8% slower on
+    // gfx950, and 3% slower spread between the score MFMAs).
+    const bool more = idx + 1 < total;
+    const int kb = 2 * sb + par;
+    const int key0 = kb * BKV;
+    if (kb < nkb && key0 <= rp0 + 31) {
+      const lds::lds_u8* tk = lds + st * STAGE + par * TILE;
+      const lds::lds_u8* tv = lds + st * STAGE + (2 + par) * TILE;
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.0f;
+      static_assert((2 * KK) % NPART == 0, "loads spread evenly over the score MFMAs");
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(attnt::row_frag<D>(tk, 32 * kt, kk), qf[kk], sacc[kt],
+                                                             0, 0, 0);
+        }
+      // Online softmax in base 2 against a per-row reference m_run that only
+      // moves when the block's scaled maximum exceeds it by more than
+      // kLazy: probabilities stay below 2^kLazy, and the running output is
+      // rescaled only on such moves.  The score scale rides on the
+      // exponent's FMA, and the block maximum is taken on the raw scores.
+      const bool need_mask = key0 + BKV - 1 > rp0 || key0 + BKV > a.s;
+      float bmax = -INFINITY;
+      auto raw_max = [&](auto masked) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            if constexpr (decltype(masked)::value) {
+              const int key = key0 + kt * 32 + 8 * (r >> 2) + 4 * hgrp + (r & 3);
+              if (key >= a.s || key > my_row) sacc[kt][r] = -INFINITY;
+            }
+            bmax = fmaxf(bmax, sacc[kt][r]);
+          }
+      };
+      if (need_mask)
+        raw_max(std::true_type{});
+      else
+        raw_max(std::false_type{});
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32)) * a.scale_log2;
+      if (__builtin_amdgcn_ballot_w64(bmax > m_run + kLazy)) {
+        const float m_new = bmax > m_run + kLazy ? bmax : m_run;
+        const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[t][e] *= alpha;
+      }
+      const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+      float psum = 0.0f;
+      bf16x8 pf[2][2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], a.scale_log2, -m_use));
+          psum += p[r];
+        }
+        pf[kt][0] = attnt::pack8(p);
+        pf[kt][1] = attnt::pack8(p + 8);
+      }
+      l_run += psum;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int t = 0; t < DT; ++t)
+            oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(attnt::tr_frag<D>(tv, 32 * kt, t, jj), pf[kt][jj],
+                                                              oacc[t], 0, 0, 0);
+    }
+    if (more) {
+      lds::wait_lgkm0();
+      issue(idx + 1, st ^ 1);
+    }
+    if (sb + 1 < (inB ? nsbB : nsbA)) continue;
+    // the query block is done: set 1 hands its state to set 0 through this
+    // stage's memory, free once every wave has passed the barrier below
+    lds::wait_lgkm0();
+    lds::barrier();
+    float* xo = reinterpret_cast<float*>(smem + st * STAGE) + w4 * (DT * 16 * 64) + lane;
+    if (par == 1) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xo[(t * 16 + e) * 64] = oacc[t][e];
+      ml[w4][0][lane] = m_run;
+      ml[w4][1][lane] = l_run;
+    }
+    lds::wait_lgkm0();
+    lds::barrier();
+    if (par == 0) {
+      const float m1 = ml[w4][0][lane], l1 = ml[w4][1][lane];
+      const float m = fmaxf(m_run, m1);
+      const float c0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
+      const float c1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+      const float l = l_run * c0 + l1 * c1;
+      const float l_tot = l + __shfl_xor(l, 32);
+      if (my_row < a.s) {
+        const float inv = 1.0f / l_tot;
+        uint16_t* orow = a.o + (tok0 + my_row) * a.ld_o + (int64_t)j * D;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (oacc[t][4 * q4 + e] * c0 + xo[(t * 16 + 4 * q4 + e) * 64] * c1) * inv;
+            Elem<uint16_t>::store4(orow + t * 32 + 8 * q4 + 4 * hgrp, v);
+          }
+        if (a.lse && hgrp == 0)
+          a.lse[((int64_t)beta * a.q + j) * a.s + my_row] = (m + __log2f(l_tot)) * 0.69314718055994531f;
+      }
+    }
+  }
+}
+
 }  // namespace attn
+
+// Whether the causal forward runs as attn_fwd_paired_kernel: one round of
+// equal work-groups (pairs of query blocks) fills every CU.
+inline bool attn_fwd_paired(int s, int causal, int b, int q, int kv, int hg) {
+  const int rows_per_wg = 32 * (4 / hg);
+  const int npb = (s + rows_per_wg - 1) / rows_per_wg;
+  const int64_t jobs = (int64_t)((npb + 1) / 2) * b * kv * ((q / kv) / hg);
+  return causal && npb >= 2 && jobs >= 256;
+}
 
 // Query blocks of the forward launch worth splitting (AttnArgs::split): the
 // heavier half for a causal mask when the unsplit launch leaves some of its
@@ -329,6 +570,11 @@ hipError_t launch_attn_fwd(const attn::AttnArgs& a, hipStream_t stream) {
   const int npb = (a.s + rows_per_wg - 1) / rows_per_wg;
   const int ny = a.b * a.kv * ((a.q / a.kv) / a.hg);
   if (npb == 0 || ny == 0) return hipSuccess;
+  if (a.paired) {
+    hipLaunchKernelGGL((attn::attn_fwd_paired_kernel<D>), dim3(((npb + 1) / 2) * ny), dim3(2 * attn::NTHREADS), 0,
+                       stream, a);
+    return hipGetLastError();
+  }
   if (a.split == 0) {
     hipLaunchKernelGGL((attn::attn_fwd_kernel<D>), dim3(npb, ny), dim3(attn::NTHREADS), 0, stream, a);
     return hipGetLastError();

@@ -77,28 +77,33 @@ __device__ __forceinline__ bf16x8 tr_frag(const lds_u8* tile, int r0, int dt, in
 
 // LDS-direct load of rows [row0, row0 + ROWS) x D bf16 columns starting at
 // byte column col_bytes of a row-major matrix (ld_bytes per row, nrows rows,
-// behind `rsrc`) into a swizzled [ROWS][D] tile at LDS byte address dst.
-// This wave issues the tile's 1 KiB instructions i0, i0 + step, ...
+// behind `rsrc`) into a swizzled [ROWS][D] tile at LDS byte address dst:
+// instruction i of the tile's ROWS * D * 2 / 1024 one-KiB instructions.
 // Row offsets use the full-rate 24-bit multiply: row indices and ld_bytes
 // stay below 2^24 (the host rejects larger attention shapes).
+template <int D>
+__device__ __forceinline__ void dma_tile_part(const u32x4& rsrc, uint32_t ld_bytes, int row0, int nrows,
+                                              uint32_t col_bytes, uint32_t dst, int i) {
+  const int lane = threadIdx.x & 63;
+  const int o = i * 1024 + 16 * lane;
+  const int r = o / (2 * D), pos = (o % (2 * D)) >> 4;
+  const int c = pos ^ swz<D>(r);
+  const uint32_t voff =
+      row0 + r < nrows ? __umul24((uint32_t)(row0 + r), ld_bytes) + col_bytes + (uint32_t)c * 16u : kOOB;
+  lds::dma16(rsrc, voff, dst + (uint32_t)i * 1024u);
+}
+
+// The whole tile: this wave issues instructions i0, i0 + step, ...
 template <int D, int ROWS>
 __device__ __forceinline__ void dma_tile(const u32x4& rsrc, uint32_t ld_bytes, int row0, int nrows,
                                          uint32_t col_bytes, uint32_t dst, int i0, int step) {
   constexpr int NI = ROWS * D * 2 / 1024;
-  const int lane = threadIdx.x & 63;
-  for (int i = i0; i < NI; i += step) {
-    const int o = i * 1024 + 16 * lane;
-    const int r = o / (2 * D), pos = (o % (2 * D)) >> 4;
-    const int c = pos ^ swz<D>(r);
-    const uint32_t voff =
-        row0 + r < nrows ? __umul24((uint32_t)(row0 + r), ld_bytes) + col_bytes + (uint32_t)c * 16u : kOOB;
-    lds::dma16(rsrc, voff, dst + (uint32_t)i * 1024u);
-  }
+  for (int i = i0; i < NI; i += step) dma_tile_part<D>(rsrc, ld_bytes, row0, nrows, col_bytes, dst, i);
 }
 
 // One 4-byte load per lane from `rsrc` at `voff` into LDS at m0 + 4 * lane.
 __device__ __forceinline__ void dma4(const u32x4& rsrc, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc)
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(rsrc)
                : "memory");
 }
 

@@ -23,7 +23,7 @@ __device__ __forceinline__ u32x4 sgpr_rsrc(const void* base, uint32_t num_bytes)
 // is tracked explicitly with wait_vmcnt.  Offsets at or past the descriptor's
 // size read zeros.
 __device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc)
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(rsrc)
                : "memory");
 }
 

@@ -581,7 +581,8 @@ int tp_attn_shard_fwd(const tp_attn_desc* d, const void* X, const void* Wqkv_i, 
   // the heaviest query blocks of a launch that leaves slots empty run as two
   // halves whose softmax state goes to Z_i's memory (written only by the
   // output projection below)
-  a.split = split_tail_enabled() ? attn_fwd_split(a.s, a.causal, a.b, a.q, a.kv, a.hg) : 0;
+  a.paired = split_tail_enabled() && attn_fwd_paired(a.s, a.causal, a.b, a.q, a.kv, a.hg) ? 1 : 0;
+  a.split = split_tail_enabled() && !a.paired ? attn_fwd_split(a.s, a.causal, a.b, a.q, a.kv, a.hg) : 0;
   if (attn_fwd_part_floats(a.b, a.q, a.kv, a.hg, a.split, D) * 4 > (int64_t)T_ * h * 2) a.split = 0;
   a.part = static_cast<float*>(Z_i);
   hipError_t e;

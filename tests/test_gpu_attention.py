@@ -289,3 +289,50 @@ def test_attention_backward_pair_half_width_tail():
     sh, X, w, dZ = _run_bwd(c, 0, True)
     torch.cuda.synchronize()
     _check_bwd("tail", c, sh, X, w, dZ, True)
+
+
+FWD_PAIRED = {
+    # one round of paired query blocks (>= 256 work-groups of eight waves): 16 query blocks of 32 rows,
+    # 4 heads per work-group half, 32 head groups
+    "gqa8_d128_b16_s512": I.custom_attn(211, 16, 512, 256, 8, 1, 128, 1),
+    # ragged last query block (rows 480..499) and sequence
+    "gqa8_d128_b16_s500_ragged": I.custom_attn(212, 16, 500, 256, 8, 1, 128, 1),
+    "gqa8_d64_b16_s512": I.custom_attn(213, 16, 512, 256, 8, 1, 64, 1),
+    # 15 query blocks: the middle job holds one block only
+    "gqa8_d128_b16_s480_odd": I.custom_attn(214, 16, 480, 256, 8, 1, 128, 1),
+    # groups of 4 and 2 (64-row blocks: two row tiles per head in a half)
+    "gqa4_d128_b32_s512": I.custom_attn(215, 32, 512, 256, 8, 2, 128, 1),
+    "gqa2_d64_b32_s512": I.custom_attn(216, 32, 512, 256, 4, 2, 64, 1),
+}
+
+
+@pytest.mark.parametrize("name", list(FWD_PAIRED))
+def test_attention_forward_paired_blocks(name, lib_options):
+    """A causal forward with at least one full round of paired query blocks
+    runs each work-group over blocks pr and npb-1-pr, its two wave sets
+    taking alternate 64-key blocks and merging through LDS.  O_i, lse_i and
+    Z_i against the oracle with the pairing on and off (the plain kernel);
+    O_i differs in rounding between them (proof that it ran)."""
+    torch = need_gpu()
+    c = FWD_PAIRED[name]
+    ref = None
+    got = {}
+    for split in (1, 0):
+        lib_options(split_tail=split)
+        banner(f"attn fwd paired={split} {name} b={c.b} s={c.s} n_q={c.n_q} n_kv={c.n_kv} d={c.d}")
+        sh, X, w = _run(c, 0, True)
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = OA.shard_forward(X, w["Wqkv"], w["Wo"], b=c.b, s=c.s, q=c.q, kv=c.kv, d=c.d, causal=True)
+        check(f"paired{split}.O_i", _np(sh.O), ref["O"], BF)
+        check(f"paired{split}.lse_i", _np(sh.lse), ref["lse"], BF)
+        check(f"paired{split}.Z_i", _np(sh.Z), ref["Z"], BF)
+        q, kv, d = c.q, c.kv, c.d
+        QKV = _np(sh.QKV)
+        Oc, lc = OA.core(QKV[:, :q * d], QKV[:, q * d:(q + kv) * d], QKV[:, (q + kv) * d:], b=c.b, s=c.s,
+                         n_q=q, n_kv=kv, d=d, causal=True)
+        check(f"paired{split}.core(O_i)", _np(sh.O), Oc, 1e-2)
+        check(f"paired{split}.core(lse_i)", _np(sh.lse), lc, 1e-3)
+        got[split] = sh.O.clone()
+        del sh
+    assert not torch.equal(got[1], got[0]), "the paired kernel did not run"
