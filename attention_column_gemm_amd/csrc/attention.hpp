@@ -318,19 +318,31 @@ __global__ void __launch_bounds__(NTHREADS) attn_fwd_merge_kernel(AttnArgs a) {
 // eight waves are two sets of four: set `par` (0 or 1) runs attn_fwd_kernel's
 // four row/head roles on the 64-key blocks 2 i + par of each 128-key
 // superblock i, both sets sharing one superblock in LDS ([K even, K odd,
-// V even, V odd]), so each SIMD holds two waves with the same amount of work.
-// At the end of a query block set 1 hands its unnormalized output, running
-// maximum and row sums to set 0 through LDS, which merges them (each half
-// rescaled to the common maximum, first + second), normalizes and stores.
+// V even, V odd]).  Wave w of set 0 and wave w of set 1 share a SIMD, and
+// set 1 runs half a step behind: in step i set 0 computes the scores of
+// its block of superblock i, their softmax and the output product, while
+// set 1 first finishes superblock i-1 (softmax and output product of the
+// scores it kept) and then computes the scores of superblock i.  Each
+// set's matrix instructions thus meet the other set's softmax arithmetic on
+// the SIMD instead of its own.  V odd is read one step later than the
+// rest of a superblock, so it is loaded one step later too.  At the end of
+// a query block set 1 finishes its last block, then hands its unnormalized
+// output, running maximum and row sums to set 0 through LDS, which merges
+// them (each half rescaled to the common maximum, first + second),
+// normalizes and stores.
 template <int D>
 __global__ void __launch_bounds__(2 * NTHREADS, 1) attn_fwd_paired_kernel(AttnArgs a) {
   constexpr int DT = D / 32;                 // 32-wide d tiles of O
   constexpr int KK = D / 16;                 // k steps of S = Q K^T
   constexpr int TILE = BKV * D * 2;          // one 64-key K or V block in LDS
   constexpr int STAGE = 4 * TILE;            // one 128-key superblock
+  constexpr int QT = 32 * D * 2;              // one wave's [32][D] Q tile
+  constexpr int OROW = 2 * D + 16;            // padded row of the staged bf16 output
   static_assert(4 * DT * 16 * 64 * 4 <= STAGE, "set 1's outputs fit in one stage");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
-  __shared__ float ml[4][2][64];             // set 1's running maximum and row sums
+  static_assert(32 * OROW <= DT * 16 * 64 * 4, "the staged output fits in a wave's share of it");
+  static_assert(2 * 4 * 64 * 4 <= TILE, "set 1's maxima and sums fit in one tile");
+  // two superblock stages, then the four row/head roles' Q tiles
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE + 4 * QT];
   const lds::lds_u8* lds = (const lds::lds_u8*)smem;
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
@@ -359,87 +371,70 @@ __global__ void __launch_bounds__(2 * NTHREADS, 1) attn_fwd_paired_kernel(AttnAr
   const int nsbA = (nkb_of(pbA) + 1) / 2;
   const int nsbB = pbB != pbA ? (nkb_of(pbB) + 1) / 2 : 0;
   const int total = nsbA + nsbB;
-  // Loads of superblock idx into stage st: its four 64-key tiles [K even,
-  // K odd, V even, V odd], TILE / 1024 one-KiB instructions each, dealt
-  // out over the eight waves; this wave's share is NPART instructions, of
-  // which part u is instruction wave + 8 (u % (NPART / 4)) of tile
-  // u / (NPART / 4).  Stage st was last read in step idx - 1, which every
-  // wave has finished at the barrier of step idx.
-  constexpr int NPART = 4 * TILE / 1024 / 8;
+  // Loads of a superblock's four 64-key tiles [K even, K odd, V even,
+  // V odd], TILE / 1024 one-KiB instructions each, dealt out over the eight
+  // waves; this wave's share of a tile is PER_TILE instructions, part u
+  // being instruction wave + 8 (u % PER_TILE) of tile u / PER_TILE.
+  static_assert(TILE % 8192 == 0, "each tile splits evenly over the eight waves");
+  constexpr int PER_TILE = TILE / 1024 / 8;
   auto issue_part = [&](int idx, int st, int u) {
     const int sb = idx < nsbA ? idx : idx - nsbA;
-    const int tile = u / (NPART / 4), i = wave + 8 * (u % (NPART / 4));
+    const int tile = u / PER_TILE, i = wave + 8 * (u % PER_TILE);
     const int row0 = sb * 2 * BKV + (tile & 1) * BKV;
     attnt::dma_tile_part<D>(rkv, ldb, row0, a.s, tile < 2 ? kcol : vcol,
                             lds_base + (uint32_t)st * STAGE + (uint32_t)tile * TILE, i);
   };
-  auto issue = [&](int idx, int st) {
+  // Step idx's loads: K even, K odd and V even of superblock idx + 1 into
+  // the other stage (read last in step idx - 1), and V odd of superblock
+  // idx into this stage (its previous V odd was read by set 1 in step
+  // idx - 1); both are waited for at the top of step idx + 1.
+  auto issue = [&](int idx, int st, bool next) {
+    if (next) {
 #pragma unroll
-    for (int u = 0; u < NPART; ++u) issue_part(idx, st, u);
-  };
-
-  bf16x8 qf[KK];
-  f32x16 oacc[DT];
-  float m_run = -INFINITY, l_run = 0.0f;
-  int rp0 = 0, my_row = 0, nkb = 0;
-
-  if (total > 0) issue(0, 0);
-  for (int idx = 0; idx < total; ++idx) {
-    const int st = idx & 1;
-    const bool inB = idx >= nsbA;
-    const int sb = inB ? idx - nsbA : idx;
-    const int pb = inB ? pbB : pbA;
-    lds::wait_vmcnt<0>();
-    lds::wait_lgkm0();
-    lds::barrier();  // superblock idx is in LDS; every wave is done with idx-1's stage and the merge
-    if (sb == 0) {   // a new query block: this lane's Q row (zero beyond the sequence), fresh state
-      const int pos0 = pb * rows_per_wg;
-      rp0 = pos0 + (w4 / a.hg) * 32;
-      my_row = rp0 + l32;
-      nkb = nkb_of(pb);
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const uint32_t off = (uint32_t)my_row * ldb + (uint32_t)(j * D + kk * 16 + hgrp * 8) * 2u;
-        qf[kk] = __builtin_bit_cast(bf16x8, buf_load16(seq, my_row < a.s ? off : kOOB));
-      }
-      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): keep these out of the stage pipeline's counts
-#pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[t][e] = 0.0f;
-      m_run = -INFINITY;
-      l_run = 0.0f;
+      for (int u = 0; u < 3 * PER_TILE; ++u) issue_part(idx + 1, st ^ 1, u);
     }
-    // The next superblock's loads go out after this block's output MFMAs
-    // (below): a wave issuing LDS-direct loads is held until the CU's
-    // L2-to-LDS path (tens of bytes per clock) accepts them, and held there
-    // the MFMAs it has already issued keep the matrix unit busy; issued at
-    // the top of the step the hold came before any MFMA (8% slower on
-    // gfx950, and 3% slower spread between the score MFMAs).
-    const bool more = idx + 1 < total;
-    const int kb = 2 * sb + par;
-    const int key0 = kb * BKV;
-    if (kb < nkb && key0 <= rp0 + 31) {
-      const lds::lds_u8* tk = lds + st * STAGE + par * TILE;
-      const lds::lds_u8* tv = lds + st * STAGE + (2 + par) * TILE;
-      f32x16 sacc[2];
+#pragma unroll
+    for (int u = 3 * PER_TILE; u < 4 * PER_TILE; ++u) issue_part(idx, st, u);
+  };
+  // Q of query block pb: role w4's tile (rows rp0 .. rp0 + 31 of head j,
+  // zeros beyond the sequence) in Q slot w4, half of its D / 16 one-KiB
+  // instructions from each set.
+  auto issue_q = [&](int pb) {
+    const int rq0 = pb * rows_per_wg + (w4 / a.hg) * 32;
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u)
+      attnt::dma_tile_part<D>(rkv, ldb, rq0, a.s, (uint32_t)j * D * 2u, lds_base + 2 * STAGE + (uint32_t)w4 * QT,
+                              par * (D / 32) + u);
+  };
+  const lds::lds_u8* tq = lds + 2 * STAGE + w4 * QT;
+
+  // Each set runs its own copy of the loop (the same barriers in the same
+  // order), so neither copy's registers are shaped by the other's.
+  auto run = [&](auto set) {
+    constexpr int P = decltype(set)::value;
+    f32x16 oacc[DT];
+    f32x16 sacc[2];      // the scores of this wave's current block (set 1: kept to the next step)
+    float m_run = -INFINITY, l_run = 0.0f;
+    int rp0 = 0, my_row = 0, nkb = 0, key0p = 0;
+    bool pend = false;   // set 1: sacc holds the scores of block key0p, not yet taken further
+    auto scores = [&](const lds::lds_u8* tk) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.0f;
-      static_assert((2 * KK) % NPART == 0, "loads spread evenly over the score MFMAs");
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(attnt::row_frag<D>(tk, 32 * kt, kk), qf[kk], sacc[kt],
-                                                             0, 0, 0);
-        }
-      // Online softmax in base 2 against a per-row reference m_run that only
-      // moves when the block's scaled maximum exceeds it by more than
-      // kLazy: probabilities stay below 2^kLazy, and the running output is
-      // rescaled only on such moves.  The score scale rides on the
-      // exponent's FMA, and the block maximum is taken on the raw scores.
+        for (int kk = 0; kk < KK; ++kk)
+          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(attnt::row_frag<D>(tk, 32 * kt, kk),
+                                                             attnt::row_frag<D>(tq, 0, kk), sacc[kt], 0, 0, 0);
+    };
+    // Online softmax in base 2 against a per-row reference m_run that only
+    // moves when the block's scaled maximum exceeds it by more than kLazy:
+    // probabilities stay below 2^kLazy, and the running output is rescaled
+    // only on such moves.  The score scale rides on the exponent's FMA, and
+    // the block maximum is taken on the raw scores.  Then O += P V.
+    auto softmax_pv = [&](int key0, const lds::lds_u8* tv) {
       const bool need_mask = key0 + BKV - 1 > rp0 || key0 + BKV > a.s;
       float bmax = -INFINITY;
       auto raw_max = [&](auto masked) {
@@ -492,51 +487,135 @@ __global__ void __launch_bounds__(2 * NTHREADS, 1) attn_fwd_paired_kernel(AttnAr
           for (int t = 0; t < DT; ++t)
             oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(attnt::tr_frag<D>(tv, 32 * kt, t, jj), pf[kt][jj],
                                                               oacc[t], 0, 0, 0);
+    };
+    if (total > 0) {
+      issue_q(pbA);
+#pragma unroll
+      for (int u = 0; u < 3 * PER_TILE; ++u) issue_part(0, 0, u);
     }
-    if (more) {
+    for (int idx = 0; idx < total; ++idx) {
+      const int st = idx & 1;
+      const bool inB = idx >= nsbA;
+      const int sb = inB ? idx - nsbA : idx;
+      const int pb = inB ? pbB : pbA;
+      lds::wait_vmcnt<0>();
       lds::wait_lgkm0();
-      issue(idx + 1, st ^ 1);
-    }
-    if (sb + 1 < (inB ? nsbB : nsbA)) continue;
-    // the query block is done: set 1 hands its state to set 0 through this
-    // stage's memory, free once every wave has passed the barrier below
-    lds::wait_lgkm0();
-    lds::barrier();
-    float* xo = reinterpret_cast<float*>(smem + st * STAGE) + w4 * (DT * 16 * 64) + lane;
-    if (par == 1) {
+      lds::barrier();  // this step's tiles are in LDS; every wave is done with the stages they replace
+      if (sb == 0) {   // a new query block (its Q tiles are in LDS): fresh state
+        rp0 = pb * rows_per_wg + (w4 / a.hg) * 32;
+        my_row = rp0 + l32;
+        nkb = nkb_of(pb);
 #pragma unroll
-      for (int t = 0; t < DT; ++t)
+        for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) xo[(t * 16 + e) * 64] = oacc[t][e];
-      ml[w4][0][lane] = m_run;
-      ml[w4][1][lane] = l_run;
-    }
-    lds::wait_lgkm0();
-    lds::barrier();
-    if (par == 0) {
-      const float m1 = ml[w4][0][lane], l1 = ml[w4][1][lane];
-      const float m = fmaxf(m_run, m1);
-      const float c0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
-      const float c1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
-      const float l = l_run * c0 + l1 * c1;
-      const float l_tot = l + __shfl_xor(l, 32);
-      if (my_row < a.s) {
+          for (int e = 0; e < 16; ++e) oacc[t][e] = 0.0f;
+        m_run = -INFINITY;
+        l_run = 0.0f;
+      }
+      const int kb = 2 * sb + par;
+      const int key0 = kb * BKV;
+      const bool act = kb < nkb && key0 <= rp0 + 31;
+      if constexpr (P == 0) {
+        if (act) {
+          scores(lds + st * STAGE);
+          softmax_pv(key0, lds + st * STAGE + 2 * TILE);
+        }
+      } else {
+        if (pend) softmax_pv(key0p, lds + (st ^ 1) * STAGE + 3 * TILE);
+        pend = act;
+        if (act) {
+          scores(lds + st * STAGE + TILE);
+          key0p = key0;
+        }
+      }
+      // The loads go out after the matrix instructions: a wave issuing
+      // LDS-direct loads is held until the CU's L2-to-LDS path (tens of bytes
+      // per clock) accepts them, and held there the MFMAs it has already
+      // issued keep the matrix unit busy.
+      lds::wait_lgkm0();
+      issue(idx, st, idx + 1 < total);
+      if (sb + 1 < (inB ? nsbB : nsbA)) continue;
+      // The query block is done.  Set 1 takes its last block further (its
+      // V odd tile has arrived at the barrier) while the next block's Q tiles
+      // load (every score product of this block is done), then hands its
+      // output to set 0 through this stage's memory and its maxima and sums
+      // through the other stage's V odd slot (idle until the next step's
+      // loads), both free once every wave has passed the second barrier.
+      lds::wait_vmcnt<0>();
+      lds::wait_lgkm0();
+      lds::barrier();
+      if (idx + 1 < total) issue_q(pbB);
+      if constexpr (P == 1) {
+        if (pend) softmax_pv(key0p, lds + st * STAGE + 3 * TILE);
+        pend = false;
+      }
+      lds::wait_lgkm0();
+      lds::barrier();
+      uint8_t* const wbuf = smem + st * STAGE + w4 * (DT * 16 * 64 * 4);  // this role's share of the stage
+      lds::lds_u8* const wl = (lds::lds_u8*)wbuf;
+      float* xo = reinterpret_cast<float*>(wbuf) + lane;
+      float* ml = reinterpret_cast<float*>(smem + (st ^ 1) * STAGE + 3 * TILE) + w4 * 128 + lane;
+      if constexpr (P == 1) {
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) xo[(t * 16 + e) * 64] = oacc[t][e];
+        ml[0] = m_run;
+        ml[64] = l_run;
+      }
+      lds::wait_lgkm0();
+      lds::barrier();
+      if constexpr (P == 0) {
+        const float m1 = ml[0], l1 = ml[64];
+        const float m = fmaxf(m_run, m1);
+        const float c0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
+        const float c1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+        const float l = l_run * c0 + l1 * c1;
+        const float l_tot = l + __shfl_xor(l, 32);
         const float inv = 1.0f / l_tot;
-        uint16_t* orow = a.o + (tok0 + my_row) * a.ld_o + (int64_t)j * D;
+        // Set 1's output into registers, then the merged, normalized bf16
+        // rows into the same memory ([32][D] with padded rows), read back
+        // so that each store covers whole rows.
+        float x1[DT][16];
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) x1[t][e] = xo[(t * 16 + e) * 64];
+        lds::wait_lgkm0();
+        asm volatile("" ::: "memory");  // every lane's reads before any lane's writes
 #pragma unroll
         for (int t = 0; t < DT; ++t)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (oacc[t][4 * q4 + e] * c0 + xo[(t * 16 + 4 * q4 + e) * 64] * c1) * inv;
-            Elem<uint16_t>::store4(orow + t * 32 + 8 * q4 + 4 * hgrp, v);
+            for (int e = 0; e < 4; ++e) v[e] = (oacc[t][4 * q4 + e] * c0 + x1[t][4 * q4 + e] * c1) * inv;
+            u32x2 w;
+            w[0] = pack_bf16x2(v[0], v[1]);
+            w[1] = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(wl + l32 * OROW +
+                                                                        (t * 32 + 8 * q4 + 4 * hgrp) * 2) = w;
           }
-        if (a.lse && hgrp == 0)
+        lds::wait_lgkm0();
+        asm volatile("" ::: "memory");
+        constexpr int CPR = 2 * D / 16, RPI = 64 / CPR;  // 16-byte chunks per row, rows per pass
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+          const int r = it * RPI + lane / CPR, c = lane % CPR;
+          const u32x4 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(wl + r * OROW + c * 16);
+          if (rp0 + r < a.s)
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(a.o + (tok0 + rp0 + r) * a.ld_o + (int64_t)j * D +
+                                                                  c * 8));
+        }
+        if (a.lse && hgrp == 0 && my_row < a.s)
           a.lse[((int64_t)beta * a.q + j) * a.s + my_row] = (m + __log2f(l_tot)) * 0.69314718055994531f;
       }
     }
-  }
+  };
+  if (par == 0)
+    run(std::integral_constant<int, 0>{});
+  else
+    run(std::integral_constant<int, 1>{});
 }
 
 }  // namespace attn
