@@ -337,10 +337,12 @@ __global__ void __launch_bounds__(2 * NTHREADS, 1) attn_fwd_paired_kernel(AttnAr
   constexpr int TILE = BKV * D * 2;          // one 64-key K or V block in LDS
   constexpr int STAGE = 4 * TILE;            // one 128-key superblock
   constexpr int QT = 32 * D * 2;              // one wave's [32][D] Q tile
-  constexpr int OROW = 2 * D + 16;            // padded row of the staged bf16 output
-  static_assert(4 * DT * 16 * 64 * 4 <= STAGE, "set 1's outputs fit in one stage");
-  static_assert(32 * OROW <= DT * 16 * 64 * 4, "the staged output fits in a wave's share of it");
-  static_assert(2 * 4 * 64 * 4 <= TILE, "set 1's maxima and sums fit in one tile");
+  constexpr int HT = DT / 2;                  // d tiles of 32 that each set merges
+  constexpr int HALF = HT * 16 * 64 * 4;      // bytes of a wave's unnormalized output on those tiles
+  constexpr int HROW = D + 16;                // padded half row (D / 2 bf16) of the staged output
+  static_assert(4 * 2 * HALF <= STAGE, "both sets' handovers fit in one stage");
+  static_assert(32 * HROW <= HALF, "a staged half row block fits in a handover");
+  static_assert(4 * 256 * 4 <= TILE, "both sets' maxima and sums fit in one tile");
   // two superblock stages, then the four row/head roles' Q tiles
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE + 4 * QT];
   const lds::lds_u8* lds = (const lds::lds_u8*)smem;
@@ -373,13 +375,13 @@ __global__ void __launch_bounds__(2 * NTHREADS, 1) attn_fwd_paired_kernel(AttnAr
   const int total = nsbA + nsbB;
   // Loads of a superblock's four 64-key tiles [K even, K odd, V even,
   // V odd], TILE / 1024 one-KiB instructions each, dealt out over the eight
-  // waves; this wave's share of a tile is PER_TILE instructions, part u
-  // being instruction wave + 8 (u % PER_TILE) of tile u / PER_TILE.
+  // wave slots; slot w's share of a tile is PER_TILE instructions, part u
+  // being instruction w + 8 (u % PER_TILE) of tile u / PER_TILE.
   static_assert(TILE % 8192 == 0, "each tile splits evenly over the eight waves");
   constexpr int PER_TILE = TILE / 1024 / 8;
-  auto issue_part = [&](int idx, int st, int u) {
+  auto issue_part = [&](int idx, int st, int u, int w) {
     const int sb = idx < nsbA ? idx : idx - nsbA;
-    const int tile = u / PER_TILE, i = wave + 8 * (u % PER_TILE);
+    const int tile = u / PER_TILE, i = w + 8 * (u % PER_TILE);
     const int row0 = sb * 2 * BKV + (tile & 1) * BKV;
     attnt::dma_tile_part<D>(rkv, ldb, row0, a.s, tile < 2 ? kcol : vcol,
                             lds_base + (uint32_t)st * STAGE + (uint32_t)tile * TILE, i);
@@ -387,14 +389,24 @@ __global__ void __launch_bounds__(2 * NTHREADS, 1) attn_fwd_paired_kernel(AttnAr
   // Step idx's loads: K even, K odd and V even of superblock idx + 1 into
   // the other stage (read last in step idx - 1), and V odd of superblock
   // idx into this stage (its previous V odd was read by set 1 in step
-  // idx - 1); both are waited for at the top of step idx + 1.
+  // idx - 1); both are waited for at the top of step idx + 1.  Set 0
+  // finishes its step's work earlier than set 1, which carries the softmax
+  // of its previous block, so each set 0 wave also issues its set 1
+  // partner's share of superblock idx + 1: a wave issuing LDS-direct loads
+  // is held until the CU's L2-to-LDS path accepts them, and set 0 would
+  // otherwise spend that time at the barrier.
   auto issue = [&](int idx, int st, bool next) {
     if (next) {
 #pragma unroll
-      for (int u = 0; u < 3 * PER_TILE; ++u) issue_part(idx + 1, st ^ 1, u);
+      for (int u = 0; u < 3 * PER_TILE; ++u) {
+        if (par == 0) {
+          issue_part(idx + 1, st ^ 1, u, wave);
+          issue_part(idx + 1, st ^ 1, u, wave + 4);
+        }
+      }
     }
 #pragma unroll
-    for (int u = 3 * PER_TILE; u < 4 * PER_TILE; ++u) issue_part(idx, st, u);
+    for (int u = 3 * PER_TILE; u < 4 * PER_TILE; ++u) issue_part(idx, st, u, wave);
   };
   // Q of query block pb: role w4's tile (rows rp0 .. rp0 + 31 of head j,
   // zeros beyond the sequence) in Q slot w4, half of its D / 16 one-KiB
@@ -412,6 +424,7 @@ __global__ void __launch_bounds__(2 * NTHREADS, 1) attn_fwd_paired_kernel(AttnAr
   // order), so neither copy's registers are shaped by the other's.
   auto run = [&](auto set) {
     constexpr int P = decltype(set)::value;
+    bf16x8 qf[KK];       // this role's Q fragments, read from its LDS tile once per query block
     f32x16 oacc[DT];
     f32x16 sacc[2];      // the scores of this wave's current block (set 1: kept to the next step)
     float m_run = -INFINITY, l_run = 0.0f;
@@ -427,7 +440,7 @@ __global__ void __launch_bounds__(2 * NTHREADS, 1) attn_fwd_paired_kernel(AttnAr
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
           sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(attnt::row_frag<D>(tk, 32 * kt, kk),
-                                                             attnt::row_frag<D>(tq, 0, kk), sacc[kt], 0, 0, 0);
+                                                             qf[kk], sacc[kt], 0, 0, 0);
     };
     // Online softmax in base 2 against a per-row reference m_run that only
     // moves when the block's scaled maximum exceeds it by more than kLazy:
@@ -491,7 +504,7 @@ __global__ void __launch_bounds__(2 * NTHREADS, 1) attn_fwd_paired_kernel(AttnAr
     if (total > 0) {
       issue_q(pbA);
 #pragma unroll
-      for (int u = 0; u < 3 * PER_TILE; ++u) issue_part(0, 0, u);
+      for (int u = 0; u < 3 * PER_TILE; ++u) issue_part(0, 0, u, wave);
     }
     for (int idx = 0; idx < total; ++idx) {
       const int st = idx & 1;
@@ -505,6 +518,8 @@ __global__ void __launch_bounds__(2 * NTHREADS, 1) attn_fwd_paired_kernel(AttnAr
         rp0 = pb * rows_per_wg + (w4 / a.hg) * 32;
         my_row = rp0 + l32;
         nkb = nkb_of(pb);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) qf[kk] = attnt::row_frag<D>(tq, 0, kk);
 #pragma unroll
         for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -537,10 +552,9 @@ __global__ void __launch_bounds__(2 * NTHREADS, 1) attn_fwd_paired_kernel(AttnAr
       if (sb + 1 < (inB ? nsbB : nsbA)) continue;
       // The query block is done.  Set 1 takes its last block further (its
       // V odd tile has arrived at the barrier) while the next block's Q tiles
-      // load (every score product of this block is done), then hands its
-      // output to set 0 through this stage's memory and its maxima and sums
-      // through the other stage's V odd slot (idle until the next step's
-      // loads), both free once every wave has passed the second barrier.
+      // load (every score product of this block is done); this stage and the
+      // other stage's V odd slot (idle until the next step's loads) are free
+      // once every wave has passed the second barrier.
       lds::wait_vmcnt<0>();
       lds::wait_lgkm0();
       lds::barrier();
@@ -551,63 +565,69 @@ __global__ void __launch_bounds__(2 * NTHREADS, 1) attn_fwd_paired_kernel(AttnAr
       }
       lds::wait_lgkm0();
       lds::barrier();
-      uint8_t* const wbuf = smem + st * STAGE + w4 * (DT * 16 * 64 * 4);  // this role's share of the stage
-      lds::lds_u8* const wl = (lds::lds_u8*)wbuf;
-      float* xo = reinterpret_cast<float*>(wbuf) + lane;
-      float* ml = reinterpret_cast<float*>(smem + (st ^ 1) * STAGE + 3 * TILE) + w4 * 128 + lane;
-      if constexpr (P == 1) {
+      // Each set merges and stores half of the d columns, set 0 the first
+      // HT tiles of 32 and set 1 the rest, so each hands the other half of
+      // its unnormalized output over through this stage's memory (role w4's
+      // share: set 1's handover, then set 0's) and its maxima and sums
+      // through the other stage's V odd slot.
+      uint8_t* const wbuf = smem + st * STAGE + w4 * (2 * HALF);
+      float* const give = reinterpret_cast<float*>(wbuf + (P == 0 ? HALF : 0)) + lane;
+      uint8_t* const tbuf = wbuf + (P == 0 ? 0 : HALF);
+      float* const take = reinterpret_cast<float*>(tbuf) + lane;
+      float* const ml = reinterpret_cast<float*>(smem + (st ^ 1) * STAGE + 3 * TILE) + w4 * 256 + lane;
+      constexpr int tg = P == 0 ? HT : 0, tm = P == 0 ? 0 : HT;  // first tile given, first tile merged
 #pragma unroll
-        for (int t = 0; t < DT; ++t)
+      for (int t = 0; t < HT; ++t)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) xo[(t * 16 + e) * 64] = oacc[t][e];
-        ml[0] = m_run;
-        ml[64] = l_run;
-      }
+        for (int e = 0; e < 16; ++e) give[(t * 16 + e) * 64] = oacc[tg + t][e];
+      ml[P * 128] = m_run;
+      ml[P * 128 + 64] = l_run;
       lds::wait_lgkm0();
       lds::barrier();
-      if constexpr (P == 0) {
-        const float m1 = ml[0], l1 = ml[64];
-        const float m = fmaxf(m_run, m1);
+      {
+        const float mo = ml[(1 - P) * 128], lo = ml[(1 - P) * 128 + 64];
+        const float m = fmaxf(m_run, mo);
         const float c0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
-        const float c1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
-        const float l = l_run * c0 + l1 * c1;
+        const float c1 = mo == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mo - m);
+        const float l = l_run * c0 + lo * c1;
         const float l_tot = l + __shfl_xor(l, 32);
         const float inv = 1.0f / l_tot;
-        // Set 1's output into registers, then the merged, normalized bf16
-        // rows into the same memory ([32][D] with padded rows), read back
-        // so that each store covers whole rows.
-        float x1[DT][16];
+        // The other set's half into registers, then the merged, normalized
+        // bf16 half rows into the same memory ([32][D / 2] with padded
+        // rows), read back so that each store covers whole half rows.
+        float x1[HT][16];
 #pragma unroll
-        for (int t = 0; t < DT; ++t)
+        for (int t = 0; t < HT; ++t)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) x1[t][e] = xo[(t * 16 + e) * 64];
+          for (int e = 0; e < 16; ++e) x1[t][e] = take[(t * 16 + e) * 64];
         lds::wait_lgkm0();
         asm volatile("" ::: "memory");  // every lane's reads before any lane's writes
+        lds::lds_u8* const wl = (lds::lds_u8*)tbuf;
 #pragma unroll
-        for (int t = 0; t < DT; ++t)
+        for (int t = 0; t < HT; ++t)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (oacc[t][4 * q4 + e] * c0 + x1[t][4 * q4 + e] * c1) * inv;
+            for (int e = 0; e < 4; ++e) v[e] = (oacc[tm + t][4 * q4 + e] * c0 + x1[t][4 * q4 + e] * c1) * inv;
             u32x2 w;
             w[0] = pack_bf16x2(v[0], v[1]);
             w[1] = pack_bf16x2(v[2], v[3]);
-            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(wl + l32 * OROW +
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(wl + l32 * HROW +
                                                                         (t * 32 + 8 * q4 + 4 * hgrp) * 2) = w;
           }
         lds::wait_lgkm0();
         asm volatile("" ::: "memory");
-        constexpr int CPR = 2 * D / 16, RPI = 64 / CPR;  // 16-byte chunks per row, rows per pass
+        constexpr int CPR = D / 16, RPI = 64 / CPR;  // 16-byte chunks per half row, half rows per pass
 #pragma unroll
         for (int it = 0; it < 32 / RPI; ++it) {
           const int r = it * RPI + lane / CPR, c = lane % CPR;
-          const u32x4 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(wl + r * OROW + c * 16);
+          const u32x4 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(wl + r * HROW + c * 16);
           if (rp0 + r < a.s)
             __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(a.o + (tok0 + rp0 + r) * a.ld_o + (int64_t)j * D +
-                                                                  c * 8));
+                                                                  tm * 32 + c * 8));
         }
-        if (a.lse && hgrp == 0 && my_row < a.s)
+        if (P == 0 && a.lse && hgrp == 0 && my_row < a.s)
           a.lse[((int64_t)beta * a.q + j) * a.s + my_row] = (m + __log2f(l_tot)) * 0.69314718055994531f;
       }
     }
