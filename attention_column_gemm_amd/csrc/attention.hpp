@@ -379,12 +379,14 @@ __global__ void __launch_bounds__(2 * NTHREADS, 1) attn_fwd_paired_kernel(AttnAr
   // being instruction w + 8 (u % PER_TILE) of tile u / PER_TILE.
   static_assert(TILE % 8192 == 0, "each tile splits evenly over the eight waves");
   constexpr int PER_TILE = TILE / 1024 / 8;
+  // every instruction i = w + 8 p this wave issues has i = wave mod 4
+  const uint32_t kv_lane = attnt::dma_lane_off<D>(ldb, wave);
   auto issue_part = [&](int idx, int st, int u, int w) {
     const int sb = idx < nsbA ? idx : idx - nsbA;
     const int tile = u / PER_TILE, i = w + 8 * (u % PER_TILE);
     const int row0 = sb * 2 * BKV + (tile & 1) * BKV;
-    attnt::dma_tile_part<D>(rkv, ldb, row0, a.s, tile < 2 ? kcol : vcol,
-                            lds_base + (uint32_t)st * STAGE + (uint32_t)tile * TILE, i);
+    attnt::dma_tile_part_at<D>(rkv, ldb, row0, tile < 2 ? kcol : vcol,
+                               lds_base + (uint32_t)st * STAGE + (uint32_t)tile * TILE, i, kv_lane);
   };
   // Step idx's loads: K even, K odd and V even of superblock idx + 1 into
   // the other stage (read last in step idx - 1), and V odd of superblock

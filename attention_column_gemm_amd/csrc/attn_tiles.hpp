@@ -93,6 +93,27 @@ __device__ __forceinline__ void dma_tile_part(const u32x4& rsrc, uint32_t ld_byt
   lds::dma16(rsrc, voff, dst + (uint32_t)i * 1024u);
 }
 
+// The same load with the per-lane half of the source offset computed once:
+// dma_lane_off<D>(ld_bytes, i0) serves every instruction i that swz<D>
+// cannot tell apart from i0 (it sees rows modulo 16, and instruction i
+// starts at row RI i: i = i0 mod 4 for D = 128, mod 2 for D = 64), and
+// the rest of the offset is wave-uniform.  Rows at or past the
+// descriptor's end (num_records = nrows ld_bytes) read zeros.
+template <int D>
+__device__ __forceinline__ uint32_t dma_lane_off(uint32_t ld_bytes, int i0) {
+  constexpr int CPR = 2 * D / 16, RI = 1024 / (2 * D);  // 16-byte chunks per row, rows per instruction
+  const int lane = threadIdx.x & 63;
+  const int rl = lane / CPR;
+  const int c = (lane % CPR) ^ swz<D>(i0 * RI + rl);
+  return __umul24((uint32_t)rl, ld_bytes) + (uint32_t)c * 16u;
+}
+template <int D>
+__device__ __forceinline__ void dma_tile_part_at(const u32x4& rsrc, uint32_t ld_bytes, int row0, uint32_t col_bytes,
+                                                 uint32_t dst, int i, uint32_t lane_off) {
+  constexpr int RI = 1024 / (2 * D);
+  lds::dma16(rsrc, lane_off + (uint32_t)(row0 + i * RI) * ld_bytes + col_bytes, dst + (uint32_t)i * 1024u);
+}
+
 // The whole tile: this wave issues instructions i0, i0 + step, ...
 template <int D, int ROWS>
 __device__ __forceinline__ void dma_tile(const u32x4& rsrc, uint32_t ld_bytes, int row0, int nrows,
