@@ -220,8 +220,14 @@ __global__ void __launch_bounds__(64 * DKV_WAVES, 1) attn_bwd_dkv_kernel(BwdArgs
     const int j = g * group + n / ntile;
     const int i0 = (nqt - 1 - n % ntile) * Q_TILE;
     lds::wait_lgkm0();  // this wave's reads of its slot are done
-    dma_tile<D, Q_TILE>(rq, ldq, i0, a.s, (uint32_t)j * D * 2u, slot, 0, 1);
-    dma_tile<D, Q_TILE>(rdo, ldo, i0, a.s, (uint32_t)j * D * 2u, slot + TILE, 0, 1);
+    // the tiles' TI instructions, their per-lane offsets from the loop
+    // invariants of dma_lane_off (rows past the sequence read zeros through
+    // the descriptors' bounds)
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      attnt::dma_tile_part_at<D>(rq, ldq, i0, (uint32_t)j * D * 2u, slot, i, attnt::dma_lane_off<D>(ldq, i));
+      attnt::dma_tile_part_at<D>(rdo, ldo, i0, (uint32_t)j * D * 2u, slot + TILE, i, attnt::dma_lane_off<D>(ldo, i));
+    }
     {  // lanes 2i, 2i+1: the {lse2, Delta} pair of row i0 + i
       const int row = i0 + (lane >> 1);
       dma4(rst, row < a.s ? ((uint32_t)j * a.s + row) * 8u + (lane & 1) * 4u : kOOB, slot + 2 * TILE);
@@ -452,10 +458,17 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_kernel(BwdArgs a, int
   const int nkb = part < 0 ? nkb_all : (part == 0 ? nkb_all / 2 : nkb_all - nkb_all / 2);
   const u32x4 rkv = lds::sgpr_rsrc(a.qkv + tok0 * a.ld_qkv, (uint32_t)a.s * ldq);
   const uint32_t kcol = (uint32_t)(a.q + g) * D * 2u, vcol = (uint32_t)(a.q + a.kv + g) * D * 2u;
+  // every instruction i = wave + 4 p this wave issues has i = wave mod 4:
+  // the per-lane part of its offsets is computed once
+  const uint32_t kv_lane = attnt::dma_lane_off<D>(ldq, wave);
   auto issue = [&](int kb, int st) {
     const uint32_t dst = lds_base + (uint32_t)st * STAGE;
-    dma_tile<D, DQ_KEYS>(rkv, ldq, (kb0 + kb) * DQ_KEYS, a.s, kcol, dst, wave, 4);
-    dma_tile<D, DQ_KEYS>(rkv, ldq, (kb0 + kb) * DQ_KEYS, a.s, vcol, dst + TILE, wave, 4);
+    const int row0 = (kb0 + kb) * DQ_KEYS;
+#pragma unroll
+    for (int i = wave; i < TI; i += 4) {
+      attnt::dma_tile_part_at<D>(rkv, ldq, row0, kcol, dst, i, kv_lane);
+      attnt::dma_tile_part_at<D>(rkv, ldq, row0, vcol, dst + TILE, i, kv_lane);
+    }
   };
   if (nkb > 0) issue(0, 0);
   for (int kb = 0; kb < nkb; ++kb) {
