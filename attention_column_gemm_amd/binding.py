@@ -63,6 +63,12 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m attention_column_gemm_amd.build`")
+        # torch first: its HIP libraries ask for libamdhip64 by file name, not by soname, so
+        # loading this library (which asks for the soname) first would leave two HIP runtimes
+        # in the process, and torch's tensors and streams would be foreign to the one that
+        # launches the kernels here (every launch then fails).  Loaded after torch, the soname
+        # resolves to torch's runtime.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         L.tp_mlp_shard_fwd.argtypes = [ctypes.POINTER(tp_mlp_desc)] + [_VP] * 8 + [_VP]
         L.tp_mlp_shard_bwd.argtypes = ([ctypes.POINTER(tp_mlp_desc), _VP, ctypes.c_float, ctypes.c_uint64]

@@ -21,6 +21,23 @@ def test_library_exports_every_declared_function():
         assert hasattr(L, n), n
 
 
+def test_library_shares_torchs_hip_runtime():
+    """Loading the library before torch is imported must still leave one HIP
+    runtime in the process (torch's), or torch's tensors and streams are
+    foreign to the runtime that launches the kernels."""
+    import os
+    import subprocess
+    import sys
+    code = ("from attention_column_gemm_amd import binding as B\n"
+            "B.lib()\n"
+            "import torch\n"
+            "print(len({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1", out.stdout
+
+
 @pytest.mark.parametrize("tokens,h,t,delta", [
     (64, 128, 2, 4), (2048, 1024, 4, 2), (4096, 4096, 8, 2), (8192, 8192, 8, 2), (7, 9, 1, 2), (0, 16, 3, 2)])
 def test_comm_bytes_matches_oracle(tokens, h, t, delta):
