@@ -216,9 +216,13 @@ __global__ void __launch_bounds__(64 * DKV_WAVES, 1) attn_bwd_dkv_kernel(BwdArgs
   // KV head (all key blocks) read the same Q and dO tiles at about the same
   // time and share them in L2; a half takes one half of the items
   const int n_begin = part == 1 ? nitems / 2 : 0, n_end = part == 0 ? nitems / 2 : nitems;
+  // item n = (head hq, tile index ti) with n = hq ntile + ti, advanced by
+  // DKV_WAVES per pass without a division
+  int hq = (n_begin + wave) / ntile, ti = (n_begin + wave) % ntile;
   for (int n = n_begin + wave; n < n_end; n += DKV_WAVES) {
-    const int j = g * group + n / ntile;
-    const int i0 = (nqt - 1 - n % ntile) * Q_TILE;
+    const int j = g * group + hq;
+    const int i0 = (nqt - 1 - ti) * Q_TILE;
+    for (ti += DKV_WAVES; ti >= ntile; ti -= ntile) ++hq;
     lds::wait_lgkm0();  // this wave's reads of its slot are done
     // the tiles' TI instructions, their per-lane offsets from the loop
     // invariants of dma_lane_off (rows past the sequence read zeros through
@@ -511,12 +515,15 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_kernel(BwdArgs a, int
       else
         grads(std::true_type{});
       const bf16x8 df0 = pack8(ds), df1 = pack8(ds + 8);
-      // dQ^T += K^T dS^T: lane = query, registers = head dims
+      // dQ^T += K^T dS^T: lane = query, registers = head dims; every d tile's
+      // first product before any second one, so consecutive MFMAs do not
+      // accumulate into the same registers
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
+      for (int dt = 0; dt < DT; ++dt)
         dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(tk, 32 * kt, dt, 0), df0, dq[dt], 0, 0, 0);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
         dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(tk, 32 * kt, dt, 1), df1, dq[dt], 0, 0, 0);
-      }
     }
   }
 
