@@ -106,32 +106,49 @@ __device__ __forceinline__ void dq_job(int J, int npb, int ny, int S, int& pb, i
 
 // ---- stats -------------------------------------------------------------------
 // Row r = (beta q + j) s + i: stats[2r] = lse * log2(e), stats[2r+1] = Delta.
-// D/8 lanes per row, eight elements each, folded with cross-lane adds.
+// D/8 lanes per row, each with one 16-byte load of dO and of O per row (read
+// once: sc1 policy, through descriptors over the whole tensors, which the
+// host keeps under 2^31 bytes); a work-group takes STATS_ROWS consecutive
+// groups of rows and issues all their loads before using any.  The eight
+// products of a lane are added in element order and folded with cross-lane
+// adds, and lane 0 of the row stores the pair as one 8-byte store.
+constexpr int STATS_ROWS = 4;
 template <int D>
 __global__ void __launch_bounds__(NTHREADS) attn_bwd_stats_kernel(BwdArgs a, int64_t nrows) {
-  constexpr int LPR = D / 8;
-  const int64_t r = (int64_t)blockIdx.x * (NTHREADS / LPR) + threadIdx.x / LPR;
+  constexpr int LPR = D / 8, RPG = NTHREADS / LPR;
   const int sub = threadIdx.x % LPR;
-  float acc = 0.0f;
-  int64_t beta = 0, j = 0, i = 0;
-  if (r < nrows) {
-    i = r % a.s;
-    j = (r / a.s) % a.q;
-    beta = r / ((int64_t)a.s * a.q);
-    const int64_t off = (beta * a.s + i) * a.ld_o + j * D + sub * 8;
-    float x[8], y[8];
-    Elem<uint16_t>::load4(a.dO + off, *reinterpret_cast<float(*)[4]>(x));
-    Elem<uint16_t>::load4(a.dO + off + 4, *reinterpret_cast<float(*)[4]>(x + 4));
-    Elem<uint16_t>::load4(a.o + off, *reinterpret_cast<float(*)[4]>(y));
-    Elem<uint16_t>::load4(a.o + off + 4, *reinterpret_cast<float(*)[4]>(y + 4));
+  const uint32_t bytes = (uint32_t)((int64_t)a.b * a.s * a.ld_o * 2);
+  const rsrc_t rd = make_rsrc(a.dO, bytes), ro = make_rsrc(a.o, bytes);
+  u32x4 x[STATS_ROWS], y[STATS_ROWS];
+  float lse[STATS_ROWS];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += x[e] * y[e];
+  for (int u = 0; u < STATS_ROWS; ++u) {
+    const int64_t r = ((int64_t)blockIdx.x * STATS_ROWS + u) * RPG + threadIdx.x / LPR;
+    lse[u] = 0.0f;
+    uint32_t off = kOOB;
+    if (r < nrows) {
+      if (sub == 0) lse[u] = a.lse[r];
+      const int64_t i = r % a.s, j = (r / a.s) % a.q, beta = r / ((int64_t)a.s * a.q);
+      off = (uint32_t)(((beta * a.s + i) * a.ld_o + j * D + sub * 8) * 2);
+    }
+    x[u] = __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 2 /* sc1 */);
+    y[u] = __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 2 /* sc1 */);
   }
 #pragma unroll
-  for (int m = LPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m);
-  if (r < nrows && sub == 0) {
-    a.stats[2 * r] = a.lse[r] * 1.4426950408889634f;
-    a.stats[2 * r + 1] = acc;
+  for (int u = 0; u < STATS_ROWS; ++u) {
+    const int64_t r = ((int64_t)blockIdx.x * STATS_ROWS + u) * RPG + threadIdx.x / LPR;
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc += bf16lo(x[u][w]) * bf16lo(y[u][w]);
+      acc += bf16hi(x[u][w]) * bf16hi(y[u][w]);
+    }
+#pragma unroll
+    for (int m = LPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m);
+    if (r < nrows && sub == 0) {
+      const f32x2_t v = {lse[u] * 1.4426950408889634f, acc};
+      *reinterpret_cast<f32x2_t*>(a.stats + 2 * r) = v;
+    }
   }
 }
 
@@ -594,7 +611,7 @@ template <int D>
 hipError_t launch_attn_bwd_stats(const attnb::BwdArgs& a, hipStream_t stream) {
   const int64_t nrows = (int64_t)a.b * a.q * a.s;
   if (nrows == 0) return hipSuccess;
-  constexpr int RPB = attnb::NTHREADS / (D / 8);
+  constexpr int RPB = attnb::NTHREADS / (D / 8) * attnb::STATS_ROWS;
   hipLaunchKernelGGL((attnb::attn_bwd_stats_kernel<D>), dim3((unsigned)((nrows + RPB - 1) / RPB)),
                      dim3(attnb::NTHREADS), 0, stream, a, nrows);
   return hipGetLastError();
