@@ -243,28 +243,33 @@ __global__ void __launch_bounds__(64 * DKV_WAVES, 1) attn_bwd_dkv_kernel(BwdArgs
     lds::wait_lgkm0();  // this wave's reads of its slot are done
     // the tiles' TI instructions, their per-lane offsets from the loop
     // invariants of dma_lane_off (rows past the sequence read zeros through
-    // the descriptors' bounds)
+    // the descriptors' bounds): dO and the statistics first, then Q, so that
+    // dP's products run while the Q tile is still landing
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      attnt::dma_tile_part_at<D>(rq, ldq, i0, (uint32_t)j * D * 2u, slot, i, attnt::dma_lane_off<D>(ldq, i));
+    for (int i = 0; i < TI; ++i)
       attnt::dma_tile_part_at<D>(rdo, ldo, i0, (uint32_t)j * D * 2u, slot + TILE, i, attnt::dma_lane_off<D>(ldo, i));
-    }
     {  // lanes 2i, 2i+1: the {lse2, Delta} pair of row i0 + i
       const int row = i0 + (lane >> 1);
       dma4(rst, row < a.s ? ((uint32_t)j * a.s + row) * 8u + (lane & 1) * 4u : kOOB, slot + 2 * TILE);
     }
-    lds::wait_vmcnt<0>();
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+      attnt::dma_tile_part_at<D>(rq, ldq, i0, (uint32_t)j * D * 2u, slot, i, attnt::dma_lane_off<D>(ldq, i));
 
-    // S = Q K^T and dP = dO V^T for 32 queries x 32 keys: lane = key, registers = queries
+    // dP = dO V^T and S = Q K^T for 32 queries x 32 keys: lane = key, registers = queries
     f32x16 sacc, pacc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sacc[e] = pacc[e] = 0.0f;
+    lds::wait_vmcnt<TI>();  // dO and the statistics have landed
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(tq, 0, kk), row_frag<D>(tkey, 0, kk), sacc, 0, 0, 0);
+    for (int kk = 0; kk < KK; ++kk)
       pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(tdo, 0, kk), row_frag<D>(tval, 0, kk), pacc, 0, 0,
                                                      0);
-    }
+    asm volatile("" : "+v"(pacc));  // dP's products stay ahead of the wait for Q
+    lds::wait_vmcnt<0>();   // and Q
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(tq, 0, kk), row_frag<D>(tkey, 0, kk), sacc, 0, 0, 0);
     // P = exp2(S c log2e - lse2), dS = P (dP - Delta); register r holds query 8(r/4) + 4h + r%4.
     // Items wholly inside the sequence and below the causal diagonal skip the mask.
     const int key = k0 + l32;
