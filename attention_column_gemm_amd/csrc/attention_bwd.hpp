@@ -58,6 +58,7 @@ constexpr int KEY_BLOCK = 32;   // keys per dK/dV work-group
 constexpr int Q_TILE = 32;      // query rows per dK/dV item
 constexpr int DQ_KEYS = 64;     // keys per dQ block
 
+
 struct BwdArgs {
   const uint16_t* qkv;  // [T, (q + 2kv) d] forward projections
   const uint16_t* o;    // [T, q d] forward output
@@ -83,7 +84,28 @@ struct BwdArgs {
   // adds them.
   float* dq_part;
   int dq_split;
+  // dS tiles handed from dK/dV to dQ (causal only, when they fit): dK/dV
+  // stores every item's bf16 dS tile (32 queries x 32 keys, 2 KiB) as its
+  // registers hold it, and attn_bwd_dq_ds_kernel computes dQ = c dS K from
+  // them, transposing on its LDS reads.  A tile is 256 quads of 8 bytes,
+  // quad (key k, query group g) holding the four queries 4g .. 4g + 3 of key
+  // k; the 128-byte block 2 (k / 4) + g / 4 holds keys 4 (k / 4) .. + 3 and
+  // groups 4 (g / 4) .. + 3, with quad (k, g) at 8-byte slot
+  // 4 (k % 4) + 2 (g % 2) + (g % 4) / 2 of it.  Tile t of
+  // (sequence beta, head j, query tile qt, key block kb <= qt) is
+  // (beta q + j) T + qt (qt + 1) / 2 + kb with T = nqt (nqt + 1) / 2 tiles per
+  // head; tiles t < ds_t0 sit at ds_a + 2 KiB t, the rest at
+  // ds_b + 2 KiB (t - ds_t0).
+  uint8_t* ds_a;
+  uint8_t* ds_b;
+  int64_t ds_t0;
+  int ds_path;
 };
+
+// 2 KiB dS tile t of the hand-over (see BwdArgs::ds_a).
+__device__ __forceinline__ uint8_t* ds_tile(const BwdArgs& a, int64_t t) {
+  return t < a.ds_t0 ? a.ds_a + t * 2048 : a.ds_b + (t - a.ds_t0) * 2048;
+}
 
 // Job j of the dQ launch (npb query blocks x ny head groups, dq_split of the
 // blocks split), heaviest first: for i < dq_split, both halves of block
@@ -302,6 +324,18 @@ __global__ void __launch_bounds__(64 * DKV_WAVES, 1) attn_bwd_dkv_kernel(BwdArgs
     for (int jj = 0; jj < 2; ++jj) {
       pf[jj] = pack8(p + 8 * jj);
       df[jj] = pack8(ds + 8 * jj);
+    }
+    if (a.ds_path) {
+      // the item's dS tile for the dQ kernel, before the products below,
+      // whose time covers the stores' write acknowledgement: df[jj] of lane
+      // (key k, h) holds quads (k, 4 jj + h) and (k, 4 jj + 2 + h), which are
+      // adjacent, so it goes out as one 16-byte store, and each store
+      // instruction writes whole 128-byte blocks
+      const int qt = i0 / Q_TILE;
+      uint8_t* dst = ds_tile(a, ((int64_t)beta * a.q + j) * ((int64_t)nqt * (nqt + 1) / 2) + (int64_t)qt * (qt + 1) / 2 +
+                                    kb) + (l32 >> 2) * 256 + (l32 & 3) * 32 + h * 16;
+      *reinterpret_cast<bf16x8*>(dst) = df[0];
+      *reinterpret_cast<bf16x8*>(dst + 128) = df[1];
     }
     // dV^T += dO^T P and dK^T += Q^T dS: lane = key, registers = head dims
 #pragma unroll
@@ -570,6 +604,138 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_kernel(BwdArgs a, int
   }
 }
 
+// dQ from the dS tiles handed over by dK/dV (BwdArgs::ds_path): nothing of
+// the scores, dP or the exponentials is recomputed.  Work-groups, waves and
+// block order as attn_bwd_dq_kernel; per 64-key block a wave of 32 query rows
+// (query tile qt) takes the block's K rows (shared in LDS, double buffered)
+// and its own two 32 x 32 dS tiles (the key halves kb <= qt; three stages,
+// loaded two blocks ahead, both with LDS-direct loads) and adds
+// dQ^T += K^T dS^T in the order of attn_bwd_dq_kernel's products.
+template <int D>
+__global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_ds_kernel(BwdArgs a, int hg) {
+  constexpr int DT = D / 32;
+  constexpr int TILE = DQ_KEYS * D * 2;  // one 64-key K tile
+  constexpr int TI = TILE / 1024;
+  constexpr int DSS = 4 * 4096;          // one dS stage: each wave's two 2 KiB tiles
+  // two K stages, then three dS stages (dS loads run two blocks ahead)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * TILE + 3 * DSS];
+  const lds_u8* lds = (const lds_u8*)smem;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+  const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rows_per_wg = 32 * (4 / hg);
+  const int npb = (a.s + rows_per_wg - 1) / rows_per_wg;
+  const int group = a.q / a.kv;
+  const int sub_per_kv = group / hg;
+  const int ny = a.b * a.kv * sub_per_kv;
+  int pb, y;
+  attnt::causal_block_order(npb, ny, pb, y);
+  const int beta = y / (a.kv * sub_per_kv);
+  const int rem = y % (a.kv * sub_per_kv);
+  const int g = rem / sub_per_kv;
+  const int j = g * group + (rem % sub_per_kv) * hg + (wave % hg);
+  const int pos0 = pb * rows_per_wg;
+  const int rp0 = pos0 + (wave / hg) * 32;
+  const int qt = rp0 / 32;
+  const int my_row = rp0 + l32;
+  const int64_t tok0 = (int64_t)beta * a.s;
+  const uint32_t ldq = (uint32_t)a.ld_qkv * 2u;
+  const int nqt = (a.s + 31) / 32;
+  const int64_t tile0 = ((int64_t)beta * a.q + j) * ((int64_t)nqt * (nqt + 1) / 2) + (int64_t)qt * (qt + 1) / 2;
+  const int64_t tiles_all = (int64_t)a.b * a.q * ((int64_t)nqt * (nqt + 1) / 2);
+  const u32x4 rkv = lds::sgpr_rsrc(a.qkv + tok0 * a.ld_qkv, (uint32_t)a.s * ldq);
+  const u32x4 rda = lds::sgpr_rsrc(a.ds_a, (uint32_t)(a.ds_t0 * 2048));
+  const u32x4 rdb = lds::sgpr_rsrc(a.ds_b, (uint32_t)(tiles_all > a.ds_t0 ? (tiles_all - a.ds_t0) * 2048 : 0));
+  const uint32_t kcol = (uint32_t)(a.q + g) * D * 2u;
+
+  f32x16 dq[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dq[t][e] = 0.0f;
+
+  const int kv_end = min(a.s, pos0 + rows_per_wg);
+  const int nkb = (kv_end + DQ_KEYS - 1) / DQ_KEYS;
+  // every K instruction i = wave + 4 p this wave issues has i = wave mod 4:
+  // the per-lane part of its offsets is computed once
+  const uint32_t kv_lane = attnt::dma_lane_off<D>(ldq, wave);
+  auto issue_k = [&](int kb) {
+    const uint32_t dst = lds_base + (uint32_t)(kb & 1) * TILE;
+#pragma unroll
+    for (int i = wave; i < TI; i += 4) attnt::dma_tile_part_at<D>(rkv, ldq, kb * DQ_KEYS, kcol, dst, i, kv_lane);
+  };
+  // always four loads (halves past the causal range or past the last block
+  // read zeros), so that the count the waits below rely on is fixed
+  auto issue_ds = [&](int kb) {
+    const uint32_t dst = lds_base + 2u * TILE + (uint32_t)((kb % 3) * DSS + wave * 4096);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int kb32 = 2 * kb + kt;
+      const int64_t t = tile0 + kb32;
+      const bool ok = kb < nkb && kb32 <= qt;
+      const bool in_a = t < a.ds_t0;
+      const uint32_t off = ok ? (uint32_t)((in_a ? t : t - a.ds_t0) * 2048) + (uint32_t)lane * 16u : kOOB;
+      lds::dma16(in_a ? rda : rdb, off, dst + (uint32_t)kt * 2048u);
+      lds::dma16(in_a ? rda : rdb, ok ? off + 1024u : kOOB, dst + (uint32_t)kt * 2048u + 1024u);
+    }
+  };
+  // dQ's operand df[jj] (lane = query, registers = keys 16 jj + 8 hf + 4 h
+  // + {0..3} for its halves hf) from a dS tile: in the transposing read, lane
+  // i of a 16-lane group gets slot s from element i % 4 of the quad that lane
+  // 4 s + i / 4 addresses, so group lane c addresses quad (key 16 jj + 8 hf
+  // + 4 h + c / 4, group 4 (lane / 16 % 2) + c % 4): one 512-byte run per
+  // read, each group's 128 bytes a block of the tile
+  const int c16 = lane & 15;
+  const uint32_t ds_lane = (uint32_t)((lane >> 4) * 128 + (4 * (c16 >> 2) + 2 * (c16 & 1) + ((c16 >> 1) & 1)) * 8);
+  auto ds_frag = [&](const lds_u8* tile, int jj) {
+    const v4i16 lo = lds::read_tr16(tile, (uint32_t)(2 * jj) * 512u);
+    const v4i16 hi = lds::read_tr16(tile, (uint32_t)(2 * jj + 1) * 512u);
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+  if (nkb > 0) {
+    issue_k(0);
+    issue_ds(0);
+    issue_ds(1);
+  }
+  for (int kb = 0; kb < nkb; ++kb) {
+    // everything but the last four loads (dS of block kb + 1) has landed:
+    // K of block kb and this wave's dS of block kb
+    lds::wait_vmcnt<4>();
+    lds::wait_lgkm0();
+    lds::barrier();  // block kb's K is in LDS for every wave; every wave is done with block kb-1
+    if (kb + 1 < nkb) issue_k(kb + 1);
+    issue_ds(kb + 2);
+    const lds_u8* tk = lds + (kb & 1) * TILE;
+    const lds_u8* tds = lds + 2 * TILE + (kb % 3) * DSS + wave * 4096 + ds_lane;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      if (2 * kb + kt > qt) break;
+      const bf16x8 df0 = ds_frag(tds + kt * 2048, 0), df1 = ds_frag(tds + kt * 2048, 1);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(tk, 32 * kt, dt, 0), df0, dq[dt], 0, 0, 0);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(tk, 32 * kt, dt, 1), df1, dq[dt], 0, 0, 0);
+    }
+  }
+  lds::wait_vmcnt<0>();  // no load into LDS outlives the work-group
+  if (my_row < a.s) {
+    uint16_t* dst = a.dqkv + (tok0 + my_row) * a.ld_qkv + (int64_t)j * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float w4[4] = {dq[dt][4 * q4] * a.scale, dq[dt][4 * q4 + 1] * a.scale, dq[dt][4 * q4 + 2] * a.scale,
+                             dq[dt][4 * q4 + 3] * a.scale};
+        Elem<uint16_t>::store4(dst + 32 * dt + 8 * q4 + 4 * h, w4);
+      }
+  }
+}
+
 // dQ of the split query blocks: the two halves added in a fixed order (first
 // + second), scaled and stored as bf16, with the row and head mapping of
 // attn_bwd_dq_kernel.  One thread per (slot, wave, dt, lane), the lane
@@ -667,14 +833,19 @@ inline int64_t attn_bwd_dq_part_floats(int b, int q, int kv, int hg, int dq_spli
   return (int64_t)dq_split * b * kv * ((q / kv) / hg) * 2 * 4 * (d / 32) * 16 * 64;
 }
 
-// dQ (a.dq_split and a.dq_part set by the caller; dq_split <= npb / 2), then
-// the kernel that finishes the split blocks.
+// dQ: from the handed-over dS tiles when a.ds_path, else recomputing the
+// scores (a.dq_split and a.dq_part set by the caller; dq_split <= npb / 2),
+// then the kernel that finishes the split blocks.
 template <int D>
 hipError_t launch_attn_bwd_dq(const attnb::BwdArgs& a, int hg, hipStream_t stream) {
   const int rows_per_wg = 32 * (4 / hg);
   const int npb = (a.s + rows_per_wg - 1) / rows_per_wg;
   const int ny = a.b * a.kv * ((a.q / a.kv) / hg);
   if (npb == 0 || ny == 0) return hipSuccess;
+  if (a.ds_path) {
+    hipLaunchKernelGGL((attnb::attn_bwd_dq_ds_kernel<D>), dim3(npb, ny), dim3(attnb::NTHREADS), 0, stream, a, hg);
+    return hipGetLastError();
+  }
   if (a.dq_split == 0) {
     hipLaunchKernelGGL((attnb::attn_bwd_dq_kernel<D>), dim3(npb, ny), dim3(attnb::NTHREADS), 0, stream, a, hg);
     return hipGetLastError();

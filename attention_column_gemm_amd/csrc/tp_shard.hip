@@ -678,7 +678,25 @@ int attn_bwd_impl(const tp_attn_desc* d, const void* dZ, const void* X, const vo
   const int hg = heads_per_wg(q / kv);
   // dQ's heaviest query blocks likewise, their halves' sums in dX_i's memory
   // (written only by the last GEMM below)
-  a.dq_split = split_tail_enabled() ? attn_bwd_dq_split(a.s, a.causal, a.b, a.q, a.kv, hg) : 0;
+  // dK/dV hands its dS tiles to dQ (no recompute of the scores there) where
+  // they fit in dX_i's memory and the part of dWqkv_i's after the dK/dV
+  // halves, both written only by the last GEMM below
+  a.ds_path = 0;
+  if (split_tail_enabled() && a.causal) {
+    const int64_t nqt = (a.s + 31) / 32;
+    const int64_t tiles = (int64_t)a.b * a.q * (nqt * (nqt + 1) / 2);
+    const int64_t cap_a = T64 * d->h * 2 / 2048;
+    const int64_t part_bytes = a.split > 0 ? attn_bwd_dkv_part_floats(a.b, a.kv, a.split, D) * 4 : 0;
+    const int64_t b_off = (part_bytes + 2047) / 2048 * 2048;
+    const int64_t cap_b = d->h * nqkv64 * 4 > b_off ? (d->h * nqkv64 * 4 - b_off) / 2048 : 0;
+    if (tiles > 0 && tiles <= cap_a + cap_b) {
+      a.ds_path = 1;
+      a.ds_a = static_cast<uint8_t*>(dX_i);
+      a.ds_t0 = tiles < cap_a ? tiles : cap_a;
+      a.ds_b = reinterpret_cast<uint8_t*>(dWqkv_i) + b_off;
+    }
+  }
+  a.dq_split = split_tail_enabled() && !a.ds_path ? attn_bwd_dq_split(a.s, a.causal, a.b, a.q, a.kv, hg) : 0;
   if (attn_bwd_dq_part_floats(a.b, a.q, a.kv, hg, a.dq_split, D) * 4 > T64 * d->h * 2) a.dq_split = 0;
   a.dq_part = static_cast<float*>(dX_i);
   hipError_t e;

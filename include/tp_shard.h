@@ -258,14 +258,18 @@ int tp_attn_shard_fwd(const tp_attn_desc* desc, const void* X, const void* Wqkv_
  *   dQKV_i  [T, (q+2kv) d]     out, bf16
  *   dWqkv_i [h, (q+2kv) d] fp32 out.  Its memory is also scratch for the
  *                          dK/dV kernel (fp32 halves of the split causal key
- *                          blocks) before the last GEMM writes it, so it
+ *                          blocks, then the dS tiles that do not fit in
+ *                          dX_i's) before the last GEMM writes it, so it
  *                          must not overlap any other argument.
  *   dWo_i   [q d, h] fp32      out
  *   dX_i    [T, h]             out, bf16 partial input gradient.  Its memory is
- *                              also scratch for the dQ kernel (fp32 halves of
- *                              split causal query blocks) before the last GEMM
- *                              writes it, so it must not overlap any other
- *                              argument.
+ *                              also scratch before the last GEMM writes it:
+ *                              causal, the bf16 dS tiles (2 KiB per 32 x 32
+ *                              query x key tile on or below the diagonal)
+ *                              that dK/dV hands to dQ when they fit here and
+ *                              in dWqkv_i's memory, else the fp32 halves of
+ *                              dQ's split causal query blocks; so it must not
+ *                              overlap any other argument.
  * Same descriptor and conditions as tp_attn_shard_fwd.  The result does not
  * depend on the order in which work-groups run (no atomics).
  */
@@ -449,11 +453,13 @@ int tp_profile_arm(void* const* events, int32_t n_events);
  *   tile        TP_TILE_AUTO, or a tile shape every bf16 GEMM then takes
  *   split_tail  1 (default): a GEMM whose last round of tiles is at most half
  *               full splits it (over K into a caller buffer that the entry
- *               point documents as scratch, or over N in a paired launch), and
- *               the attention kernels split their heaviest causal blocks;
- *               0: no splits.
+ *               point documents as scratch, or over N in a paired launch),
+ *               the attention kernels split their heaviest causal blocks, and
+ *               the causal attention backward hands its dS tiles from dK/dV
+ *               to dQ where they fit;
+ *               0: no splits and no hand-over.
  * The results are the same either way up to fp32 rounding order (paired
- * half-width tails are bit-identical).  Returns TP_EINVAL for values outside
+ * half-width tails and dQ from handed-over tiles are bit-identical).  Returns TP_EINVAL for values outside
  * these ranges (the options are then unchanged).
  */
 int tp_set_options(int32_t tile, int32_t split_tail);

@@ -336,3 +336,38 @@ def test_attention_forward_paired_blocks(name, lib_options):
         got[split] = sh.O.clone()
         del sh
     assert not torch.equal(got[1], got[0]), "the paired kernel did not run"
+
+
+DS_HANDOVER = {
+    # causal dS tiles that fit in dX_i's memory: dK/dV hands them to dQ
+    "gqa4_d128_s256_h1024": I.custom_attn(221, 2, 256, 1024, 8, 2, 128, 2),
+    # ragged sequence, d = 64
+    "gqa4_d64_s200_h1024_ragged": I.custom_attn(222, 2, 200, 1024, 8, 2, 64, 2),
+    # more tiles than dX_i holds: the last ones go to dWqkv_i's memory after the dK/dV halves
+    "mqa4_d128_s512_h1024_overflow": I.custom_attn(223, 1, 512, 1024, 4, 1, 128, 1),
+}
+
+
+@pytest.mark.parametrize("name", list(DS_HANDOVER))
+def test_attention_backward_ds_handover(name, lib_options):
+    """Where the causal dS tiles fit in dX_i's memory (and dWqkv_i's after
+    the dK/dV halves), the dK/dV kernel stores them and dQ is computed from
+    them without recomputing the scores.  One forward, then the backward with
+    the hand-over on and off: both against the oracle, and dQ bit-identical
+    (the handed-over tiles hold the values the recompute forms, and dQ's
+    products run in the same order)."""
+    torch = need_gpu()
+    from attention_column_gemm_amd.shard import to_device
+    c = DS_HANDOVER[name]
+    lib_options(split_tail=1)
+    banner(f"attn bwd dS hand-over {name} b={c.b} s={c.s} h={c.h} n_q={c.n_q} n_kv={c.n_kv} d={c.d}")
+    sh, X, w = _run(c, 0, True)
+    dZ = I.attn_upstream_grad(c)
+    got = {}
+    for split in (1, 0):
+        lib_options(split_tail=split)
+        sh.backward(to_device(dZ, "bf16"))
+        torch.cuda.synchronize()
+        _check_bwd(f"handover{split}", c, sh, X, w, dZ, True)
+        got[split] = sh.dQKV[:, :c.q * c.d].clone()
+    assert torch.equal(got[1], got[0]), "dQ from the handed-over dS tiles differs from the recompute"
