@@ -371,3 +371,30 @@ def test_attention_backward_ds_handover(name, lib_options):
         _check_bwd(f"handover{split}", c, sh, X, w, dZ, True)
         got[split] = sh.dQKV[:, :c.q * c.d].clone()
     assert torch.equal(got[1], got[0]), "dQ from the handed-over dS tiles differs from the recompute"
+
+
+def test_attention_backward_ds_not_fitting(lib_options):
+    """Causal dS tiles that do not fit in dX_i's and dWqkv_i's memory: dQ
+    recomputes the scores, and with split_tail on its heaviest query blocks
+    are split in two (their fp32 halves in dX_i's memory).  One forward, then
+    the backward with the split on and off, both against the oracle; dQ
+    differs between the two in rounding only, which shows the split ran."""
+    torch = need_gpu()
+    from attention_column_gemm_amd.shard import to_device
+    c = I.custom_attn(224, 1, 1024, 512, 4, 1, 64, 1)
+    nqt = (c.s + 31) // 32
+    tiles = c.b * c.q * nqt * (nqt + 1) // 2
+    room = c.b * c.s * c.h * 2 + c.h * (c.q + 2 * c.kv) * c.d * 4
+    assert tiles * 2048 > room, "the shape no longer exceeds the hand-over's room"
+    lib_options(split_tail=1)
+    banner(f"attn bwd dS not fitting b={c.b} s={c.s} h={c.h} n_q={c.n_q} n_kv={c.n_kv} d={c.d}")
+    sh, X, w = _run(c, 0, True)
+    dZ = I.attn_upstream_grad(c)
+    got = {}
+    for split in (1, 0):
+        lib_options(split_tail=split)
+        sh.backward(to_device(dZ, "bf16"))
+        torch.cuda.synchronize()
+        _check_bwd(f"nofit{split}", c, sh, X, w, dZ, True)
+        got[split] = sh.dQKV[:, :c.q * c.d].clone()
+    assert not torch.equal(got[1], got[0]), "dQ's split query blocks did not run"
