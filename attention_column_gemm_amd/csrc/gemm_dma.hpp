@@ -265,6 +265,9 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmProblem& p, const Epi& e
     for (int b = 0; b < NB; ++b) opb[s][b] = make_doperand(p.B[s][b], p.ldb[s], p.N, p.K[s], BL);
   }
 
+  // With a K-contiguous A and a single M/N-contiguous B the waves issue their
+  // LDS-direct loads at raised priority, ahead of the SIMD's other wave
+  constexpr bool PRIO_LOADS = AL == KMAJOR && BL != KMAJOR && NB == 1;
   // kt (local) may be nk (one past the last tile): it is then sent past the
   // end of K, where every offset is out of range and the loads only write
   // zeros into LDS
@@ -273,9 +276,11 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmProblem& p, const Epi& e
     const int s = (gk < nk0 || p.nseg == 1) ? 0 : 1;
     const int k0 = (gk - (s ? nk0 : 0)) * BK;
     const uint32_t st = lds_base + (uint32_t)(kt % NSTAGE) * STAGE;
+    if constexpr (PRIO_LOADS) __builtin_amdgcn_s_setprio(2);
     la.issue(opa[s], k0, st);
 #pragma unroll
     for (int b = 0; b < NB; ++b) lb.issue(opb[s][b], k0, st + A_BYTES + b * B_BYTES);
+    if constexpr (PRIO_LOADS) __builtin_amdgcn_s_setprio(0);
   };
 
   // Fragments of one k step (16 of the tile's 32 k) for all of this wave's MFMA tiles.
