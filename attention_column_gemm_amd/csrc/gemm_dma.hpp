@@ -202,11 +202,20 @@ __device__ __forceinline__ void interleave_reads() {
 
 // LDS bytes of one work-group: two operand stages, reused by the epilogue's
 // staging area once the K loop is done.
+// Operand stages in LDS: two for the 256- and 128-row tiles; the 64 x 64
+// tile, whose waves issue one MFMA per k step and so cannot cover a K tile's
+// load latency with one tile in flight, takes three (two tiles in flight
+// while one is read; measured on gfx950 against two and four stages).
+template <int BM, int BN, int NB>
+constexpr int gemm_nstage() {
+  return BM * BN <= 64 * 64 ? 3 : 2;
+}
 template <int BM, int BN, int WGM, int WGN, int BK, int NB>
 constexpr int smem_bytes() {
   constexpr int STAGE = BM * BK * 2 + NB * BN * BK * 2;
+  constexpr int STAGES = gemm_nstage<BM, BN, NB>() * STAGE;
   constexpr int STAGING = WGM * WGN * NB * 32 * ((BN / WGN) * 4 + 16);  // epilogue staging (see below)
-  return 2 * STAGE > STAGING ? 2 * STAGE : STAGING;
+  return STAGES > STAGING ? STAGES : STAGING;
 }
 
 // One output tile: tile w of problem p's launch, computed by the whole
@@ -225,7 +234,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmProblem& p, const Epi& e
   static_assert(TM >= 1 && TN >= 1, "wave sub-tile must hold whole 32x32 MFMA tiles");
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   constexpr int STAGE = A_BYTES + NB * B_BYTES;
-  constexpr int NSTAGE = 2, KK = BK / 16;
+  constexpr int NSTAGE = gemm_nstage<BM, BN, NB>(), KK = BK / 16;
   static_assert(KK >= 3 && NW % 2 == 0, "staggered issue needs at least three k steps and paired waves");
 
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
@@ -334,7 +343,7 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmProblem& p, const Epi& e
       interleave_reads<0, NMF, NDS>();
     }
   };
-  if (nk > 0) {
+  if (NSTAGE == 2 && nk > 0) {
     issue(0);
     sync_next();
     if (half == 0 && nk > 1) issue(1);
@@ -370,20 +379,52 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmProblem& p, const Epi& e
       }
     }
   };
-  if constexpr (AL == KMAJOR && (BL == KMAJOR || NB == 1)) {
-    if (half == 0)
-      kloop(std::integral_constant<int, 0>{});
-    else
-      kloop(std::integral_constant<int, 1>{});
-  } else {
-    kloop(std::integral_constant<int, 2>{});  // one copy, the half chosen at run time
-  }
-  if (nk > 0) {
+  if constexpr (NSTAGE > 2) {
+    // Deep pipeline: before tile kt's last k step every wave waits for tile
+    // kt+1 only (tiles kt+2 .. kt+NSTAGE-1 stay in flight: L loads each per
+    // wave), and after the barrier refills the stage tile kt has freed with
+    // tile kt+NSTAGE (past K: zeros, no memory access).
+    constexpr int L = DmaLoader<BM, AL, NW, BK>::PER + NB * DmaLoader<BN, BL, NW, BK>::PER;
+    if (nk > 0) {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (kk + 1 < KK) load_frags(F[(kk + 1) & 1], nk - 1, kk + 1);
-      mfmas(F[kk & 1]);
-      interleave();
+      for (int t = 0; t < NSTAGE; ++t) issue(t);
+      wait_vmcnt<(NSTAGE - 1) * L>();
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      barrier();
+      load_frags(F[0], 0, 0);
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 1 < KK) {
+          load_frags(F[(kk + 1) & 1], kt, kk + 1);
+        } else if (kt + 1 < nk) {
+          wait_vmcnt<(NSTAGE - 2) * L>();
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of tile kt are done
+          barrier();
+          issue(kt + NSTAGE);
+          load_frags(F[0], kt + 1, 0);
+        }
+        mfmas(F[kk & 1]);
+        interleave();
+      }
+    }
+  } else {
+    if constexpr (AL == KMAJOR && (BL == KMAJOR || NB == 1)) {
+      if (half == 0)
+        kloop(std::integral_constant<int, 0>{});
+      else
+        kloop(std::integral_constant<int, 1>{});
+    } else {
+      kloop(std::integral_constant<int, 2>{});  // one copy, the half chosen at run time
+    }
+    if (nk > 0) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 1 < KK) load_frags(F[(kk + 1) & 1], nk - 1, kk + 1);
+        mfmas(F[kk & 1]);
+        interleave();
+      }
     }
   }
 
