@@ -672,19 +672,19 @@ hipError_t launch_attn_fwd(const attn::AttnArgs& a, hipStream_t stream) {
   const int ny = a.b * a.kv * ((a.q / a.kv) / a.hg);
   if (npb == 0 || ny == 0) return hipSuccess;
   if (a.paired) {
-    hipLaunchKernelGGL((attn::attn_fwd_paired_kernel<D>), dim3(((npb + 1) / 2) * ny), dim3(2 * attn::NTHREADS), 0,
+    tp_launch((attn::attn_fwd_paired_kernel<D>), dim3(((npb + 1) / 2) * ny), dim3(2 * attn::NTHREADS), 0,
                        stream, a);
     return hipGetLastError();
   }
   if (a.split == 0) {
-    hipLaunchKernelGGL((attn::attn_fwd_kernel<D>), dim3(npb, ny), dim3(attn::NTHREADS), 0, stream, a);
+    tp_launch((attn::attn_fwd_kernel<D>), dim3(npb, ny), dim3(attn::NTHREADS), 0, stream, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((attn::attn_fwd_kernel<D>), dim3((npb + a.split) * ny), dim3(attn::NTHREADS), 0, stream, a);
+  tp_launch((attn::attn_fwd_kernel<D>), dim3((npb + a.split) * ny), dim3(attn::NTHREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = (int64_t)a.split * ny * 4 * (D / 32) * 64;
-  hipLaunchKernelGGL((attn::attn_fwd_merge_kernel<D>), dim3((unsigned)((n + attn::NTHREADS - 1) / attn::NTHREADS)),
+  tp_launch((attn::attn_fwd_merge_kernel<D>), dim3((unsigned)((n + attn::NTHREADS - 1) / attn::NTHREADS)),
                      dim3(attn::NTHREADS), 0, stream, a);
   return hipGetLastError();
 }

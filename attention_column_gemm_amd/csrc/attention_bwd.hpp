@@ -783,7 +783,7 @@ hipError_t launch_attn_bwd_stats(const attnb::BwdArgs& a, hipStream_t stream) {
   const int64_t nrows = (int64_t)a.b * a.q * a.s;
   if (nrows == 0) return hipSuccess;
   constexpr int RPB = attnb::NTHREADS / (D / 8) * attnb::STATS_ROWS;
-  hipLaunchKernelGGL((attnb::attn_bwd_stats_kernel<D>), dim3((unsigned)((nrows + RPB - 1) / RPB)),
+  tp_launch((attnb::attn_bwd_stats_kernel<D>), dim3((unsigned)((nrows + RPB - 1) / RPB)),
                      dim3(attnb::NTHREADS), 0, stream, a, nrows);
   return hipGetLastError();
 }
@@ -808,12 +808,12 @@ hipError_t launch_attn_bwd_dkv(const attnb::BwdArgs& a, hipStream_t stream) {
   const int nkb = (a.s + attnb::KEY_BLOCK - 1) / attnb::KEY_BLOCK;
   const int BG = a.b * a.kv;
   if (nkb == 0 || BG == 0) return hipSuccess;
-  hipLaunchKernelGGL((attnb::attn_bwd_dkv_kernel<D>), dim3(BG * (nkb + a.split)), dim3(64 * attnb::DKV_WAVES), 0,
+  tp_launch((attnb::attn_bwd_dkv_kernel<D>), dim3(BG * (nkb + a.split)), dim3(64 * attnb::DKV_WAVES), 0,
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.split == 0) return e;
   const int64_t n = (int64_t)BG * a.split * 2 * (D / 32) * 256;
-  hipLaunchKernelGGL((attnb::attn_bwd_dkv_combine_kernel<D>), dim3((unsigned)((n + attnb::NTHREADS - 1) / attnb::NTHREADS)),
+  tp_launch((attnb::attn_bwd_dkv_combine_kernel<D>), dim3((unsigned)((n + attnb::NTHREADS - 1) / attnb::NTHREADS)),
                      dim3(attnb::NTHREADS), 0, stream, a);
   return hipGetLastError();
 }
@@ -843,19 +843,19 @@ hipError_t launch_attn_bwd_dq(const attnb::BwdArgs& a, int hg, hipStream_t strea
   const int ny = a.b * a.kv * ((a.q / a.kv) / hg);
   if (npb == 0 || ny == 0) return hipSuccess;
   if (a.ds_path) {
-    hipLaunchKernelGGL((attnb::attn_bwd_dq_ds_kernel<D>), dim3(npb, ny), dim3(attnb::NTHREADS), 0, stream, a, hg);
+    tp_launch((attnb::attn_bwd_dq_ds_kernel<D>), dim3(npb, ny), dim3(attnb::NTHREADS), 0, stream, a, hg);
     return hipGetLastError();
   }
   if (a.dq_split == 0) {
-    hipLaunchKernelGGL((attnb::attn_bwd_dq_kernel<D>), dim3(npb, ny), dim3(attnb::NTHREADS), 0, stream, a, hg);
+    tp_launch((attnb::attn_bwd_dq_kernel<D>), dim3(npb, ny), dim3(attnb::NTHREADS), 0, stream, a, hg);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((attnb::attn_bwd_dq_kernel<D>), dim3((npb + a.dq_split) * ny), dim3(attnb::NTHREADS), 0, stream,
+  tp_launch((attnb::attn_bwd_dq_kernel<D>), dim3((npb + a.dq_split) * ny), dim3(attnb::NTHREADS), 0, stream,
                      a, hg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = (int64_t)a.dq_split * ny * 4 * 64 * (D / 32);
-  hipLaunchKernelGGL((attnb::attn_bwd_dq_combine_kernel<D>), dim3((unsigned)((n + attnb::NTHREADS - 1) / attnb::NTHREADS)),
+  tp_launch((attnb::attn_bwd_dq_combine_kernel<D>), dim3((unsigned)((n + attnb::NTHREADS - 1) / attnb::NTHREADS)),
                      dim3(attnb::NTHREADS), 0, stream, a, hg);
   return hipGetLastError();
 }

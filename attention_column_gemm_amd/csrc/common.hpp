@@ -1,10 +1,35 @@
 // Shared device types and helpers for the gfx950 kernels of libtpshard.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace tp {
+
+// ---- kernel launches -------------------------------------------------------
+// Every kernel of the library is launched through tp_launch.  While a
+// profiling scope is open on the calling thread (tp_profile_arm), the launch
+// carries the scope's events: the start event on the scope's first kernel
+// and the stop event on each kernel, so that they hold the first kernel's
+// start and the last one's end as the dispatches themselves timestamp them
+// (no marker packets between kernels).
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool started = false;
+};
+inline thread_local LaunchEvents* g_launch_events = nullptr;
+
+template <typename F, typename... Args>
+inline void tp_launch(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t stream, Args... args) {
+  if (LaunchEvents* ev = g_launch_events) {
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, ev->started ? nullptr : ev->start, ev->stop, 0u,
+                          args...);
+    ev->started = true;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, args...);
+  }
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

@@ -638,7 +638,7 @@ template <int BM, int BN, int WGM, int WGN, int BK, int AL, int BL, class Epi>
 hipError_t launch_gemm_dma(const GemmProblem& p, const Epi& epi, hipStream_t stream) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm3::gemm_dma_kernel<BM, BN, WGM, WGN, BK, AL, BL, Epi>), dim3(tiles),
+  tp_launch((gemm3::gemm_dma_kernel<BM, BN, WGM, WGN, BK, AL, BL, Epi>), dim3(tiles),
                      dim3(64 * WGM * WGN), 0, stream, p, epi, gemm3::SplitTail{nullptr, tiles, 0});
   return hipGetLastError();
 }
@@ -662,12 +662,12 @@ hipError_t launch_gemm_dma_split(const GemmProblem& p, const Epi& epi, float* sc
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   const int tail = tiles % 256;
   const gemm3::SplitTail sp{scratch, tiles - tail, tail};
-  hipLaunchKernelGGL((gemm3::gemm_dma_kernel<BM, BN, WGM, WGN, BK, AL, BL, Epi, true>), dim3(tiles + tail),
+  tp_launch((gemm3::gemm_dma_kernel<BM, BN, WGM, WGN, BK, AL, BL, Epi, true>), dim3(tiles + tail),
                      dim3(64 * WGM * WGN), 0, stream, p, epi, sp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = (int64_t)tail * BM * (BN / 4);
-  hipLaunchKernelGGL((gemm3::split_tail_finish_kernel<BM, BN, Epi>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+  tp_launch((gemm3::split_tail_finish_kernel<BM, BN, Epi>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                      stream, p, epi, sp);
   return hipGetLastError();
 }
@@ -679,7 +679,7 @@ hipError_t launch_gemm_dma_pair(const GemmProblem& p1, const E1& e1, const GemmP
   const int t1 = ((p1.M + C1::BM - 1) / C1::BM) * ((p1.N + C1::BN - 1) / C1::BN);
   const int t2 = ((p2.M + C2::BM - 1) / C2::BM) * ((p2.N + C2::BN - 1) / C2::BN);
   if (t1 + t2 == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm3::gemm_dma_pair_kernel<C1, E1, C2, E2>), dim3(t1 + t2), dim3(C1::THREADS), 0, stream,
+  tp_launch((gemm3::gemm_dma_pair_kernel<C1, E1, C2, E2>), dim3(t1 + t2), dim3(C1::THREADS), 0, stream,
                      p1, e1, p2, e2, t1);
   return hipGetLastError();
 }
@@ -710,7 +710,7 @@ hipError_t launch_gemm_dma_pair_tail(const GemmProblem& p1, const E1& e1, const 
   const int rows = (p2.M + C2::BM - 1) / C2::BM;
   const int t2 = rows2 * ((p2.N + C2::BN - 1) / C2::BN);
   const int t3 = (rows - rows2) * ((p2.N + C2::BN / 2 - 1) / (C2::BN / 2));
-  hipLaunchKernelGGL((gemm3::gemm_dma_pair_tail_kernel<C1, E1, C2, E2>), dim3(t1 + t2 + t3), dim3(C1::THREADS), 0,
+  tp_launch((gemm3::gemm_dma_pair_tail_kernel<C1, E1, C2, E2>), dim3(t1 + t2 + t3), dim3(C1::THREADS), 0,
                      stream, p1, e1, p2, e2, t1, rows2);
   return hipGetLastError();
 }

@@ -81,7 +81,7 @@ template <int AL, int BL, class Epi>
 hipError_t launch_gemm_f32(const GemmProblem& p, const Epi& epi, hipStream_t stream) {
   const int tiles = ((p.M + simt::BM - 1) / simt::BM) * ((p.N + simt::BN - 1) / simt::BN);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((simt::gemm_f32_kernel<AL, BL, Epi>), dim3(tiles), dim3(simt::NTHREADS), 0, stream, p, epi);
+  tp_launch((simt::gemm_f32_kernel<AL, BL, Epi>), dim3(tiles), dim3(simt::NTHREADS), 0, stream, p, epi);
   return hipGetLastError();
 }
 

@@ -37,22 +37,35 @@ struct ProfileHook {
   int next = 0;       // next slot to hand out
 } g_prof;
 
-// Brackets one kernel launch with the armed events, if any.
+// Opens a profiling scope over the kernels launched while it lives, with the
+// next armed event pair, if any: tp_launch attaches the events to those
+// kernels' dispatches.  A scope that launches nothing records both events on
+// the stream.
 struct Probe {
   hipStream_t st;
-  hipEvent_t after = nullptr;
+  tp::LaunchEvents ev;
+  tp::LaunchEvents* outer = nullptr;
+  bool open = false;
   explicit Probe(hipStream_t s) : st(s) {
     if (!g_prof.armed.load(std::memory_order_acquire)) return;
     std::lock_guard<std::mutex> lk(g_prof.mu);
     if (g_prof.next < g_prof.n_kernels) {
       const int idx = g_prof.next++;
-      hipEventRecord(g_prof.ev[2 * idx], st);
-      after = g_prof.ev[2 * idx + 1];
+      ev.start = g_prof.ev[2 * idx];
+      ev.stop = g_prof.ev[2 * idx + 1];
+      outer = tp::g_launch_events;
+      tp::g_launch_events = &ev;
+      open = true;
       if (g_prof.next == g_prof.n_kernels) g_prof.armed.store(false, std::memory_order_release);
     }
   }
   ~Probe() {
-    if (after) hipEventRecord(after, st);
+    if (!open) return;
+    tp::g_launch_events = outer;
+    if (!ev.started) {
+      hipEventRecord(ev.start, st);
+      hipEventRecord(ev.stop, st);
+    }
   }
 };
 
@@ -208,7 +221,7 @@ hipError_t dropout_bwd(int64_t n, const void* dOut, uint32_t thr, float scale, u
   const int64_t nv = n / Vec<T>::N;
   if (nv == 0) return hipSuccess;
   Probe pr(st);
-  hipLaunchKernelGGL(dropout_bwd_kernel<T>, dim3(grid_for(nv)), dim3(256), 0, st, nv, static_cast<const T*>(dOut), thr,
+  tp_launch(dropout_bwd_kernel<T>, dim3(grid_for(nv)), dim3(256), 0, st, nv, static_cast<const T*>(dOut), thr,
                      scale, seed, static_cast<T*>(dY));
   return hipGetLastError();
 }
@@ -224,10 +237,10 @@ hipError_t colsum(int64_t rows, int64_t cols, const void* X, float* out, hipStre
   Probe pr(st);
   const T* x = static_cast<const T*>(X);
   switch (cv) {
-    case 8: hipLaunchKernelGGL((colsum_kernel<T, 8>), dim3(blocks), dim3(256), 0, st, rows, cols, cols, x, out); break;
-    case 4: hipLaunchKernelGGL((colsum_kernel<T, 4>), dim3(blocks), dim3(256), 0, st, rows, cols, cols, x, out); break;
-    case 2: hipLaunchKernelGGL((colsum_kernel<T, 2>), dim3(blocks), dim3(256), 0, st, rows, cols, cols, x, out); break;
-    default: hipLaunchKernelGGL((colsum_kernel<T, 1>), dim3(blocks), dim3(256), 0, st, rows, cols, cols, x, out);
+    case 8: tp_launch((colsum_kernel<T, 8>), dim3(blocks), dim3(256), 0, st, rows, cols, cols, x, out); break;
+    case 4: tp_launch((colsum_kernel<T, 4>), dim3(blocks), dim3(256), 0, st, rows, cols, cols, x, out); break;
+    case 2: tp_launch((colsum_kernel<T, 2>), dim3(blocks), dim3(256), 0, st, rows, cols, cols, x, out); break;
+    default: tp_launch((colsum_kernel<T, 1>), dim3(blocks), dim3(256), 0, st, rows, cols, cols, x, out);
   }
   return hipGetLastError();
 }
@@ -817,11 +830,11 @@ int sum_rows(int64_t rows_total, int64_t row0, int64_t nrows, int64_t cols, int3
   const uint64_t idx0 = (uint64_t)(row0 * cols);
   Probe pr(st);
   if (dtype == TP_BF16)
-    hipLaunchKernelGGL(sum_partials_kernel<uint16_t>, dim3(grid_for(nv)), dim3(256), 0, st, nv, cols, t, P,
+    tp_launch(sum_partials_kernel<uint16_t>, dim3(grid_for(nv)), dim3(256), 0, st, nv, cols, t, P,
                        static_cast<const uint16_t*>(bias), thr, scale, seed, idx0,
                        static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(out));
   else
-    hipLaunchKernelGGL(sum_partials_kernel<float>, dim3(grid_for(nv)), dim3(256), 0, st, nv, cols, t, P,
+    tp_launch(sum_partials_kernel<float>, dim3(grid_for(nv)), dim3(256), 0, st, nv, cols, t, P,
                        static_cast<const float*>(bias), thr, scale, seed, idx0, static_cast<const float*>(residual),
                        static_cast<float*>(out));
   return hip_status(hipGetLastError());
@@ -834,7 +847,7 @@ template <class T, int NV>
 void launch_sum_norm(int64_t nrows, int64_t cols, int t, const PartialPtrs& P, const void* bias, uint32_t thr,
                      float scale, uint64_t seed, uint64_t idx0, const void* residual, int layer, const void* gamma,
                      const void* beta, float eps, void* out, void* normed, hipStream_t st) {
-  hipLaunchKernelGGL((sum_norm_kernel<T, NV>), dim3((unsigned)nrows), dim3(256), 0, st, cols, t, P,
+  tp_launch((sum_norm_kernel<T, NV>), dim3((unsigned)nrows), dim3(256), 0, st, cols, t, P,
                      static_cast<const T*>(bias), thr, scale, seed, idx0, static_cast<const T*>(residual), layer,
                      static_cast<const T*>(gamma), static_cast<const T*>(beta), eps, static_cast<T*>(out),
                      static_cast<T*>(normed));
@@ -976,7 +989,7 @@ int tp_all_gather(int64_t rows_per_rank, int64_t cols, int32_t t, int32_t dtype,
   if (nv == 0) return TP_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Probe pr(st);
-  hipLaunchKernelGGL(gather_kernel, dim3(grid_for(nv * t)), dim3(256), 0, st, nv, t, S, static_cast<u32x4*>(out));
+  tp_launch(gather_kernel, dim3(grid_for(nv * t)), dim3(256), 0, st, nv, t, S, static_cast<u32x4*>(out));
   return hip_status(hipGetLastError());
 }
 

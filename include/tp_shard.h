@@ -436,14 +436,17 @@ int tp_all_gather(int64_t rows_per_rank, int64_t cols, int32_t t, int32_t dtype,
 int tp_comm_bytes(int64_t tokens, int64_t h, int32_t t, int32_t delta, tp_comm* out);
 
 /*
- * tp_profile_arm -- profiling aid: bracket the library's next kernels with events.
+ * tp_profile_arm -- profiling aid: time the library's next kernels with events.
  * `events` is a host array of n_events hipEvent_t handles (as void*), n_events
- * even and at most 64.  Each of the next n_events/2 kernels the library
- * enqueues records events[2i] just before and events[2i+1] just after kernel i,
- * on that kernel's stream; after that the hook is idle again.  n_events = 0
- * disarms it.  Process-wide: with several threads launching, each kernel
- * claims the next free pair under a lock, so which kernel gets which pair
- * follows the order the launches happen in.
+ * even and at most 64.  Each of the next n_events/2 step kernels the library
+ * enqueues (one launch, or a launch and the small kernel finishing its split
+ * part) takes one pair: events[2i] is stamped when its first dispatch starts
+ * and events[2i+1] when its last one ends, by the dispatches themselves
+ * (hipExtLaunchKernel), so no marker packet sits between kernels; after that
+ * the hook is idle again.  n_events = 0 disarms it.  Process-wide: with
+ * several threads launching, each step kernel claims the next free pair
+ * under a lock, so which kernel gets which pair follows the order the
+ * launches happen in.
  * Returns TP_EINVAL for an odd or out-of-range count or a NULL handle.
  */
 int tp_profile_arm(void* const* events, int32_t n_events);
