@@ -46,6 +46,7 @@ namespace attnb {
 
 using lds::lds_u8;
 using lds::v4i16;
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 using attnt::dma4;
 using attnt::dma_tile;
 using attnt::pack8;
@@ -85,13 +86,11 @@ struct BwdArgs {
   float* dq_part;
   int dq_split;
   // dS tiles handed from dK/dV to dQ (causal only, when they fit): dK/dV
-  // stores every item's bf16 dS tile (32 queries x 32 keys, 2 KiB) as its
-  // registers hold it, and attn_bwd_dq_ds_kernel computes dQ = c dS K from
-  // them, transposing on its LDS reads.  A tile is 256 quads of 8 bytes,
-  // quad (key k, query group g) holding the four queries 4g .. 4g + 3 of key
-  // k; the 128-byte block 2 (k / 4) + g / 4 holds keys 4 (k / 4) .. + 3 and
-  // groups 4 (g / 4) .. + 3, with quad (k, g) at 8-byte slot
-  // 4 (k % 4) + 2 (g % 2) + (g % 4) / 2 of it.  Tile t of
+  // stores every item's bf16 dS tile (32 queries x 32 keys, 2 KiB, in the
+  // register image dQ's products take: the first 1 KiB holds each lane's
+  // first eight values, the second its last eight, 16 bytes per lane), and
+  // attn_bwd_dq_ds_kernel loads them straight into registers and computes
+  // dQ = c dS K from them.  Tile t of
   // (sequence beta, head j, query tile qt, key block kb <= qt) is
   // (beta q + j) T + qt (qt + 1) / 2 + kb with T = nqt (nqt + 1) / 2 tiles per
   // head; tiles t < ds_t0 sit at ds_a + 2 KiB t, the rest at
@@ -326,16 +325,38 @@ __global__ void __launch_bounds__(64 * DKV_WAVES, 1) attn_bwd_dkv_kernel(BwdArgs
       df[jj] = pack8(ds + 8 * jj);
     }
     if (a.ds_path) {
-      // the item's dS tile for the dQ kernel, before the products below,
-      // whose time covers the stores' write acknowledgement: df[jj] of lane
-      // (key k, h) holds quads (k, 4 jj + h) and (k, 4 jj + 2 + h), which are
-      // adjacent, so it goes out as one 16-byte store, and each store
-      // instruction writes whole 128-byte blocks
+      // The item's dS tile for the dQ kernel, before the products below,
+      // whose time covers the stores' write acknowledgement, transposed on
+      // the matrix cores: with dS as the first operand (row = key, k = the
+      // query order of the registers) and a 0/1 permutation matrix as the
+      // second, the product holds dS[query][key] with lane = query and
+      // registers = keys in the order dQ's products read K^T, exactly
+      // (products with 1 and sums with 0).  Query 16 jj + 8 (m / 4) + 4 h +
+      // m % 4 of lane (key, h) sits at k = 8 h + m of df[jj], so operand lane
+      // (row, hy) holds 1 at position m when row = 16 jj + 8 (m / 4) + 4 hy +
+      // m % 4.
+      f32x16 tr;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) tr[e] = 0.0f;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        u16x8 pm;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+          pm[m] = l32 == 16 * jj + 8 * (m >> 2) + 4 * h + (m & 3) ? (uint16_t)0x3F80 : (uint16_t)0;
+        tr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(df[jj], __builtin_bit_cast(bf16x8, pm), tr, 0, 0, 0);
+      }
       const int qt = i0 / Q_TILE;
       uint8_t* dst = ds_tile(a, ((int64_t)beta * a.q + j) * ((int64_t)nqt * (nqt + 1) / 2) + (int64_t)qt * (qt + 1) / 2 +
-                                    kb) + (l32 >> 2) * 256 + (l32 & 3) * 32 + h * 16;
-      *reinterpret_cast<bf16x8*>(dst) = df[0];
-      *reinterpret_cast<bf16x8*>(dst + 128) = df[1];
+                                    kb) + lane * 16;
+      float lo[8], hi[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        lo[e] = tr[e];
+        hi[e] = tr[8 + e];
+      }
+      *reinterpret_cast<bf16x8*>(dst) = pack8(lo);
+      *reinterpret_cast<bf16x8*>(dst + 1024) = pack8(hi);
     }
     // dV^T += dO^T P and dK^T += Q^T dS: lane = key, registers = head dims
 #pragma unroll
@@ -607,18 +628,17 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_kernel(BwdArgs a, int
 // dQ from the dS tiles handed over by dK/dV (BwdArgs::ds_path): nothing of
 // the scores, dP or the exponentials is recomputed.  Work-groups, waves and
 // block order as attn_bwd_dq_kernel; per 64-key block a wave of 32 query rows
-// (query tile qt) takes the block's K rows (shared in LDS, double buffered)
-// and its own two 32 x 32 dS tiles (the key halves kb <= qt; three stages,
-// loaded two blocks ahead, both with LDS-direct loads) and adds
-// dQ^T += K^T dS^T in the order of attn_bwd_dq_kernel's products.
+// (query tile qt) takes the block's K rows (shared in LDS, double buffered,
+// LDS-direct loads) and its own two 32 x 32 dS tiles (the key halves
+// kb <= qt), loaded two blocks ahead straight into registers in the image
+// its products take, and adds dQ^T += K^T dS^T in the order of
+// attn_bwd_dq_kernel's products.
 template <int D>
 __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_ds_kernel(BwdArgs a, int hg) {
   constexpr int DT = D / 32;
   constexpr int TILE = DQ_KEYS * D * 2;  // one 64-key K tile
   constexpr int TI = TILE / 1024;
-  constexpr int DSS = 4 * 4096;          // one dS stage: each wave's two 2 KiB tiles
-  // two K stages, then three dS stages (dS loads run two blocks ahead)
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * TILE + 3 * DSS];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * TILE];
   const lds_u8* lds = (const lds_u8*)smem;
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
@@ -645,8 +665,8 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_ds_kernel(BwdArgs a, 
   const int64_t tile0 = ((int64_t)beta * a.q + j) * ((int64_t)nqt * (nqt + 1) / 2) + (int64_t)qt * (qt + 1) / 2;
   const int64_t tiles_all = (int64_t)a.b * a.q * ((int64_t)nqt * (nqt + 1) / 2);
   const u32x4 rkv = lds::sgpr_rsrc(a.qkv + tok0 * a.ld_qkv, (uint32_t)a.s * ldq);
-  const u32x4 rda = lds::sgpr_rsrc(a.ds_a, (uint32_t)(a.ds_t0 * 2048));
-  const u32x4 rdb = lds::sgpr_rsrc(a.ds_b, (uint32_t)(tiles_all > a.ds_t0 ? (tiles_all - a.ds_t0) * 2048 : 0));
+  const rsrc_t rda = make_rsrc(a.ds_a, (uint32_t)(a.ds_t0 * 2048));
+  const rsrc_t rdb = make_rsrc(a.ds_b, (uint32_t)(tiles_all > a.ds_t0 ? (tiles_all - a.ds_t0) * 2048 : 0));
   const uint32_t kcol = (uint32_t)(a.q + g) * D * 2u;
 
   f32x16 dq[DT];
@@ -665,10 +685,13 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_ds_kernel(BwdArgs a, 
 #pragma unroll
     for (int i = wave; i < TI; i += 4) attnt::dma_tile_part_at<D>(rkv, ldq, kb * DQ_KEYS, kcol, dst, i, kv_lane);
   };
-  // always four loads (halves past the causal range or past the last block
-  // read zeros), so that the count the waits below rely on is fixed
-  auto issue_ds = [&](int kb) {
-    const uint32_t dst = lds_base + 2u * TILE + (uint32_t)((kb % 3) * DSS + wave * 4096);
+  // a block's two dS tiles, [kt][jj]: always four loads (halves past the
+  // causal range or past the last block read zeros), so that the count the
+  // wait below relies on is fixed
+  struct DsRegs {
+    bf16x8 f[2][2];
+  };
+  auto load_ds = [&](int kb, DsRegs& r) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int kb32 = 2 * kb + kt;
@@ -676,50 +699,41 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_ds_kernel(BwdArgs a, 
       const bool ok = kb < nkb && kb32 <= qt;
       const bool in_a = t < a.ds_t0;
       const uint32_t off = ok ? (uint32_t)((in_a ? t : t - a.ds_t0) * 2048) + (uint32_t)lane * 16u : kOOB;
-      lds::dma16(in_a ? rda : rdb, off, dst + (uint32_t)kt * 2048u);
-      lds::dma16(in_a ? rda : rdb, ok ? off + 1024u : kOOB, dst + (uint32_t)kt * 2048u + 1024u);
+      const rsrc_t rd = in_a ? rda : rdb;
+      r.f[kt][0] = __builtin_bit_cast(bf16x8, buf_load16(rd, off));
+      r.f[kt][1] = __builtin_bit_cast(bf16x8, buf_load16(rd, ok ? off + 1024u : kOOB));
     }
   };
-  // dQ's operand df[jj] (lane = query, registers = keys 16 jj + 8 hf + 4 h
-  // + {0..3} for its halves hf) from a dS tile: in the transposing read, lane
-  // i of a 16-lane group gets slot s from element i % 4 of the quad that lane
-  // 4 s + i / 4 addresses, so group lane c addresses quad (key 16 jj + 8 hf
-  // + 4 h + c / 4, group 4 (lane / 16 % 2) + c % 4): one 512-byte run per
-  // read, each group's 128 bytes a block of the tile
-  const int c16 = lane & 15;
-  const uint32_t ds_lane = (uint32_t)((lane >> 4) * 128 + (4 * (c16 >> 2) + 2 * (c16 & 1) + ((c16 >> 1) & 1)) * 8);
-  auto ds_frag = [&](const lds_u8* tile, int jj) {
-    const v4i16 lo = lds::read_tr16(tile, (uint32_t)(2 * jj) * 512u);
-    const v4i16 hi = lds::read_tr16(tile, (uint32_t)(2 * jj + 1) * 512u);
-    typedef short v8i16 __attribute__((ext_vector_type(8)));
-    const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, v);
-  };
+  DsRegs R[3];
   if (nkb > 0) {
     issue_k(0);
-    issue_ds(0);
-    issue_ds(1);
+    load_ds(0, R[0]);
+    load_ds(1, R[1]);
   }
-  for (int kb = 0; kb < nkb; ++kb) {
-    // everything but the last four loads (dS of block kb + 1) has landed:
-    // K of block kb and this wave's dS of block kb
-    lds::wait_vmcnt<4>();
-    lds::wait_lgkm0();
-    lds::barrier();  // block kb's K is in LDS for every wave; every wave is done with block kb-1
-    if (kb + 1 < nkb) issue_k(kb + 1);
-    issue_ds(kb + 2);
-    const lds_u8* tk = lds + (kb & 1) * TILE;
-    const lds_u8* tds = lds + 2 * TILE + (kb % 3) * DSS + wave * 4096 + ds_lane;
+  for (int kb0 = 0; kb0 < nkb; kb0 += 3) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      if (2 * kb + kt > qt) break;
-      const bf16x8 df0 = ds_frag(tds + kt * 2048, 0), df1 = ds_frag(tds + kt * 2048, 1);
+    for (int u = 0; u < 3; ++u) {
+      const int kb = kb0 + u;
+      if (kb >= nkb) break;
+      // everything but the last four loads (dS of block kb + 1) has landed:
+      // K of block kb (and this wave's dS of block kb, loaded before it)
+      lds::wait_vmcnt<4>();
+      lds::wait_lgkm0();
+      lds::barrier();  // block kb's K is in LDS for every wave; every wave is done with block kb-1
+      if (kb + 1 < nkb) issue_k(kb + 1);
+      load_ds(kb + 2, R[(u + 2) % 3]);
+      const lds_u8* tk = lds + (kb & 1) * TILE;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(tk, 32 * kt, dt, 0), df0, dq[dt], 0, 0, 0);
+      for (int kt = 0; kt < 2; ++kt) {
+        if (2 * kb + kt > qt) break;
+        const bf16x8 df0 = R[u].f[kt][0], df1 = R[u].f[kt][1];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(tk, 32 * kt, dt, 1), df1, dq[dt], 0, 0, 0);
+        for (int dt = 0; dt < DT; ++dt)
+          dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(tk, 32 * kt, dt, 0), df0, dq[dt], 0, 0, 0);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(tk, 32 * kt, dt, 1), df1, dq[dt], 0, 0, 0);
+      }
     }
   }
   lds::wait_vmcnt<0>();  // no load into LDS outlives the work-group
