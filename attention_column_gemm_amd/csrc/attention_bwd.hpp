@@ -630,8 +630,8 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_kernel(BwdArgs a, int
 // block order as attn_bwd_dq_kernel; per 64-key block a wave of 32 query rows
 // (query tile qt) takes the block's K rows (shared in LDS, double buffered,
 // LDS-direct loads) and its own two 32 x 32 dS tiles (the key halves
-// kb <= qt), loaded two blocks ahead straight into registers in the image
-// its products take, and adds dQ^T += K^T dS^T in the order of
+// kb <= qt), loaded a block ahead straight into registers in the image its
+// products take, and adds dQ^T += K^T dS^T in the order of
 // attn_bwd_dq_kernel's products.
 template <int D>
 __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_ds_kernel(BwdArgs a, int hg) {
@@ -685,9 +685,8 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_ds_kernel(BwdArgs a, 
 #pragma unroll
     for (int i = wave; i < TI; i += 4) attnt::dma_tile_part_at<D>(rkv, ldq, kb * DQ_KEYS, kcol, dst, i, kv_lane);
   };
-  // a block's two dS tiles, [kt][jj]: always four loads (halves past the
-  // causal range or past the last block read zeros), so that the count the
-  // wait below relies on is fixed
+  // a block's two dS tiles, [kt][jj] (halves past the causal range or past
+  // the last block read zeros)
   struct DsRegs {
     bf16x8 f[2][2];
   };
@@ -704,24 +703,22 @@ __global__ void __launch_bounds__(NTHREADS, 2) attn_bwd_dq_ds_kernel(BwdArgs a, 
       r.f[kt][1] = __builtin_bit_cast(bf16x8, buf_load16(rd, ok ? off + 1024u : kOOB));
     }
   };
-  DsRegs R[3];
+  DsRegs R[2];
   if (nkb > 0) {
-    issue_k(0);
     load_ds(0, R[0]);
-    load_ds(1, R[1]);
+    issue_k(0);
   }
-  for (int kb0 = 0; kb0 < nkb; kb0 += 3) {
+  for (int kb0 = 0; kb0 < nkb; kb0 += 2) {
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
+    for (int u = 0; u < 2; ++u) {
       const int kb = kb0 + u;
       if (kb >= nkb) break;
-      // everything but the last four loads (dS of block kb + 1) has landed:
-      // K of block kb (and this wave's dS of block kb, loaded before it)
-      lds::wait_vmcnt<4>();
+      // K of block kb and this wave's dS of block kb have landed
+      lds::wait_vmcnt<0>();
       lds::wait_lgkm0();
       lds::barrier();  // block kb's K is in LDS for every wave; every wave is done with block kb-1
+      load_ds(kb + 1, R[(u + 1) % 2]);
       if (kb + 1 < nkb) issue_k(kb + 1);
-      load_ds(kb + 2, R[(u + 2) % 3]);
       const lds_u8* tk = lds + (kb & 1) * TILE;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
