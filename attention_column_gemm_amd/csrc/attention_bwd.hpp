@@ -24,7 +24,10 @@
 //    decreasing order of work; a small kernel adds the two halves in a fixed
 //    order.
 //  * dQ: the forward's layout (waves own 32 query rows; the work-group shares
-//    64-key K and V blocks in LDS).
+//    64-key K and V blocks in LDS).  Causal, where the tiles fit in memory
+//    that the final GEMM writes later, dK/dV hands its dS tiles over instead
+//    (transposed on the matrix cores into the register image dQ's products
+//    take) and dQ loads them rather than recomputing the scores.
 // Operand layouts: with v_mfma_f32_32x32x16_bf16 computing C[i][j] += sum_k
 // X[i][k] Y[j][k], lane l holding column j = l % 32 of C, the score tile is
 // formed so that the lane's column is the index the next product keeps
@@ -32,7 +35,7 @@
 // registers; those registers are used directly as the Y operand of the
 // next product, in a permuted k order, and the matching X operand (Q^T,
 // dO^T or K^T) is read with ds_read_b64_tr_b16 from the row-major LDS tile
-// in that same order, so no tile is ever stored transposed.
+// in that same order, so no operand tile is ever stored transposed.
 #pragma once
 
 #include <type_traits>
