@@ -673,7 +673,7 @@ hipError_t launch_attn_fwd(const attn::AttnArgs& a, hipStream_t stream) {
   if (npb == 0 || ny == 0) return hipSuccess;
   if (a.paired) {
     tp_launch((attn::attn_fwd_paired_kernel<D>), dim3(((npb + 1) / 2) * ny), dim3(2 * attn::NTHREADS), 0,
-                       stream, a);
+              stream, a);
     return hipGetLastError();
   }
   if (a.split == 0) {
@@ -685,7 +685,7 @@ hipError_t launch_attn_fwd(const attn::AttnArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int64_t n = (int64_t)a.split * ny * 4 * (D / 32) * 64;
   tp_launch((attn::attn_fwd_merge_kernel<D>), dim3((unsigned)((n + attn::NTHREADS - 1) / attn::NTHREADS)),
-                     dim3(attn::NTHREADS), 0, stream, a);
+            dim3(attn::NTHREADS), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -798,7 +798,7 @@ hipError_t launch_attn_bwd_stats(const attnb::BwdArgs& a, hipStream_t stream) {
   if (nrows == 0) return hipSuccess;
   constexpr int RPB = attnb::NTHREADS / (D / 8) * attnb::STATS_ROWS;
   tp_launch((attnb::attn_bwd_stats_kernel<D>), dim3((unsigned)((nrows + RPB - 1) / RPB)),
-                     dim3(attnb::NTHREADS), 0, stream, a, nrows);
+            dim3(attnb::NTHREADS), 0, stream, a, nrows);
   return hipGetLastError();
 }
 
@@ -823,12 +823,12 @@ hipError_t launch_attn_bwd_dkv(const attnb::BwdArgs& a, hipStream_t stream) {
   const int BG = a.b * a.kv;
   if (nkb == 0 || BG == 0) return hipSuccess;
   tp_launch((attnb::attn_bwd_dkv_kernel<D>), dim3(BG * (nkb + a.split)), dim3(64 * attnb::DKV_WAVES), 0,
-                     stream, a);
+            stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.split == 0) return e;
   const int64_t n = (int64_t)BG * a.split * 2 * (D / 32) * 256;
   tp_launch((attnb::attn_bwd_dkv_combine_kernel<D>), dim3((unsigned)((n + attnb::NTHREADS - 1) / attnb::NTHREADS)),
-                     dim3(attnb::NTHREADS), 0, stream, a);
+            dim3(attnb::NTHREADS), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -865,12 +865,12 @@ hipError_t launch_attn_bwd_dq(const attnb::BwdArgs& a, int hg, hipStream_t strea
     return hipGetLastError();
   }
   tp_launch((attnb::attn_bwd_dq_kernel<D>), dim3((npb + a.dq_split) * ny), dim3(attnb::NTHREADS), 0, stream,
-                     a, hg);
+            a, hg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = (int64_t)a.dq_split * ny * 4 * 64 * (D / 32);
   tp_launch((attnb::attn_bwd_dq_combine_kernel<D>), dim3((unsigned)((n + attnb::NTHREADS - 1) / attnb::NTHREADS)),
-                     dim3(attnb::NTHREADS), 0, stream, a, hg);
+            dim3(attnb::NTHREADS), 0, stream, a, hg);
   return hipGetLastError();
 }
 

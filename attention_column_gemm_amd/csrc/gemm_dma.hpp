@@ -200,8 +200,6 @@ __device__ __forceinline__ void interleave_reads() {
   }
 }
 
-// LDS bytes of one work-group: two operand stages, reused by the epilogue's
-// staging area once the K loop is done.
 // Operand stages in LDS: two for the 256- and 128-row tiles; the 64 x 64
 // tile, whose waves issue one MFMA per k step and so cannot cover a K tile's
 // load latency with one tile in flight, takes three (two tiles in flight
@@ -210,6 +208,8 @@ template <int BM, int BN, int NB>
 constexpr int gemm_nstage() {
   return BM * BN <= 64 * 64 ? 3 : 2;
 }
+// LDS bytes of one work-group: the operand stages, reused by the epilogue's
+// staging area once the K loop is done.
 template <int BM, int BN, int WGM, int WGN, int BK, int NB>
 constexpr int smem_bytes() {
   constexpr int STAGE = BM * BK * 2 + NB * BN * BK * 2;
@@ -277,9 +277,10 @@ __device__ __forceinline__ void gemm_dma_tile(const GemmProblem& p, const Epi& e
   // With a K-contiguous A and a single M/N-contiguous B the waves issue their
   // LDS-direct loads at raised priority, ahead of the SIMD's other wave
   constexpr bool PRIO_LOADS = AL == KMAJOR && BL != KMAJOR && NB == 1;
-  // kt (local) may be nk (one past the last tile): it is then sent past the
-  // end of K, where every offset is out of range and the loads only write
-  // zeros into LDS
+  // kt (local) may lie past the last tile (by one with two stages, by up to
+  // NSTAGE with the deeper pipeline): it is then sent past the end of K,
+  // where every offset is out of range and the loads only write zeros into
+  // LDS
   auto issue = [&](int kt) {
     const int gk = KRANGE ? (kt < nk ? kt_begin + kt : nk_all) : kt;
     const int s = (gk < nk0 || p.nseg == 1) ? 0 : 1;
@@ -639,7 +640,7 @@ hipError_t launch_gemm_dma(const GemmProblem& p, const Epi& epi, hipStream_t str
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   if (tiles == 0) return hipSuccess;
   tp_launch((gemm3::gemm_dma_kernel<BM, BN, WGM, WGN, BK, AL, BL, Epi>), dim3(tiles),
-                     dim3(64 * WGM * WGN), 0, stream, p, epi, gemm3::SplitTail{nullptr, tiles, 0});
+            dim3(64 * WGM * WGN), 0, stream, p, epi, gemm3::SplitTail{nullptr, tiles, 0});
   return hipGetLastError();
 }
 
@@ -663,12 +664,12 @@ hipError_t launch_gemm_dma_split(const GemmProblem& p, const Epi& epi, float* sc
   const int tail = tiles % 256;
   const gemm3::SplitTail sp{scratch, tiles - tail, tail};
   tp_launch((gemm3::gemm_dma_kernel<BM, BN, WGM, WGN, BK, AL, BL, Epi, true>), dim3(tiles + tail),
-                     dim3(64 * WGM * WGN), 0, stream, p, epi, sp);
+            dim3(64 * WGM * WGN), 0, stream, p, epi, sp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = (int64_t)tail * BM * (BN / 4);
   tp_launch((gemm3::split_tail_finish_kernel<BM, BN, Epi>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                     stream, p, epi, sp);
+            stream, p, epi, sp);
   return hipGetLastError();
 }
 
@@ -680,7 +681,7 @@ hipError_t launch_gemm_dma_pair(const GemmProblem& p1, const E1& e1, const GemmP
   const int t2 = ((p2.M + C2::BM - 1) / C2::BM) * ((p2.N + C2::BN - 1) / C2::BN);
   if (t1 + t2 == 0) return hipSuccess;
   tp_launch((gemm3::gemm_dma_pair_kernel<C1, E1, C2, E2>), dim3(t1 + t2), dim3(C1::THREADS), 0, stream,
-                     p1, e1, p2, e2, t1);
+            p1, e1, p2, e2, t1);
   return hipGetLastError();
 }
 
@@ -711,7 +712,7 @@ hipError_t launch_gemm_dma_pair_tail(const GemmProblem& p1, const E1& e1, const 
   const int t2 = rows2 * ((p2.N + C2::BN - 1) / C2::BN);
   const int t3 = (rows - rows2) * ((p2.N + C2::BN / 2 - 1) / (C2::BN / 2));
   tp_launch((gemm3::gemm_dma_pair_tail_kernel<C1, E1, C2, E2>), dim3(t1 + t2 + t3), dim3(C1::THREADS), 0,
-                     stream, p1, e1, p2, e2, t1, rows2);
+            stream, p1, e1, p2, e2, t1, rows2);
   return hipGetLastError();
 }
 

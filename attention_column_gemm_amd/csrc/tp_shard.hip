@@ -222,7 +222,7 @@ hipError_t dropout_bwd(int64_t n, const void* dOut, uint32_t thr, float scale, u
   if (nv == 0) return hipSuccess;
   Probe pr(st);
   tp_launch(dropout_bwd_kernel<T>, dim3(grid_for(nv)), dim3(256), 0, st, nv, static_cast<const T*>(dOut), thr,
-                     scale, seed, static_cast<T*>(dY));
+            scale, seed, static_cast<T*>(dY));
   return hipGetLastError();
 }
 
@@ -831,12 +831,12 @@ int sum_rows(int64_t rows_total, int64_t row0, int64_t nrows, int64_t cols, int3
   Probe pr(st);
   if (dtype == TP_BF16)
     tp_launch(sum_partials_kernel<uint16_t>, dim3(grid_for(nv)), dim3(256), 0, st, nv, cols, t, P,
-                       static_cast<const uint16_t*>(bias), thr, scale, seed, idx0,
-                       static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(out));
+              static_cast<const uint16_t*>(bias), thr, scale, seed, idx0,
+              static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(out));
   else
     tp_launch(sum_partials_kernel<float>, dim3(grid_for(nv)), dim3(256), 0, st, nv, cols, t, P,
-                       static_cast<const float*>(bias), thr, scale, seed, idx0, static_cast<const float*>(residual),
-                       static_cast<float*>(out));
+              static_cast<const float*>(bias), thr, scale, seed, idx0, static_cast<const float*>(residual),
+              static_cast<float*>(out));
   return hip_status(hipGetLastError());
 }
 
@@ -848,9 +848,9 @@ void launch_sum_norm(int64_t nrows, int64_t cols, int t, const PartialPtrs& P, c
                      float scale, uint64_t seed, uint64_t idx0, const void* residual, int layer, const void* gamma,
                      const void* beta, float eps, void* out, void* normed, hipStream_t st) {
   tp_launch((sum_norm_kernel<T, NV>), dim3((unsigned)nrows), dim3(256), 0, st, cols, t, P,
-                     static_cast<const T*>(bias), thr, scale, seed, idx0, static_cast<const T*>(residual), layer,
-                     static_cast<const T*>(gamma), static_cast<const T*>(beta), eps, static_cast<T*>(out),
-                     static_cast<T*>(normed));
+            static_cast<const T*>(bias), thr, scale, seed, idx0, static_cast<const T*>(residual), layer,
+            static_cast<const T*>(gamma), static_cast<const T*>(beta), eps, static_cast<T*>(out),
+            static_cast<T*>(normed));
 }
 
 template <class T>
